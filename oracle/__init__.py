@@ -1,0 +1,240 @@
+"""CPU oracle for HSTU jagged pointwise attention (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. It wraps ``oracle.c`` (plain fp64 loops,
+OpenMP over (sequence, head)) through ctypes and adds two small pieces of pure
+Python: the tile schedule built from the brute-force tile classifier and the
+longest-first (LPT) ordering of query tiles.
+
+Everything here takes numpy arrays; floating-point inputs are converted to
+float64 (bf16 and fp32 values are represented exactly). Nothing here imports
+the HIP package, and the HIP package never imports this one.
+
+What is pinned and how is described in the header of ``oracle.c``. Every
+function below has a pin in the CPU test suite; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+NORM_NONE, NORM_LN, NORM_GLN = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (-O2, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall", "-o", tmp, _SRC, "-lm"],
+            check=True,
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = ctypes.CDLL(_LIB_PATH)
+        _lib.oracle_time_bucket.restype = ctypes.c_int
+        _lib.oracle_time_bucket.argtypes = [ctypes.c_int64, ctypes.c_int]
+        _lib.oracle_visible.restype = ctypes.c_int
+        _lib.oracle_visible.argtypes = [ctypes.c_int] * 5
+        _lib.oracle_classify_tiles.restype = ctypes.c_int
+        _lib.oracle_classify_tiles.argtypes = [ctypes.c_int] * 7 + [ctypes.c_void_p]
+        for name in ("oracle_fwd", "oracle_bwd", "oracle_mfalcon"):
+            getattr(_lib, name).restype = ctypes.c_int
+    return _lib
+
+
+def _p(a):
+    """Pointer of a numpy array, or NULL for None."""
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _i64(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+
+
+def _u8(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.uint8))
+
+
+def _threads(nthreads):
+    return int(nthreads) if nthreads else (os.cpu_count() or 1)
+
+
+def time_bucket(dt: int, n_tb: int) -> int:
+    return int(_load().oracle_time_bucket(int(dt), int(n_tb)))
+
+
+def visible(i: int, j: int, L: int, P: int, C: int) -> bool:
+    return bool(_load().oracle_visible(int(i), int(j), int(L), int(P), int(C)))
+
+
+def fwd(offsets, Q, K, V, U, *, H, d, prefix_len=None, cand_len=None, ts=None, rab_p=None,
+        rab_t=None, n_max=1.0, norm=NORM_LN, eps=1e-5, group=None, n_groups=1, gamma=None,
+        beta=None, row_sel=None, nthreads=0):
+    """Forward pass. Q/K/V/U: [T, H, d] (any float dtype). Returns dict with
+    Y, O ([T, H*d] float64), mean, rstd ([T] float64)."""
+    lib = _load()
+    offsets = _i32(offsets)
+    B = len(offsets) - 1
+    T = int(offsets[-1])
+    D = H * d
+    Q, K, V, U = (_f64(x).reshape(T, D) for x in (Q, K, V, U))
+    rp, rt = _f64(rab_p), _f64(rab_t)
+    gm, bt = _f64(gamma), _f64(beta)
+    Y = np.zeros((T, D)); O = np.zeros((T, D)); mean = np.zeros(T); rstd = np.zeros(T)
+    pl, cl, ts_, grp, sel = _i32(prefix_len), _i32(cand_len), _i64(ts), _u8(group), _u8(row_sel)
+    rc = lib.oracle_fwd(
+        ctypes.c_int(B), ctypes.c_int(H), ctypes.c_int(d), _p(offsets), _p(pl), _p(cl),
+        _p(Q), _p(K), _p(V), _p(U), _p(ts_),
+        _p(rp), ctypes.c_int(0 if rp is None else len(rp)),
+        _p(rt), ctypes.c_int(0 if rt is None else len(rt)),
+        ctypes.c_double(n_max), ctypes.c_int(norm), ctypes.c_double(eps),
+        _p(grp), ctypes.c_int(n_groups), _p(gm), _p(bt), _p(sel),
+        _p(Y), _p(O), _p(mean), _p(rstd), ctypes.c_int(_threads(nthreads)))
+    if rc != 0:
+        raise ValueError(f"oracle_fwd rejected its input (code {rc})")
+    return {"Y": Y, "O": O, "mean": mean, "rstd": rstd}
+
+
+def bwd(offsets, Q, K, V, U, dY, *, H, d, prefix_len=None, cand_len=None, ts=None, rab_p=None,
+        rab_t=None, n_max=1.0, norm=NORM_LN, eps=1e-5, group=None, n_groups=1, gamma=None,
+        beta=None, nthreads=0):
+    """Backward pass (recomputes the forward). Returns dict with dQ, dK, dV,
+    dU ([T, H*d]), drab_p, drab_t, dgamma, dbeta (None when not applicable)."""
+    lib = _load()
+    offsets = _i32(offsets)
+    B = len(offsets) - 1
+    T = int(offsets[-1])
+    D = H * d
+    Q, K, V, U, dY = (_f64(x).reshape(T, D) for x in (Q, K, V, U, dY))
+    rp, rt = _f64(rab_p), _f64(rab_t)
+    gm, bt = _f64(gamma), _f64(beta)
+    G = n_groups if norm == NORM_GLN else 1
+    dQ, dK, dV, dU = (np.zeros((T, D)) for _ in range(4))
+    drp = np.zeros(len(rp)) if rp is not None else None
+    drt = np.zeros(len(rt)) if rt is not None else None
+    dgm = np.zeros((G, D)) if gm is not None else None
+    dbt = np.zeros((G, D)) if bt is not None else None
+    pl, cl, ts_, grp = _i32(prefix_len), _i32(cand_len), _i64(ts), _u8(group)
+    rc = lib.oracle_bwd(
+        ctypes.c_int(B), ctypes.c_int(H), ctypes.c_int(d), _p(offsets), _p(pl), _p(cl),
+        _p(Q), _p(K), _p(V), _p(U), _p(ts_),
+        _p(rp), ctypes.c_int(0 if rp is None else len(rp)),
+        _p(rt), ctypes.c_int(0 if rt is None else len(rt)),
+        ctypes.c_double(n_max), ctypes.c_int(norm), ctypes.c_double(eps),
+        _p(grp), ctypes.c_int(n_groups), _p(gm), _p(bt), _p(dY),
+        _p(dQ), _p(dK), _p(dV), _p(dU), _p(drp), _p(drt), _p(dgm), _p(dbt),
+        ctypes.c_int(_threads(nthreads)))
+    if rc != 0:
+        raise ValueError(f"oracle_bwd rejected its input (code {rc})")
+    return {"dQ": dQ, "dK": dK, "dV": dV, "dU": dU, "drab_p": drp, "drab_t": drt,
+            "dgamma": dgm, "dbeta": dbt}
+
+
+def mfalcon(hist_offsets, cand_offsets, K_cache, V_cache, Qc, Kc, Vc, Uc, *, H, d, hist_ts=None,
+            cand_ts=None, rab_p=None, rab_t=None, n_max=1.0, norm=NORM_LN, eps=1e-5,
+            cand_group=None, n_groups=1, gamma=None, beta=None, nthreads=0):
+    """M-FALCON scoring of candidates against cached history K/V. Returns dict
+    with Y, O ([Tc, H*d]), mean, rstd ([Tc])."""
+    lib = _load()
+    ho, co = _i32(hist_offsets), _i32(cand_offsets)
+    B = len(co) - 1
+    Th, Tc = int(ho[-1]), int(co[-1])
+    D = H * d
+    Kh, Vh = (_f64(x).reshape(Th, D) for x in (K_cache, V_cache))
+    Qc, Kc, Vc, Uc = (_f64(x).reshape(Tc, D) for x in (Qc, Kc, Vc, Uc))
+    rp, rt = _f64(rab_p), _f64(rab_t)
+    gm, bt = _f64(gamma), _f64(beta)
+    Y = np.zeros((Tc, D)); O = np.zeros((Tc, D)); mean = np.zeros(Tc); rstd = np.zeros(Tc)
+    hts, cts, grp = _i64(hist_ts), _i64(cand_ts), _u8(cand_group)
+    rc = lib.oracle_mfalcon(
+        ctypes.c_int(B), ctypes.c_int(H), ctypes.c_int(d), _p(ho), _p(co), _p(Kh), _p(Vh), _p(hts),
+        _p(Qc), _p(Kc), _p(Vc), _p(Uc), _p(cts),
+        _p(rp), ctypes.c_int(0 if rp is None else len(rp)),
+        _p(rt), ctypes.c_int(0 if rt is None else len(rt)),
+        ctypes.c_double(n_max), ctypes.c_int(norm), ctypes.c_double(eps),
+        _p(grp), ctypes.c_int(n_groups), _p(gm), _p(bt),
+        _p(Y), _p(O), _p(mean), _p(rstd), ctypes.c_int(_threads(nthreads)))
+    if rc != 0:
+        raise ValueError(f"oracle_mfalcon rejected its input (code {rc})")
+    return {"Y": Y, "O": O, "mean": mean, "rstd": rstd}
+
+
+def classify_tiles(L, P, C, r0, nrows, BN, nkt):
+    """Brute-force kinds (0 absent, 1 partial, 2 full) of key tiles [0, nkt)
+    for query rows [r0, r0+nrows) of a frame (L, P, C)."""
+    kind = np.zeros(max(nkt, 1), dtype=np.int8)
+    _load().oracle_classify_tiles(int(L), int(P), int(C), int(r0), int(nrows), int(BN), int(nkt),
+                                  ctypes.c_void_p(kind.ctypes.data))
+    return kind[:nkt]
+
+
+def _qtile_entry(b, frame_L, P, C, frame_r0, nrows, BN, local_row0):
+    nkt = -(-frame_L // BN)
+    kinds = classify_tiles(frame_L, P, C, frame_r0, nrows, BN, nkt)
+    return {"b": b, "row0": local_row0, "nrows": nrows, "kinds": kinds}
+
+
+def schedule(offsets, BM, BN, prefix_len=None, cand_len=None):
+    """Query-tile schedule of the attention forward: one entry per query tile
+    (sequence b, first row row0, row count nrows, kinds of its key tiles),
+    canonical order (b, row0) ascending."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    out = []
+    for b in range(len(offsets) - 1):
+        L = int(offsets[b + 1] - offsets[b])
+        P = int(prefix_len[b]) if prefix_len is not None else 0
+        C = int(cand_len[b]) if cand_len is not None else 0
+        for r0 in range(0, L, BM):
+            out.append(_qtile_entry(b, L, P, C, r0, min(BM, L - r0), BN, r0))
+    return out
+
+
+def schedule_mfalcon(hist_offsets, cand_offsets, BM, BN, microbatch):
+    """Query-tile schedule of M-FALCON scoring: the candidates of user b are
+    cut into microbatches of `microbatch` candidates (0 = one microbatch), and
+    each microbatch into query tiles of at most BM rows. Row indices are local
+    candidate indices; the tiles are classified in the frame
+    [history | candidates] with the candidate tail as the only segment."""
+    ho = np.asarray(hist_offsets, dtype=np.int64)
+    co = np.asarray(cand_offsets, dtype=np.int64)
+    out = []
+    for b in range(len(co) - 1):
+        n = int(ho[b + 1] - ho[b])
+        m = int(co[b + 1] - co[b])
+        mb = microbatch if microbatch > 0 else max(m, 1)
+        for s in range(0, m, mb):
+            e = min(m, s + mb)
+            for r0 in range(s, e, BM):
+                nrows = min(BM, e - r0)
+                out.append(_qtile_entry(b, n + m, 0, m, n + r0, nrows, BN, r0))
+    return out
+
+
+def lpt_order(entries):
+    """Longest-processing-time order: by number of present key tiles,
+    descending; ties keep the canonical order."""
+    return sorted(range(len(entries)), key=lambda g: (-int(np.count_nonzero(entries[g]["kinds"])), g))

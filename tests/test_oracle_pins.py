@@ -1,0 +1,452 @@
+"""Pins of the CPU oracle against things other than itself: hand-typed mask
+and schedule fixtures, integer bucket boundaries, the L = 1 closed form,
+torch library routines for the dense special cases, exact invariants, torch
+autograd and central finite differences for the backward."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from hstu_jagged_pointwise_attn_amd import synth
+from tests import dense_torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_blocks(name):
+    lines = [l.rstrip("\n") for l in open(os.path.join(GOLDEN, name))]
+    return [l for l in lines if l and not l.startswith("#")]
+
+
+def _masks():
+    out, lines, k = [], _read_blocks("masks.txt"), 0
+    while k < len(lines):
+        l = lines[k]
+        if l.startswith("mask"):
+            kv = dict(x.split("=") for x in l.split()[1:])
+            L, P, C = int(kv["L"]), int(kv["P"]), int(kv["C"])
+            rows = lines[k + 1:k + 1 + L]
+            assert lines[k + 1 + L] == "end"
+            out.append((L, P, C, np.array([[int(c) for c in r] for r in rows])))
+            k += L + 2
+        else:
+            k += 1
+    return out
+
+
+def _positions():
+    out = []
+    for l in _read_blocks("masks.txt"):
+        if l.startswith("pos"):
+            head, vals = l.split(":")
+            kv = dict(x.split("=") for x in head.split()[1:])
+            out.append((int(kv["L"]), int(kv["C"]), [int(v) for v in vals.split()]))
+    return out
+
+
+# ------------------------------------------------------------------ masks
+
+@pytest.mark.parametrize("case", _masks(), ids=lambda c: f"L{c[0]}P{c[1]}C{c[2]}")
+def test_visibility_matches_hand_fixture(oracle_mod, case):
+    L, P, C, expected = case
+    got = np.array([[int(oracle_mod.visible(i, j, L, P, C)) for j in range(L)] for i in range(L)])
+    np.testing.assert_array_equal(got, expected)
+    np.testing.assert_array_equal(dense_torch.block_mask(L, P, C).int().numpy(), expected)
+
+
+@pytest.mark.parametrize("case", _positions(), ids=lambda c: f"L{c[0]}C{c[1]}")
+def test_positions_read_out_through_rab_p(oracle_mod, case):
+    """With Q = 0, V = identity, N_max = 1, no norm and U = 1, the output
+    matrix is the attention matrix itself: O[i, j] = SiLU(rab_p[|pos i - pos j|])
+    on visible pairs. Distinct rab_p entries make each position readable."""
+    L, C, pos = case
+    P = 0
+    n_pos = 16
+    rab_p = np.array([0.25 * k - 1.0 for k in range(n_pos)])
+    Q = np.zeros((L, 1, L)); K = np.random.default_rng(0).normal(size=(L, 1, L))
+    V = np.eye(L).reshape(L, 1, L); U = np.ones((L, 1, L))
+    r = oracle_mod.fwd([0, L], Q, K, V, U, H=1, d=L, cand_len=[C], prefix_len=[P], rab_p=rab_p,
+                       n_max=1.0, norm=oracle_mod.NORM_NONE)
+    for i in range(L):
+        for j in range(L):
+            vis = oracle_mod.visible(i, j, L, P, C)
+            x = rab_p[min(abs(pos[i] - pos[j]), n_pos - 1)]
+            want = x / (1 + math.exp(-x)) if vis else 0.0
+            assert r["O"][i, j] == pytest.approx(want, rel=1e-15, abs=0)
+
+
+# ------------------------------------------------------------------ buckets
+
+def test_time_bucket_integer_boundaries(oracle_mod):
+    for n_tb in (16, 128):
+        cases = [0, 1, -1]
+        for k in range(1, 63):
+            cases += [2 ** k - 1, 2 ** k, 2 ** k + 1, -(2 ** k - 1), -(2 ** k), -(2 ** k + 1)]
+        for dt in cases:
+            want = min(n_tb - 1, max(1, abs(dt)).bit_length() - 1)
+            assert oracle_mod.time_bucket(dt, n_tb) == want, (dt, n_tb)
+
+
+def test_time_bucket_frexp_agrees(oracle_mod):
+    dts = torch.tensor([0, 1, 2, 3, 4, 7, 8, 3599, 3600, 86399, 86400, -5, -(2 ** 40)], dtype=torch.int64)
+    got = [oracle_mod.time_bucket(int(x), 128) for x in dts]
+    assert got == dense_torch.bucket(dts, 128).tolist()
+
+
+# ------------------------------------------------------------------ forward
+
+def test_single_token_closed_form(oracle_mod):
+    """L = 1: y = LN(SiLU(q.k + rab_p[0] + rab_t[0]) v / N_max) * u over all heads."""
+    rng = np.random.default_rng(1)
+    H, d = 2, 4
+    q, k, v, u = (rng.normal(size=(1, H, d)) for _ in range(4))
+    rab_p, rab_t = np.array([0.3, -1.0]), np.array([-0.2, 5.0])
+    r = oracle_mod.fwd([0, 1], q, k, v, u, H=H, d=d, ts=[123], rab_p=rab_p, rab_t=rab_t,
+                       n_max=2.0, norm=oracle_mod.NORM_LN, eps=1e-5)
+    x = []
+    for h in range(H):
+        s = float(np.dot(q[0, h], k[0, h])) + 0.3 - 0.2
+        a = s / (1 + math.exp(-s)) / 2.0
+        x += [a * float(vv) for vv in v[0, h]]
+    mu = sum(x) / len(x)
+    var = sum((t - mu) ** 2 for t in x) / len(x)
+    y = [(t - mu) / math.sqrt(var + 1e-5) * float(uu) for t, uu in zip(x, u.reshape(-1))]
+    np.testing.assert_allclose(r["Y"][0], y, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(r["O"][0], x, rtol=1e-13, atol=0)
+
+
+def _torch_inputs(p):
+    f = lambda t: t.double().clone()
+    return f(p.Q), f(p.K), f(p.V), f(p.U)
+
+
+def _dense_opts(p):
+    return dict(H=p.H, d=p.d, prefix_len=p.prefix_len, cand_len=p.cand_len, ts=p.ts,
+                rab_p=None if p.rab_p is None else torch.tensor(p.rab_p, dtype=torch.float64),
+                rab_t=None if p.rab_t is None else torch.tensor(p.rab_t, dtype=torch.float64),
+                n_max=float(p.n_max), norm=p.norm, eps=p.eps, group=p.group,
+                gamma=None if p.gamma is None else torch.tensor(p.gamma, dtype=torch.float64),
+                beta=None if p.beta is None else torch.tensor(p.beta, dtype=torch.float64))
+
+
+def _oracle_opts(p):
+    return dict(H=p.H, d=p.d, prefix_len=p.prefix_len, cand_len=p.cand_len, ts=p.ts, rab_p=p.rab_p,
+                rab_t=p.rab_t, n_max=p.n_max, norm=p.norm, eps=p.eps, group=p.group,
+                n_groups=p.n_groups, gamma=p.gamma, beta=p.beta)
+
+
+def _small_problems():
+    """Small problems covering every mask kind, rab on/off, the norms."""
+    out = []
+    out.append(synth.custom("causal_rab", [5, 17, 1, 30], H=2, d=8, dtype=torch.float32, wid=11,
+                            std=0.5, n_max=4, norm=synth.NORM_LN, n_pos=12, n_tb=8, rab_std=0.5))
+    L = np.array([12, 20, 7, 9])
+    P = np.array([3, 5, 0, 9]); C = np.array([4, 6, 7, 0])
+    grp = np.concatenate([np.minimum(np.arange(l) * 3 // max(l, 1), 2) for l in L])
+    out.append(synth.custom("mtgr_gln", L, H=3, d=4, dtype=torch.float32, wid=12, std=0.7, n_max=2,
+                            norm=synth.NORM_GLN, prefix_len=P, cand_len=C, group=grp, n_groups=3,
+                            gamma_std=0.3, beta_std=0.3, n_pos=8, n_tb=6, rab_std=0.4))
+    out.append(synth.custom("none_norm", [6, 0, 11], H=1, d=16, dtype=torch.bfloat16, wid=13,
+                            std=0.5, n_max=1, norm=synth.NORM_NONE, cand_len=[2, 0, 5]))
+    return out
+
+
+@pytest.mark.parametrize("p", _small_problems(), ids=lambda p: p.name)
+def test_forward_matches_torch_library_dense(oracle_mod, p):
+    Q, K, V, U = _torch_inputs(p)
+    Yd, Od = dense_torch.forward(p.offsets, Q, K, V, U, **_dense_opts(p))
+    r = oracle_mod.fwd(p.offsets, p.Q.double().numpy(), p.K.double().numpy(), p.V.double().numpy(),
+                       p.U.double().numpy(), **_oracle_opts(p))
+    np.testing.assert_allclose(r["O"], Od.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(r["Y"], Yd.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_zero_queries_give_zero_output(oracle_mod):
+    """Q = 0 with zero rab: S = 0, SiLU(0) = 0, so O = 0 and Y = beta * U."""
+    p = synth.custom("zq", [9, 4, 13], H=2, d=8, dtype=torch.float32, wid=14, std=1.0, n_max=3,
+                     norm=synth.NORM_LN, beta_std=1.0, gamma_std=1.0, cand_len=[3, 0, 5],
+                     n_pos=10, n_tb=5)
+    p.rab_p[:] = 0
+    p.rab_t[:] = 0
+    Q = np.zeros((p.T, p.H, p.d))
+    r = oracle_mod.fwd(p.offsets, Q, p.K.numpy(), p.V.numpy(), p.U.numpy(), **_oracle_opts(p))
+    assert np.all(r["O"] == 0.0)
+    np.testing.assert_array_equal(r["Y"], p.beta[0][None, :] * p.U.double().numpy().reshape(p.T, -1))
+
+
+def test_masked_pairs_contribute_exactly_zero(oracle_mod):
+    """Perturbing K/V of keys a row cannot see leaves that row bit-identical."""
+    L = np.array([10, 16])
+    P = np.array([2, 4]); C = np.array([3, 5])
+    p = synth.custom("mz", L, H=2, d=8, dtype=torch.float32, wid=15, std=0.5, n_max=4,
+                     norm=synth.NORM_NONE, prefix_len=P, cand_len=C, n_pos=8, n_tb=4)
+    base = oracle_mod.fwd(p.offsets, p.Q.numpy(), p.K.numpy(), p.V.numpy(), p.U.numpy(), **_oracle_opts(p))
+    for b in range(2):
+        s, Lb, Pb, Cb = int(p.offsets[b]), int(L[b]), int(P[b]), int(C[b])
+        for j in range(Lb):
+            K2, V2 = p.K.numpy().copy(), p.V.numpy().copy()
+            K2[s + j] += 3.0
+            V2[s + j] -= 7.0
+            r = oracle_mod.fwd(p.offsets, p.Q.numpy(), K2, V2, p.U.numpy(), **_oracle_opts(p))
+            for i in range(Lb):
+                if not oracle_mod.visible(i, j, Lb, Pb, Cb):
+                    np.testing.assert_array_equal(r["O"][s + i], base["O"][s + i])
+                    np.testing.assert_array_equal(r["Y"][s + i], base["Y"][s + i])
+
+
+def test_none_norm_scales_exactly_with_power_of_two_nmax(oracle_mod):
+    p = synth.custom("sc", [7, 12], H=2, d=8, dtype=torch.float32, wid=16, std=0.5, n_max=1,
+                     norm=synth.NORM_NONE, n_pos=6, n_tb=4, cand_len=[2, 3])
+    a = oracle_mod.fwd(p.offsets, p.Q.numpy(), p.K.numpy(), p.V.numpy(), p.U.numpy(),
+                       **{**_oracle_opts(p), "n_max": 1})
+    b = oracle_mod.fwd(p.offsets, p.Q.numpy(), p.K.numpy(), p.V.numpy(), p.U.numpy(),
+                       **{**_oracle_opts(p), "n_max": 8})
+    np.testing.assert_array_equal(a["O"] / 8.0, b["O"])
+
+
+# ------------------------------------------------------------------ M-FALCON
+
+def _mf_small(with_rab=True, users=3, n=37, m=19, H=2, d=8):
+    mf = synth.mfalcon_bf16(users=users, n_hist=n, m_cand=m, microbatch=5, H=H, d=d, with_rab=with_rab)
+    if with_rab:
+        mf.rab_p = mf.rab_p[:64].copy()
+    return mf
+
+
+def _mf_oracle(oracle_mod, mf, cand_rows=None, cand_offsets=None):
+    f = lambda t: t.double().numpy()
+    sel = slice(None) if cand_rows is None else cand_rows
+    cts = None if mf.cand_ts is None else mf.cand_ts[sel]
+    return oracle_mod.mfalcon(mf.hist_offsets, mf.cand_offsets if cand_offsets is None else cand_offsets,
+                              f(mf.K_cache), f(mf.V_cache), f(mf.Qc)[sel], f(mf.Kc)[sel], f(mf.Vc)[sel],
+                              f(mf.Uc)[sel], H=mf.H, d=mf.d, hist_ts=mf.hist_ts, cand_ts=cts,
+                              rab_p=mf.rab_p, rab_t=mf.rab_t, n_max=mf.n_max, norm=mf.norm, eps=mf.eps)
+
+
+def test_mfalcon_cached_equals_full_pass(oracle_mod):
+    """Scoring against cached history K/V equals the candidate rows of one
+    full pass over [history | candidates] with the candidate mask."""
+    mf = _mf_small()
+    got = _mf_oracle(oracle_mod, mf)
+    ho, co = mf.hist_offsets, mf.cand_offsets
+    f = lambda t: t.double().numpy()
+    Qs, Ks, Vs, Us, ts, lengths, cand = [], [], [], [], [], [], []
+    for b in range(mf.B):
+        hs, he, cs, ce = ho[b], ho[b + 1], co[b], co[b + 1]
+        Qs += [f(mf.Q_hist)[hs:he], f(mf.Qc)[cs:ce]]
+        Ks += [f(mf.K_cache)[hs:he], f(mf.Kc)[cs:ce]]
+        Vs += [f(mf.V_cache)[hs:he], f(mf.Vc)[cs:ce]]
+        Us += [f(mf.U_hist)[hs:he], f(mf.Uc)[cs:ce]]
+        ts += [mf.hist_ts[hs:he], mf.cand_ts[cs:ce]]
+        lengths.append(he - hs + ce - cs)
+        cand.append(ce - cs)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    full = oracle_mod.fwd(off, np.concatenate(Qs), np.concatenate(Ks), np.concatenate(Vs),
+                          np.concatenate(Us), H=mf.H, d=mf.d, cand_len=cand, ts=np.concatenate(ts),
+                          rab_p=mf.rab_p, rab_t=mf.rab_t, n_max=mf.n_max, norm=mf.norm, eps=mf.eps)
+    rows = np.concatenate([np.arange(off[b + 1] - cand[b], off[b + 1]) for b in range(mf.B)])
+    np.testing.assert_array_equal(got["Y"], full["Y"][rows])
+    np.testing.assert_array_equal(got["O"], full["O"][rows])
+
+
+def test_mfalcon_microbatches_equal_one_pass(oracle_mod):
+    mf = _mf_small()
+    full = _mf_oracle(oracle_mod, mf)
+    co = mf.cand_offsets
+    for mb in (1, 4, 7):
+        for start in range(0, int(np.max(np.diff(co))), mb):
+            rows, counts = [], []
+            for b in range(mf.B):
+                s, e = co[b] + start, min(co[b + 1], co[b] + start + mb)
+                rows += list(range(s, max(s, e)))
+                counts.append(max(0, e - s))
+            sub_off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+            r = _mf_oracle(oracle_mod, mf, cand_rows=np.array(rows), cand_offsets=sub_off)
+            np.testing.assert_array_equal(r["Y"], full["Y"][rows])
+
+
+def test_mfalcon_candidate_permutation_permutes_outputs(oracle_mod):
+    mf = _mf_small()
+    base = _mf_oracle(oracle_mod, mf)
+    rng = np.random.default_rng(5)
+    perm = np.concatenate([mf.cand_offsets[b] + rng.permutation(mf.cand_offsets[b + 1] - mf.cand_offsets[b])
+                           for b in range(mf.B)])
+    r = _mf_oracle(oracle_mod, mf, cand_rows=perm)
+    np.testing.assert_array_equal(r["Y"], base["Y"][perm])
+
+
+# ------------------------------------------------------------------ backward
+
+def _grad_problems():
+    out = []
+    out.append(synth.custom("g_causal", [6, 11, 1], H=2, d=4, dtype=torch.float32, wid=21, std=0.6,
+                            n_max=2, norm=synth.NORM_LN, n_pos=8, n_tb=6, rab_std=0.5,
+                            gamma_std=0.3, beta_std=0.3, with_dy=True))
+    L = np.array([9, 13])
+    grp = np.concatenate([np.arange(l) % 3 for l in L])
+    out.append(synth.custom("g_mtgr", L, H=2, d=4, dtype=torch.float32, wid=22, std=0.6, n_max=1,
+                            norm=synth.NORM_GLN, prefix_len=[3, 4], cand_len=[2, 5], group=grp,
+                            n_groups=3, gamma_std=0.3, beta_std=0.3, n_pos=8, n_tb=6, rab_std=0.5,
+                            with_dy=True))
+    out.append(synth.custom("g_none", [7, 5], H=1, d=8, dtype=torch.float32, wid=23, std=0.6, n_max=3,
+                            norm=synth.NORM_NONE, cand_len=[3, 0], with_dy=True))
+    return out
+
+
+@pytest.mark.parametrize("p", _grad_problems(), ids=lambda p: p.name)
+def test_backward_matches_torch_autograd(oracle_mod, p):
+    Q, K, V, U = (t.requires_grad_(True) for t in _torch_inputs(p))
+    opts = _dense_opts(p)
+    params = [opts[k] for k in ("rab_p", "rab_t", "gamma", "beta") if opts[k] is not None]
+    for t in params:
+        t.requires_grad_(True)
+    Y, _ = dense_torch.forward(p.offsets, Q, K, V, U, **opts)
+    (Y * p.dY.double()).sum().backward()
+    r = oracle_mod.bwd(p.offsets, p.Q.numpy(), p.K.numpy(), p.V.numpy(), p.U.numpy(), p.dY.numpy(),
+                       **_oracle_opts(p))
+    T, D = p.T, p.H * p.d
+    for name, t in (("dQ", Q), ("dK", K), ("dV", V), ("dU", U)):
+        np.testing.assert_allclose(r[name], t.grad.reshape(T, D).numpy(), rtol=1e-9, atol=1e-12, err_msg=name)
+    for name, key in (("drab_p", "rab_p"), ("drab_t", "rab_t"), ("dgamma", "gamma"), ("dbeta", "beta")):
+        if opts[key] is not None:
+            np.testing.assert_allclose(r[name], opts[key].grad.numpy(), rtol=1e-9, atol=1e-12, err_msg=name)
+
+
+@pytest.mark.parametrize("p", _grad_problems(), ids=lambda p: p.name)
+def test_backward_matches_central_differences_of_forward(oracle_mod, p):
+    """<grad, delta> against (f(x + h delta) - f(x - h delta)) / 2h with
+    f = sum(Y * dY) evaluated by oracle_fwd itself."""
+    base = {k: v for k, v in dict(Q=p.Q.numpy(), K=p.K.numpy(), V=p.V.numpy(), U=p.U.numpy()).items()}
+    base = {k: np.asarray(v, dtype=np.float64) for k, v in base.items()}
+    extra = {k: np.asarray(getattr(p, k), dtype=np.float64) for k in ("rab_p", "rab_t", "gamma", "beta")
+             if getattr(p, k) is not None}
+    dY = p.dY.double().numpy()
+    opts = _oracle_opts(p)
+
+    def f(vals):
+        o = dict(opts)
+        for k in extra:
+            o[k] = vals[k]
+        return float((oracle_mod.fwd(p.offsets, vals["Q"], vals["K"], vals["V"], vals["U"], **o)["Y"] * dY).sum())
+
+    g = oracle_mod.bwd(p.offsets, base["Q"], base["K"], base["V"], base["U"], dY, **opts)
+    gname = {"Q": "dQ", "K": "dK", "V": "dV", "U": "dU", "rab_p": "drab_p", "rab_t": "drab_t",
+             "gamma": "dgamma", "beta": "dbeta"}
+    rng = np.random.default_rng(3)
+    allv = {**base, **extra}
+    h = 1e-5
+    for k in allv:
+        for _ in range(2):
+            delta = rng.normal(size=allv[k].shape)
+            plus = {**allv, k: allv[k] + h * delta}
+            minus = {**allv, k: allv[k] - h * delta}
+            fd = (f(plus) - f(minus)) / (2 * h)
+            an = float((g[gname[k]].reshape(delta.shape) * delta).sum())
+            assert an == pytest.approx(fd, rel=1e-6, abs=1e-9), k
+
+
+@pytest.mark.parametrize("p", _grad_problems(), ids=lambda p: p.name)
+def test_backward_identities(oracle_mod, p):
+    """<Q, dQ> = <K, dK> per (sequence, head); sum(drab_p) = sum(drab_t);
+    LN backward makes every token's dO sum to zero (checked through dQ/dK
+    indirectly via the first identity)."""
+    r = oracle_mod.bwd(p.offsets, p.Q.numpy(), p.K.numpy(), p.V.numpy(), p.U.numpy(), p.dY.numpy(),
+                       **_oracle_opts(p))
+    T, H, d = p.T, p.H, p.d
+    Q = p.Q.double().numpy().reshape(T, H, d); K = p.K.double().numpy().reshape(T, H, d)
+    dQ = r["dQ"].reshape(T, H, d); dK = r["dK"].reshape(T, H, d)
+    for b in range(p.B):
+        s, e = p.offsets[b], p.offsets[b + 1]
+        for h in range(H):
+            a = float((Q[s:e, h] * dQ[s:e, h]).sum()); c = float((K[s:e, h] * dK[s:e, h]).sum())
+            assert a == pytest.approx(c, rel=1e-10, abs=1e-13)
+    if r["drab_p"] is not None and r["drab_t"] is not None:
+        assert r["drab_p"].sum() == pytest.approx(r["drab_t"].sum(), rel=1e-10, abs=1e-13)
+
+
+# ------------------------------------------------------------------ schedule
+
+def _schedule_fixture():
+    lines = _read_blocks("schedule.txt")
+    out, k = [], 0
+    while k < len(lines):
+        head = lines[k].split()
+        k += 1
+        rows = []
+        while lines[k] != "end":
+            rows.append([int(x) for x in lines[k].split()])
+            k += 1
+        k += 1
+        out.append((head[0], [int(x) for x in head[1:]], rows))
+    return out
+
+
+@pytest.mark.parametrize("case", _schedule_fixture(), ids=lambda c: c[0] + "_" + "_".join(map(str, c[1])))
+def test_schedule_matches_hand_fixture(oracle_mod, case):
+    kind, args, rows = case
+    if kind == "attn":
+        L, P, C, BM, BN = args
+        got = oracle_mod.schedule([0, L], BM, BN, prefix_len=[P], cand_len=[C])
+    else:
+        n, m, mb, BM, BN = args
+        got = oracle_mod.schedule_mfalcon([0, n], [0, m], BM, BN, mb)
+    assert len(got) == len(rows)
+    for e, want in zip(got, rows):
+        assert [e["row0"], e["nrows"]] + list(map(int, e["kinds"])) == want
+
+
+def _hi(i, L, P, C):
+    """Exclusive end of the keys row i carries (a prefix of the sequence)."""
+    E = L - C
+    return P if i < P else (i + 1 if i < E else E)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_schedule_tiles_form_prefixes(oracle_mod, seed):
+    """The brute-force classification always yields present tiles [0, nk) and
+    FULL tiles [0, nf) with nk = ceil(hi(last row)/BN), nf = floor(hi(first row)/BN)."""
+    rng = np.random.default_rng(seed)
+    for _ in range(30):
+        L = int(rng.integers(1, 300))
+        P = int(rng.integers(0, L + 1))
+        C = int(rng.integers(0, L - P + 1))
+        BM, BN = int(rng.choice([16, 32, 64, 128])), int(rng.choice([16, 32, 64]))
+        for e in oracle_mod.schedule([0, L], BM, BN, prefix_len=[P], cand_len=[C]):
+            k = list(map(int, e["kinds"]))
+            nk = sum(1 for x in k if x)
+            nf = sum(1 for x in k if x == 2)
+            assert all(x != 0 for x in k[:nk]) and all(x == 0 for x in k[nk:])
+            assert all(x == 2 for x in k[:nf]) and all(x == 1 for x in k[nf:nk])
+            r0, r1 = e["row0"], e["row0"] + e["nrows"] - 1
+            assert nk == -(-_hi(r1, L, P, C) // BN)
+            assert nf == _hi(r0, L, P, C) // BN
+
+
+def test_lpt_order_is_stable_longest_first(oracle_mod):
+    ent = oracle_mod.schedule([0, 130, 300, 301], 64, 64)
+    order = oracle_mod.lpt_order(ent)
+    nks = [int(np.count_nonzero(ent[g]["kinds"])) for g in order]
+    assert nks == sorted(nks, reverse=True)
+    for a, b in zip(order, order[1:]):
+        if nks[order.index(a)] == nks[order.index(b)]:
+            assert a < b
+
+
+# ------------------------------------------------------------------ inputs
+
+def test_stochastic_length_cap_matches_page():
+    for l in _read_blocks("stochastic_length.txt"):
+        n, alpha, cap = l.split()
+        assert synth.stochastic_length_cap(int(n), float(alpha)) == int(cap)
+
+
+def test_generators_are_deterministic():
+    a, b = synth.tiny_fp32(), synth.tiny_fp32()
+    assert np.array_equal(a.offsets, b.offsets)
+    assert torch.equal(a.Q, b.Q) and np.array_equal(a.ts, b.ts)
+    t = synth.train_bf16(False)
+    assert abs(t.lengths.mean() - 776) < 150
+    lit = synth.train_bf16(True)
+    assert lit.lengths.max() <= 776
