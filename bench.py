@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of the HSTU jagged pointwise-attention hot path on one MI355X.
+
+One step is one pass of the hot path over one synthetic batch, through the
+C ABI (hstu_attn_fwd: tile scheduler -> attention kernel -> Norm * U
+epilogue; for --workload long also hstu_attn_bwd; for mfalcon
+hstu_mfalcon_score). Inputs are resident in HBM before the timed region.
+
+The metric is useful TFLOP/s: 4*d FLOPs per visible (query, key) pair and
+head in the forward (2*d for Q.K, 2*d for A.V) and 8*d in the backward;
+masked pairs, the recomputation in the backward and the elementwise work are
+not counted. Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0
+
+METRIC = "HSTU jagged attention useful TFLOP/s + % of bf16 MFMA peak (1 MI355X)"
+
+WORKLOAD_TEXT = {
+    "train": "HSTU training-shape fwd bf16: 128 jagged sequences, truncated Pareto(1.2) lengths on "
+             "[lo, 4096] with mean 776, 4 heads, d=128, causal, rab_p 4096 + rab_t 128, LN, N_max 4096",
+    "train_literal": "HSTU training-shape fwd bf16: 128 sequences, Pareto(1.2) on [16, 4096] capped at the "
+                     "Stochastic Length budget 776, 4 heads, d=128, causal, rab_p/rab_t, LN, N_max 4096",
+    "mtgr": "MTGR hybrid-mask fwd bf16: 64 users [16 static | history 64-3000 | 0-64 real-time | 32-200 "
+            "candidates], 6 heads, d=128, Group LayerNorm (4 groups), N_max 3280",
+    "mfalcon": "M-FALCON ranking bf16: 16 users x 2048 cached history K/V x 1024 candidates, microbatch 256, "
+               "8 heads, d=128, LN, N_max 3072",
+    "long": "Long-sequence fwd+bwd bf16: 32 sequences, lognormal lengths (median 2048) in [256, 8192], "
+            "8 heads, d=128, causal, rab_p 8192 + rab_t 128, LN, N_max 8192",
+    "tiny_fp32": "Tiny fp32 causal fwd: 4 sequences U{8..64}, 2 heads, d=32, rab_p 64 + rab_t 16, LN, N_max 64",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_pairs(lengths, prefix=None, cand=None):
+    """Visible (query, key) pairs per head, candidate self pairs included."""
+    tot = 0
+    for b, L in enumerate(lengths):
+        L = int(L)
+        P = int(prefix[b]) if prefix is not None else 0
+        C = int(cand[b]) if cand is not None else 0
+        E = L - C
+        tot += P * P + (E * (E + 1) - P * (P + 1)) // 2 + C * (E + 1)
+    return tot
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "hstu_jagged_pointwise_attn_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload, kernel):
+    """HBM bytes per launch of `kernel` from profiles/traffic.json when it was
+    measured on the current kernel sources, else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(p, flops_per_pair, kind, budget_s):
+    """Time the CPU oracle on a bounded, deterministic sample of the workload:
+    a short calibration run gives the oracle's rate, then one timed run over
+    a sample sized to about budget_s seconds."""
+    import numpy as np
+
+    import oracle
+    from hstu_jagged_pointwise_attn_amd import synth
+    from tests.common import oracle_bwd, oracle_fwd, oracle_mfalcon
+
+    oracle.build(force=False)
+    cores = os.cpu_count() or 1
+    if kind == "mfalcon":
+        mf = p
+        ho, co = mf.hist_offsets, mf.cand_offsets
+        order = list(range(mf.B))
+        unit_pairs = [int(co[u + 1] - co[u]) * (int(ho[u + 1] - ho[u]) + 1) * mf.H for u in order]
+        label = "users"
+
+        def run(users):
+            hrows = np.concatenate([np.arange(ho[u], ho[u + 1]) for u in users])
+            crows = np.concatenate([np.arange(co[u], co[u + 1]) for u in users])
+            sub = synth.MFalconProblem(
+                name="s", dtype=mf.dtype, H=mf.H, d=mf.d,
+                hist_offsets=np.concatenate([[0], np.cumsum([ho[u + 1] - ho[u] for u in users])]).astype(np.int32),
+                cand_offsets=np.concatenate([[0], np.cumsum([co[u + 1] - co[u] for u in users])]).astype(np.int32),
+                K_cache=mf.K_cache[hrows], V_cache=mf.V_cache[hrows], Qc=mf.Qc[crows], Kc=mf.Kc[crows],
+                Vc=mf.Vc[crows], Uc=mf.Uc[crows], n_max=mf.n_max, microbatch=mf.microbatch, norm=mf.norm)
+            t0 = time.perf_counter()
+            oracle_mfalcon(sub)
+            return time.perf_counter() - t0
+    else:
+        order = np.random.default_rng(12345).permutation(p.B).tolist()
+        unit_pairs = [visible_pairs([p.lengths[s]], None if p.prefix_len is None else [p.prefix_len[s]],
+                                    None if p.cand_len is None else [p.cand_len[s]]) * p.H for s in order]
+        label = "sequences"
+
+        def run(seqs):
+            sub = synth.subbatch(p, seqs)
+            t0 = time.perf_counter()
+            oracle_fwd(sub)
+            if kind == "fwdbwd":
+                oracle_bwd(sub)
+            return time.perf_counter() - t0
+
+    def take(target):
+        n, acc = 0, 0
+        while n < len(order) and (acc < target or n == 0):
+            acc += unit_pairs[n]
+            n += 1
+        return n, acc
+
+    n0, pairs0 = take(min(sum(unit_pairs), 2e7))
+    t0 = run(order[:n0])
+    rate = pairs0 / max(t0, 1e-6)
+    n1, pairs1 = take(rate * budget_s)
+    t1 = run(order[:n1])
+    value = flops_per_pair * pairs1 / t1 / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n1} of {len(order)} {label} in a seeded order ({pairs1} visible pairs x heads); "
+                      f"{t1:.1f} s of fp64 oracle time with OpenMP on {cores} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="train", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from hstu_jagged_pointwise_attn_amd import _lib, api, device, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    wl = args.workload
+    log(f"[bench] generating workload {wl}")
+    if wl == "mfalcon":
+        src = synth.mfalcon_bf16()
+        ns = device.upload_mfalcon(src)
+        pairs = sum(int(np.diff(src.cand_offsets)[u]) * (int(np.diff(src.hist_offsets)[u]) + 1)
+                    for u in range(src.B)) * src.H
+        out = device.run_mfalcon(ns)
+        ws = out.ws
+
+        def step():
+            device.run_mfalcon(ns, Yc=out.Y, Oc=out.O, mean=out.mean, rstd=out.rstd, ws=ws)
+        flops = 4.0 * src.d * pairs
+        kind = "mfalcon"
+        dtype = "bf16"
+        shape = {"users": src.B, "history": int(np.diff(src.hist_offsets)[0]),
+                 "candidates": int(np.diff(src.cand_offsets)[0]), "microbatch": src.microbatch,
+                 "heads": src.H, "d": src.d}
+    else:
+        src = synth.WORKLOADS[wl]()
+        ns = device.upload(src)
+        pairs = visible_pairs(src.lengths, src.prefix_len, src.cand_len) * src.H
+        out = device.run_fwd(ns)
+        ws = out.ws
+        if wl == "long":
+            g = api.attn_bwd(ns.problem, ns.Q, ns.K, ns.V, ns.U, out.O, out.mean, out.rstd, ns.dY)
+            bws = g.ws
+
+            def step():
+                api.attn_fwd(ns.problem, ns.Q, ns.K, ns.V, ns.U, Y=out.Y, O=out.O, mean=out.mean, rstd=out.rstd,
+                             ws=ws)
+                api.attn_bwd(ns.problem, ns.Q, ns.K, ns.V, ns.U, out.O, out.mean, out.rstd, ns.dY, dQ=g.dQ, dK=g.dK,
+                             dV=g.dV, dU=g.dU, d_rab_p=g.d_rab_p, d_rab_t=g.d_rab_t, d_gamma=g.d_gamma,
+                             d_beta=g.d_beta, ws=bws)
+            flops = 12.0 * src.d * pairs
+            kind = "fwdbwd"
+        else:
+            def step():
+                api.attn_fwd(ns.problem, ns.Q, ns.K, ns.V, ns.U, Y=out.Y, O=out.O, mean=out.mean, rstd=out.rstd,
+                             ws=ws)
+            flops = 4.0 * src.d * pairs
+            kind = "fwd"
+        dtype = "f32" if src.dtype == torch.float32 else "bf16"
+        shape = {"batch": src.B, "tokens": src.T, "mean_len": round(float(src.lengths.mean()), 1),
+                 "max_len": src.max_len, "heads": src.H, "d": src.d}
+
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.4f} ms/step, {value:.2f} useful TFLOP/s")
+
+    # Dominant kernel: timed per launch with HIP events on its launch stream.
+    dom = _lib.HSTU_KERNEL_ATTN_BWD if kind == "fwdbwd" else _lib.HSTU_KERNEL_ATTN_FWD
+    dom_name = "attn_bwd" if kind == "fwdbwd" else "attn_fwd"
+    api.kernel_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    per = {}
+    for kid, kname in ((_lib.HSTU_KERNEL_SCHED, "sched"), (_lib.HSTU_KERNEL_ATTN_FWD, "attn_fwd"),
+                       (_lib.HSTU_KERNEL_NORM_FWD, "norm_fwd"), (_lib.HSTU_KERNEL_NORM_BWD, "norm_bwd"),
+                       (_lib.HSTU_KERNEL_ATTN_BWD, "attn_bwd"), (_lib.HSTU_KERNEL_AUX, "aux")):
+        tms, n = api.kernel_timing_read(kid)
+        if n:
+            per[kname] = tms / n
+    api.kernel_timing(False)
+    log("[bench] per-launch ms: " + ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
+    dom_ms = per.get(dom_name)
+    dom_flops = (8.0 if kind == "fwdbwd" else 4.0) * (src.d) * pairs
+    peak = PEAK_F32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms else None
+    roofline = {"bound": "mfma" if dtype == "bf16" else "alu", "achieved": achieved, "peak": peak,
+                "unit": "TFLOP/s", "frac": (achieved / peak) if achieved else None,
+                "traffic": traffic_from_profiles(wl, dom_name), "kernel": dom_name,
+                "kernel_ms": dom_ms, "per_kernel_ms": per}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(src, 12.0 * src.d if kind == "fwdbwd" else 4.0 * src.d, kind, args.cpu_seconds)
+        log(f"[bench] CPU oracle {cpu['value']:.5f} TFLOP/s")
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded generators; no dataset)",
+        "config": {"workload": WORKLOAD_TEXT[wl], "name": wl, "step": kind, **shape,
+                   "useful_tflop_per_step": flops / 1e12, "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

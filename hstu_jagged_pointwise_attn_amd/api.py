@@ -1,0 +1,223 @@
+"""Torch-facing binding of libhstu.so: argument checking and marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; torch only
+provides device memory and the current stream. Functions mirror the C entry
+points of include/hstu.h (hstu_attn_fwd, hstu_attn_bwd, hstu_mfalcon_score,
+hstu_schedule_export, hstu_get_device_status).
+"""
+from __future__ import annotations
+
+import ctypes
+from types import SimpleNamespace
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+from ._lib import (HSTU_BF16, HSTU_F32, HSTU_NORM_GLN, HSTU_NORM_LN, HSTU_NORM_NONE,  # noqa: F401
+                   HSTU_OP_BWD, HSTU_OP_FWD, HSTU_OP_MFALCON, HSTUError)
+
+_DTYPES = {torch.bfloat16: HSTU_BF16, torch.float32: HSTU_F32}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype=None, device=None, numel=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A 256-byte aligned uint8 device buffer of at least nbytes."""
+    raw = torch.empty(int(nbytes) + 256, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % 256
+    return raw[off:off + int(nbytes)]
+
+
+def problem(offsets: torch.Tensor, *, H: int, d: int, dtype: torch.dtype, total_tokens: int,
+            max_len: int, n_max: int, prefix_len=None, cand_len=None, timestamps=None, rab_p=None,
+            rab_t=None, norm=HSTU_NORM_LN, eps=1e-5, token_group=None, n_groups=1, gamma=None,
+            beta=None):
+    """Build the hstu_problem_t of a jagged batch (device tensors; host scalars)."""
+    dev = offsets.device
+    B = offsets.numel() - 1
+    _need(offsets, "offsets", torch.int32, dev)
+    _need(prefix_len, "prefix_len", torch.int32, dev, B)
+    _need(cand_len, "cand_len", torch.int32, dev, B)
+    _need(timestamps, "timestamps", torch.int64, dev, total_tokens)
+    _need(rab_p, "rab_p", torch.float32, dev)
+    _need(rab_t, "rab_t", torch.float32, dev)
+    _need(token_group, "token_group", torch.uint8, dev, total_tokens)
+    G = n_groups if norm == HSTU_NORM_GLN else 1
+    _need(gamma, "gamma", torch.float32, dev, G * H * d)
+    _need(beta, "beta", torch.float32, dev, G * H * d)
+    if dtype not in _DTYPES:
+        raise TypeError(f"dtype {dtype} not supported (bfloat16, float32)")
+    p = L.Problem()
+    p.B, p.H, p.d, p.dtype = B, H, d, _DTYPES[dtype]
+    p.total_tokens, p.max_len, p.n_max = int(total_tokens), int(max_len), int(n_max)
+    p.offsets, p.prefix_len, p.cand_len, p.timestamps = (
+        _ptr(offsets), _ptr(prefix_len), _ptr(cand_len), _ptr(timestamps))
+    p.rab_p, p.rab_t = _ptr(rab_p), _ptr(rab_t)
+    p.n_pos = 0 if rab_p is None else rab_p.numel()
+    p.n_tb = 0 if rab_t is None else rab_t.numel()
+    p.norm, p.eps = int(norm), float(eps)
+    p.token_group, p.n_groups = _ptr(token_group), int(n_groups)
+    p.gamma, p.beta = _ptr(gamma), _ptr(beta)
+    # keep the tensors alive as long as the struct
+    p._keep = (offsets, prefix_len, cand_len, timestamps, rab_p, rab_t, token_group, gamma, beta)
+    return p
+
+
+def workspace_size(p, op, microbatch=0, hist_max_len=0, hist_tokens=0) -> int:
+    n = ctypes.c_size_t(0)
+    L.check(L.lib().hstu_workspace_size(ctypes.byref(p), op, microbatch, hist_max_len, hist_tokens,
+                                        ctypes.byref(n)))
+    return int(n.value)
+
+
+def tile_shape(p, op=HSTU_OP_FWD):
+    bm, bn = ctypes.c_int32(0), ctypes.c_int32(0)
+    L.check(L.lib().hstu_tile_shape(ctypes.byref(p), op, ctypes.byref(bm), ctypes.byref(bn)))
+    return bm.value, bn.value
+
+
+def attn_fwd(p, Q, K, V, U, *, Y=None, O=None, mean=None, rstd=None, ws=None, stream=None):
+    """hstu_attn_fwd. Q/K/V/U: [T, H, d] in the problem's dtype. Returns a
+    namespace with Y, O ([T, H*d]), mean, rstd ([T] fp32) and ws."""
+    T, D = p.total_tokens, p.H * p.d
+    dev = Q.device
+    dt = Q.dtype
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (U, "U")):
+        _need(t, n, dt, dev, T * D)
+    if _DTYPES.get(dt) != p.dtype:
+        raise TypeError("tensor dtype differs from the problem's dtype")
+    Y = torch.empty(T, D, dtype=dt, device=dev) if Y is None else Y
+    O = torch.empty(T, D, dtype=dt, device=dev) if O is None else O
+    mean = torch.empty(T, dtype=torch.float32, device=dev) if mean is None else mean
+    rstd = torch.empty(T, dtype=torch.float32, device=dev) if rstd is None else rstd
+    for t, n in ((Y, "Y"), (O, "O")):
+        _need(t, n, dt, dev, T * D)
+    _need(mean, "mean", torch.float32, dev, T)
+    _need(rstd, "rstd", torch.float32, dev, T)
+    if ws is None:
+        ws = workspace(workspace_size(p, HSTU_OP_FWD), dev)
+    L.check(L.lib().hstu_attn_fwd(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(U), _ptr(Y), _ptr(O),
+                                  _ptr(mean), _ptr(rstd), _ptr(ws), ws.numel(), _stream(stream)))
+    return SimpleNamespace(Y=Y, O=O, mean=mean, rstd=rstd, ws=ws)
+
+
+def attn_bwd(p, Q, K, V, U, O, mean, rstd, dY, *, dQ=None, dK=None, dV=None, dU=None, d_rab_p=None,
+             d_rab_t=None, d_gamma=None, d_beta=None, want_affine=True, ws=None, stream=None):
+    """hstu_attn_bwd. Returns a namespace with dQ, dK, dV, dU ([T, H, d]),
+    d_rab_p, d_rab_t, d_gamma, d_beta (fp32, None when not applicable)."""
+    T, D = p.total_tokens, p.H * p.d
+    dev, dt = Q.device, Q.dtype
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (U, "U"), (O, "O"), (dY, "dY")):
+        _need(t, n, dt, dev, T * D)
+    _need(mean, "mean", torch.float32, dev, T)
+    _need(rstd, "rstd", torch.float32, dev, T)
+    shape = (T, p.H, p.d)
+    dQ = torch.empty(shape, dtype=dt, device=dev) if dQ is None else dQ
+    dK = torch.empty(shape, dtype=dt, device=dev) if dK is None else dK
+    dV = torch.empty(shape, dtype=dt, device=dev) if dV is None else dV
+    dU = torch.empty(shape, dtype=dt, device=dev) if dU is None else dU
+    if p.rab_p and d_rab_p is None:
+        d_rab_p = torch.empty(p.n_pos, dtype=torch.float32, device=dev)
+    if p.rab_t and d_rab_t is None:
+        d_rab_t = torch.empty(p.n_tb, dtype=torch.float32, device=dev)
+    G = p.n_groups if p.norm == HSTU_NORM_GLN else 1
+    if want_affine and p.gamma and d_gamma is None:
+        d_gamma = torch.empty(G, D, dtype=torch.float32, device=dev)
+    if want_affine and p.beta and d_beta is None:
+        d_beta = torch.empty(G, D, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(workspace_size(p, HSTU_OP_BWD), dev)
+    L.check(L.lib().hstu_attn_bwd(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(U), _ptr(O), _ptr(mean),
+                                  _ptr(rstd), _ptr(dY), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dU),
+                                  _ptr(d_rab_p), _ptr(d_rab_t), _ptr(d_gamma), _ptr(d_beta), _ptr(ws),
+                                  ws.numel(), _stream(stream)))
+    return SimpleNamespace(dQ=dQ, dK=dK, dV=dV, dU=dU, d_rab_p=d_rab_p, d_rab_t=d_rab_t, d_gamma=d_gamma,
+                           d_beta=d_beta, ws=ws)
+
+
+def mfalcon_score(cand_p, hist_offsets, hist_tokens, hist_max_len, K_cache, V_cache, Qc, Kc, Vc, Uc, *,
+                  hist_ts=None, microbatch=0, Yc=None, Oc=None, mean=None, rstd=None, ws=None, stream=None):
+    """hstu_mfalcon_score. cand_p describes the candidates (offsets over Tc
+    candidate tokens). Returns a namespace with Yc, Oc, mean, rstd, ws."""
+    Tc, D = cand_p.total_tokens, cand_p.H * cand_p.d
+    dev, dt = Qc.device, Qc.dtype
+    for t, n in ((Qc, "Qc"), (Kc, "Kc"), (Vc, "Vc"), (Uc, "Uc")):
+        _need(t, n, dt, dev, Tc * D)
+    for t, n in ((K_cache, "K_cache"), (V_cache, "V_cache")):
+        _need(t, n, dt, dev, int(hist_tokens) * D)
+    _need(hist_offsets, "hist_offsets", torch.int32, dev, cand_p.B + 1)
+    _need(hist_ts, "hist_ts", torch.int64, dev, int(hist_tokens))
+    Yc = torch.empty(Tc, D, dtype=dt, device=dev) if Yc is None else Yc
+    Oc = torch.empty(Tc, D, dtype=dt, device=dev) if Oc is None else Oc
+    mean = torch.empty(Tc, dtype=torch.float32, device=dev) if mean is None else mean
+    rstd = torch.empty(Tc, dtype=torch.float32, device=dev) if rstd is None else rstd
+    if ws is None:
+        ws = workspace(workspace_size(cand_p, HSTU_OP_MFALCON, microbatch, hist_max_len, hist_tokens), dev)
+    L.check(L.lib().hstu_mfalcon_score(
+        ctypes.byref(cand_p), _ptr(hist_offsets), int(hist_tokens), int(hist_max_len), _ptr(K_cache),
+        _ptr(V_cache), _ptr(hist_ts), _ptr(Qc), _ptr(Kc), _ptr(Vc), _ptr(Uc), int(microbatch), _ptr(Yc),
+        _ptr(Oc), _ptr(mean), _ptr(rstd), _ptr(ws), ws.numel(), _stream(stream)))
+    return SimpleNamespace(Y=Yc, O=Oc, mean=mean, rstd=rstd, ws=ws)
+
+
+def schedule_export(p, op=HSTU_OP_FWD, hist_offsets=None, hist_tokens=0, hist_max_len=0, microbatch=0,
+                    stream=None):
+    """Run only the tile scheduler and return (qtile_off [B+1], tiles [N, 4])
+    as numpy int32 arrays; tiles rows are {b, row0, nk, nf | nrows << 16} in
+    execution order. Synchronises the stream."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    ws = workspace(workspace_size(p, op, microbatch, hist_max_len, hist_tokens), dev)
+    qoff = np.zeros(p.B + 1, dtype=np.int32)
+    cap = 1 << 20
+    tiles = np.zeros((cap, 4), dtype=np.int32)
+    count = ctypes.c_int64(0)
+    L.check(L.lib().hstu_schedule_export(
+        ctypes.byref(p), op, _ptr(hist_offsets), int(hist_tokens), int(hist_max_len), int(microbatch),
+        _ptr(ws), ws.numel(), _stream(stream), ctypes.c_void_p(qoff.ctypes.data),
+        ctypes.c_void_p(tiles.ctypes.data), cap, ctypes.byref(count)))
+    return qoff, tiles[:count.value].copy()
+
+
+def device_status(ws, stream=None) -> int:
+    """hstu_get_device_status: HSTU_DEV_* bits left by the last call on ws."""
+    v = ctypes.c_int32(0)
+    L.check(L.lib().hstu_get_device_status(_ptr(ws), _stream(stream), ctypes.byref(v)))
+    return int(v.value)
+
+
+def kernel_timing(enable: bool) -> None:
+    """hstu_kernel_timing: bracket every library kernel launch with HIP events."""
+    L.check(L.lib().hstu_kernel_timing(1 if enable else 0))
+
+
+def kernel_timing_read(kernel: int):
+    """hstu_kernel_timing_read: (total milliseconds, launches) of one kernel id."""
+    ms, n = ctypes.c_double(0), ctypes.c_int64(0)
+    L.check(L.lib().hstu_kernel_timing_read(int(kernel), ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)

@@ -1,0 +1,447 @@
+// C-ABI of libhstu.so: host-side validation, workspace carving and the launch
+// sequence of every entry point declared in include/hstu.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/hstu.h"
+#include "hstu_internal.h"
+
+using namespace hstu;
+
+namespace {
+
+thread_local std::string g_err;
+
+hstu_status_t fail(hstu_status_t st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+hstu_status_t fail(hstu_status_t st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+hstu_status_t hip_fail(hipError_t e, const char *what) {
+  return fail(HSTU_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                      \
+  do {                                           \
+    hipError_t e_ = (expr);                      \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+// Optional per-launch event timing (hstu_kernel_timing).
+struct TimingRecord {
+  int kernel;
+  hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimingRecord> g_timing;
+
+void timing_clear_locked() {
+  for (auto &r : g_timing) {
+    hipEventSynchronize(r.stop);
+    hipEventDestroy(r.start);
+    hipEventDestroy(r.stop);
+  }
+  g_timing.clear();
+}
+
+// Brackets one launch with events when timing is enabled.
+struct Timed {
+  int kernel;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  Timed(int k, hipStream_t s) : kernel(k), st(s) {
+    std::lock_guard<std::mutex> g(g_timing_mu);
+    if (!g_timing_on) return;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+      a = b = nullptr;
+      return;
+    }
+    hipEventRecord(a, st);
+  }
+  ~Timed() {
+    if (!a) return;
+    hipEventRecord(b, st);
+    std::lock_guard<std::mutex> g(g_timing_mu);
+    g_timing.push_back({kernel, a, b});
+  }
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+long long div_up(long long a, long long b) { return (a + b - 1) / b; }
+
+struct Tiles {
+  int BM, BN;
+};
+
+Tiles tiles_for(const hstu_problem_t *p, int op) {
+  if (p->dtype == HSTU_F32) return {kF32BM, kF32BN};
+  (void)op;
+  return {kFwdBM, kFwdBN};
+}
+
+// Workspace sections (byte offsets from ws).
+struct Layout {
+  size_t hdr, desc, qoff, tiles, total;
+  long long max_tiles;
+};
+
+Layout layout(const hstu_problem_t *p, int op, int microbatch, int hist_max_len) {
+  Tiles t = tiles_for(p, op);
+  Layout L{};
+  long long nq;
+  if (op == HSTU_OP_MFALCON) {
+    long long bm = microbatch > 0 ? microbatch : (p->max_len > 0 ? p->max_len : 1);
+    nq = div_up(p->total_tokens, t.BM) + (long long)p->B * (div_up(p->max_len, bm) + 1);
+  } else {
+    nq = div_up(p->total_tokens, t.BM) + p->B;
+  }
+  (void)hist_max_len;
+  L.max_tiles = nq;
+  size_t off = 0;
+  L.hdr = off;   off += align256(kHdrWords * sizeof(int));
+  L.desc = off;  off += align256(sizeof(SeqDesc) * (size_t)(p->B > 0 ? p->B : 1));
+  L.qoff = off;  off += align256(sizeof(int) * (size_t)(p->B + 1));
+  L.tiles = off; off += align256(sizeof(QTile) * (size_t)(nq > 0 ? nq : 1));
+  L.total = off;
+  return L;
+}
+
+hstu_status_t check_problem(const hstu_problem_t *p, int op) {
+  if (!p) return fail(HSTU_ERR_INVALID_ARG, "problem is NULL");
+  if (p->B < 0) return fail(HSTU_ERR_INVALID_ARG, "B = %d < 0", p->B);
+  if (p->B > kMaxSeqs) return fail(HSTU_ERR_UNSUPPORTED, "B = %d > %d sequences per call", p->B, kMaxSeqs);
+  if (p->H < 1) return fail(HSTU_ERR_INVALID_ARG, "H = %d < 1", p->H);
+  if (p->d != 32 && p->d != 64 && p->d != 128)
+    return fail(HSTU_ERR_UNSUPPORTED, "d = %d not in {32, 64, 128}", p->d);
+  if (p->dtype != HSTU_BF16 && p->dtype != HSTU_F32)
+    return fail(HSTU_ERR_INVALID_ARG, "dtype = %d", p->dtype);
+  if (p->total_tokens < 0 || p->total_tokens >= (1ll << 31))
+    return fail(HSTU_ERR_INVALID_ARG, "total_tokens = %lld out of [0, 2^31)", (long long)p->total_tokens);
+  if (p->max_len < 0) return fail(HSTU_ERR_INVALID_ARG, "max_len = %d < 0", p->max_len);
+  Tiles t = tiles_for(p, op);
+  if (div_up(p->max_len, t.BN) > kMaxKeyTiles)
+    return fail(HSTU_ERR_UNSUPPORTED, "max_len = %d exceeds %d key tiles", p->max_len, kMaxKeyTiles);
+  if (p->n_max < 1) return fail(HSTU_ERR_INVALID_ARG, "n_max = %d < 1", p->n_max);
+  if (!p->offsets) return fail(HSTU_ERR_INVALID_ARG, "offsets is NULL");
+  if (p->rab_p && p->n_pos < 1) return fail(HSTU_ERR_INVALID_ARG, "rab_p given with n_pos = %d", p->n_pos);
+  if (p->rab_t && p->n_tb < 1) return fail(HSTU_ERR_INVALID_ARG, "rab_t given with n_tb = %d", p->n_tb);
+  if (p->norm < HSTU_NORM_NONE || p->norm > HSTU_NORM_GLN)
+    return fail(HSTU_ERR_INVALID_ARG, "norm = %d", p->norm);
+  if (p->norm != HSTU_NORM_NONE && !(p->eps > 0.f))
+    return fail(HSTU_ERR_INVALID_ARG, "eps = %g must be > 0", (double)p->eps);
+  if (p->norm == HSTU_NORM_GLN) {
+    if (!p->token_group) return fail(HSTU_ERR_INVALID_ARG, "GLN needs token_group");
+    if (p->n_groups < 1 || p->n_groups > 255)
+      return fail(HSTU_ERR_INVALID_ARG, "n_groups = %d not in [1, 255]", p->n_groups);
+  }
+  const long long D = (long long)p->H * p->d;
+  const long long dmax = p->dtype == HSTU_BF16 ? 4096 : 2048;
+  if (D > dmax) return fail(HSTU_ERR_UNSUPPORTED, "H*d = %lld > %lld", D, dmax);
+  return HSTU_OK;
+}
+
+hstu_status_t check_ws(const void *ws, size_t ws_bytes, size_t need) {
+  if (!ws) return fail(HSTU_ERR_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)ws % 256) return fail(HSTU_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (ws_bytes < need) return fail(HSTU_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  return HSTU_OK;
+}
+
+template <class T>
+T *at(void *ws, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+void fill_sched(SchedArgs &s, const hstu_problem_t *p, int op, const Layout &L, void *ws,
+                const int32_t *hist_offsets, int64_t hist_tokens, int hist_max_len, int microbatch) {
+  Tiles t = tiles_for(p, op);
+  std::memset(&s, 0, sizeof s);
+  s.mode = op == HSTU_OP_MFALCON ? kSchedMFalcon : kSchedAttn;
+  if (op == HSTU_OP_MFALCON) {
+    s.cand_offsets = p->offsets;
+    s.hist_offsets = hist_offsets;
+  } else {
+    s.offsets = p->offsets;
+    s.prefix = p->prefix_len;
+    s.cand = p->cand_len;
+  }
+  s.B = p->B;
+  s.Tq = p->total_tokens;
+  s.Tkv = op == HSTU_OP_MFALCON ? hist_tokens : p->total_tokens;
+  s.max_len = p->max_len;
+  s.hist_max_len = hist_max_len;
+  s.BM = t.BM;
+  s.BN = t.BN;
+  s.microbatch = microbatch;
+  s.max_tiles = (int)L.max_tiles;
+  s.hdr = at<int>(ws, L.hdr);
+  s.desc = at<SeqDesc>(ws, L.desc);
+  s.qoff = at<int>(ws, L.qoff);
+  s.tiles = at<QTile>(ws, L.tiles);
+}
+
+hstu_status_t check_mfalcon(const hstu_problem_t *cand, const int32_t *hist_offsets,
+                            int64_t hist_tokens, int32_t hist_max_len, int32_t microbatch) {
+  if (!cand) return fail(HSTU_ERR_INVALID_ARG, "problem is NULL");
+  if (cand->prefix_len || cand->cand_len)
+    return fail(HSTU_ERR_INVALID_ARG, "M-FALCON candidates take no prefix_len/cand_len");
+  if (!hist_offsets) return fail(HSTU_ERR_INVALID_ARG, "hist_offsets is NULL");
+  if (hist_tokens < 0 || hist_tokens >= (1ll << 31))
+    return fail(HSTU_ERR_INVALID_ARG, "hist_tokens = %lld", (long long)hist_tokens);
+  if (hist_max_len < 0) return fail(HSTU_ERR_INVALID_ARG, "hist_max_len < 0");
+  if (microbatch < 0) return fail(HSTU_ERR_INVALID_ARG, "microbatch = %d < 0", microbatch);
+  Tiles t = tiles_for(cand, HSTU_OP_MFALCON);
+  if (div_up(hist_max_len, t.BN) > kMaxKeyTiles)
+    return fail(HSTU_ERR_UNSUPPORTED, "hist_max_len = %d exceeds %d key tiles", hist_max_len, kMaxKeyTiles);
+  if ((long long)hist_max_len + cand->max_len >= (1ll << 30))
+    return fail(HSTU_ERR_INVALID_ARG, "history + candidates too long");
+  return HSTU_OK;
+}
+
+hstu_status_t run_forward(const hstu_problem_t *p, int op, const Layout &L, void *ws,
+                          hipStream_t st, const void *Q, const void *K, const void *V,
+                          const void *Kself, const void *Vself, const void *U,
+                          const int64_t *ts_q, const int64_t *ts_kv, void *Y, void *O,
+                          float *mean, float *rstd) {
+  Tiles t = tiles_for(p, op);
+  FwdArgs f;
+  std::memset(&f, 0, sizeof f);
+  f.Q = Q; f.K = K; f.V = V; f.Kself = Kself; f.Vself = Vself; f.O = O;
+  const bool use_t = p->rab_t && ts_q && ts_kv;
+  f.ts_q = use_t ? ts_q : nullptr;
+  f.ts_kv = use_t ? ts_kv : nullptr;
+  f.rab_p = p->rab_p;
+  f.rab_t = use_t ? p->rab_t : nullptr;
+  f.n_pos = p->n_pos;
+  f.n_tb = p->n_tb;
+  f.inv_nmax = 1.0f / (float)p->n_max;
+  f.H = p->H;
+  f.d = p->d;
+  f.hdr = at<int>(ws, L.hdr);
+  f.desc = at<SeqDesc>(ws, L.desc);
+  f.tiles = at<QTile>(ws, L.tiles);
+  long long units = L.max_tiles * p->H;
+  if (units >= (1ll << 31)) return fail(HSTU_ERR_UNSUPPORTED, "too many work units");
+  f.units = (int)units;
+  (void)t;
+  {
+    Timed t_(HSTU_KERNEL_ATTN_FWD, st);
+    HIP_TRY(p->dtype == HSTU_BF16 ? launch_attn_fwd_bf16(f, st) : launch_attn_fwd_f32(f, st),
+            "attention forward launch");
+  }
+
+  NormArgs n;
+  std::memset(&n, 0, sizeof n);
+  n.X = O; n.U = U; n.Y = Y;
+  n.mean = (mean && rstd) ? mean : nullptr;
+  n.rstd = (mean && rstd) ? rstd : nullptr;
+  n.group = p->norm == HSTU_NORM_GLN ? p->token_group : nullptr;
+  n.gamma = p->gamma; n.beta = p->beta;
+  n.n_groups = p->norm == HSTU_NORM_GLN ? p->n_groups : 1;
+  n.mode = p->norm;
+  n.eps = p->eps;
+  n.T = p->total_tokens;
+  n.D = p->H * p->d;
+  n.hdr = at<int>(ws, L.hdr);
+  {
+    Timed t_(HSTU_KERNEL_NORM_FWD, st);
+    HIP_TRY(launch_norm_fwd(n, p->dtype == HSTU_BF16, st), "norm forward launch");
+  }
+  return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *hstu_version(void) { return "0.1.0"; }
+
+const char *hstu_last_error(void) { return g_err.c_str(); }
+
+hstu_status_t hstu_workspace_size(const hstu_problem_t *p, int32_t op, int32_t microbatch,
+                                  int32_t hist_max_len, int64_t hist_tokens, size_t *bytes) {
+  if (!bytes) return fail(HSTU_ERR_INVALID_ARG, "bytes is NULL");
+  if (op != HSTU_OP_FWD && op != HSTU_OP_BWD && op != HSTU_OP_MFALCON)
+    return fail(HSTU_ERR_INVALID_ARG, "op = %d", op);
+  hstu_status_t st = check_problem(p, op);
+  if (st) return st;
+  if (op == HSTU_OP_MFALCON) {
+    if (microbatch < 0) return fail(HSTU_ERR_INVALID_ARG, "microbatch = %d < 0", microbatch);
+    (void)hist_tokens;
+  }
+  if (op == HSTU_OP_BWD) return fail(HSTU_ERR_UNSUPPORTED, "backward not built yet");
+  *bytes = layout(p, op, microbatch, hist_max_len).total;
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_tile_shape(const hstu_problem_t *p, int32_t op, int32_t *BM, int32_t *BN) {
+  if (!p || !BM || !BN) return fail(HSTU_ERR_INVALID_ARG, "NULL argument");
+  Tiles t = tiles_for(p, op);
+  *BM = t.BM;
+  *BN = t.BN;
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_attn_fwd(const hstu_problem_t *p, const void *Q, const void *K, const void *V,
+                            const void *U, void *Y, void *O, float *mean, float *rstd, void *ws,
+                            size_t ws_bytes, void *stream) {
+  hstu_status_t s = check_problem(p, HSTU_OP_FWD);
+  if (s) return s;
+  if (p->total_tokens > 0 && (!Q || !K || !V || !U || !Y || !O))
+    return fail(HSTU_ERR_INVALID_ARG, "Q/K/V/U/Y/O must not be NULL");
+  if (p->norm != HSTU_NORM_NONE && (!mean || !rstd))
+    return fail(HSTU_ERR_INVALID_ARG, "mean/rstd must not be NULL with a norm");
+  Layout L = layout(p, HSTU_OP_FWD, 0, 0);
+  s = check_ws(ws, ws_bytes, L.total);
+  if (s) return s;
+  hipStream_t st = (hipStream_t)stream;
+  SchedArgs sa;
+  fill_sched(sa, p, HSTU_OP_FWD, L, ws, nullptr, 0, 0, 0);
+  {
+    Timed t_(HSTU_KERNEL_SCHED, st);
+    HIP_TRY(launch_sched(sa, st), "scheduler launch");
+  }
+  return run_forward(p, HSTU_OP_FWD, L, ws, st, Q, K, V, K, V, U, p->timestamps, p->timestamps,
+                     Y, O, mean, rstd);
+}
+
+hstu_status_t hstu_mfalcon_score(const hstu_problem_t *cand, const int32_t *hist_offsets,
+                                 int64_t hist_tokens, int32_t hist_max_len, const void *K_cache,
+                                 const void *V_cache, const int64_t *hist_ts, const void *Qc,
+                                 const void *Kc, const void *Vc, const void *Uc,
+                                 int32_t microbatch, void *Yc, void *Oc, float *mean, float *rstd,
+                                 void *ws, size_t ws_bytes, void *stream) {
+  hstu_status_t s = check_problem(cand, HSTU_OP_MFALCON);
+  if (s) return s;
+  s = check_mfalcon(cand, hist_offsets, hist_tokens, hist_max_len, microbatch);
+  if (s) return s;
+  if ((cand->timestamps == nullptr) != (hist_ts == nullptr))
+    return fail(HSTU_ERR_INVALID_ARG, "give both candidate and history timestamps, or neither");
+  if (cand->total_tokens > 0 && (!Qc || !Kc || !Vc || !Uc || !Yc || !Oc))
+    return fail(HSTU_ERR_INVALID_ARG, "Qc/Kc/Vc/Uc/Yc/Oc must not be NULL");
+  if (hist_tokens > 0 && (!K_cache || !V_cache))
+    return fail(HSTU_ERR_INVALID_ARG, "K_cache/V_cache must not be NULL");
+  if (cand->norm != HSTU_NORM_NONE && (!mean || !rstd))
+    return fail(HSTU_ERR_INVALID_ARG, "mean/rstd must not be NULL with a norm");
+  Layout L = layout(cand, HSTU_OP_MFALCON, microbatch, hist_max_len);
+  s = check_ws(ws, ws_bytes, L.total);
+  if (s) return s;
+  hipStream_t st = (hipStream_t)stream;
+  SchedArgs sa;
+  fill_sched(sa, cand, HSTU_OP_MFALCON, L, ws, hist_offsets, hist_tokens, hist_max_len, microbatch);
+  {
+    Timed t_(HSTU_KERNEL_SCHED, st);
+    HIP_TRY(launch_sched(sa, st), "scheduler launch");
+  }
+  return run_forward(cand, HSTU_OP_MFALCON, L, ws, st, Qc, K_cache, V_cache, Kc, Vc, Uc,
+                     cand->timestamps, hist_ts, Yc, Oc, mean, rstd);
+}
+
+hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *K, const void *V,
+                            const void *U, const void *O, const float *mean, const float *rstd,
+                            const void *dY, void *dQ, void *dK, void *dV, void *dU,
+                            float *d_rab_p, float *d_rab_t, float *d_gamma, float *d_beta,
+                            void *ws, size_t ws_bytes, void *stream) {
+  (void)Q; (void)K; (void)V; (void)U; (void)O; (void)mean; (void)rstd; (void)dY; (void)dQ;
+  (void)dK; (void)dV; (void)dU; (void)d_rab_p; (void)d_rab_t; (void)d_gamma; (void)d_beta;
+  (void)ws; (void)ws_bytes; (void)stream;
+  hstu_status_t s = check_problem(p, HSTU_OP_BWD);
+  if (s) return s;
+  return fail(HSTU_ERR_UNSUPPORTED, "backward not built yet");
+}
+
+hstu_status_t hstu_schedule_export(const hstu_problem_t *p, int32_t op,
+                                   const int32_t *hist_offsets, int64_t hist_tokens,
+                                   int32_t hist_max_len, int32_t microbatch, void *ws,
+                                   size_t ws_bytes, void *stream, int32_t *host_qtile_off,
+                                   int32_t *host_tiles, int64_t cap, int64_t *count) {
+  if (op != HSTU_OP_FWD && op != HSTU_OP_MFALCON)
+    return fail(HSTU_ERR_INVALID_ARG, "schedule export supports HSTU_OP_FWD and HSTU_OP_MFALCON");
+  hstu_status_t s = check_problem(p, op);
+  if (s) return s;
+  if (op == HSTU_OP_MFALCON) {
+    s = check_mfalcon(p, hist_offsets, hist_tokens, hist_max_len, microbatch);
+    if (s) return s;
+  }
+  if (!host_qtile_off || !count || (cap > 0 && !host_tiles))
+    return fail(HSTU_ERR_INVALID_ARG, "NULL host output");
+  Layout L = layout(p, op, microbatch, hist_max_len);
+  s = check_ws(ws, ws_bytes, L.total);
+  if (s) return s;
+  hipStream_t st = (hipStream_t)stream;
+  SchedArgs sa;
+  fill_sched(sa, p, op, L, ws, hist_offsets, hist_tokens, hist_max_len, microbatch);
+  HIP_TRY(launch_sched(sa, st), "scheduler launch");
+  int hdr[kHdrWords];
+  HIP_TRY(hipMemcpyAsync(hdr, at<int>(ws, L.hdr), sizeof hdr, hipMemcpyDeviceToHost, st), "copy header");
+  HIP_TRY(hipMemcpyAsync(host_qtile_off, at<int>(ws, L.qoff), sizeof(int) * (p->B + 1),
+                         hipMemcpyDeviceToHost, st), "copy query-tile offsets");
+  HIP_TRY(hipStreamSynchronize(st), "stream synchronize");
+  const long long nq = hdr[kHdrNQ];
+  *count = nq;
+  const long long n = nq < cap ? nq : cap;
+  if (n > 0) {
+    HIP_TRY(hipMemcpy(host_tiles, at<QTile>(ws, L.tiles), sizeof(QTile) * n, hipMemcpyDeviceToHost),
+            "copy tiles");
+  }
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_get_device_status(const void *ws, void *stream, int32_t *host_code) {
+  if (!ws || !host_code) return fail(HSTU_ERR_INVALID_ARG, "NULL argument");
+  hipStream_t st = (hipStream_t)stream;
+  int v = 0;
+  HIP_TRY(hipMemcpyAsync(&v, ws, sizeof v, hipMemcpyDeviceToHost, st), "copy status");
+  HIP_TRY(hipStreamSynchronize(st), "stream synchronize");
+  *host_code = v;
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_kernel_timing(int32_t enable) {
+  std::lock_guard<std::mutex> g(g_timing_mu);
+  timing_clear_locked();
+  g_timing_on = enable != 0;
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_kernel_timing_read(int32_t kernel, double *total_ms, int64_t *launches) {
+  if (!total_ms || !launches) return fail(HSTU_ERR_INVALID_ARG, "NULL argument");
+  if (kernel < 0 || kernel >= HSTU_KERNEL_COUNT) return fail(HSTU_ERR_INVALID_ARG, "kernel id %d", kernel);
+  std::lock_guard<std::mutex> g(g_timing_mu);
+  double ms = 0.0;
+  int64_t n = 0;
+  std::vector<TimingRecord> keep;
+  for (auto &r : g_timing) {
+    if (r.kernel != kernel) {
+      keep.push_back(r);
+      continue;
+    }
+    HIP_TRY(hipEventSynchronize(r.stop), "event synchronize");
+    float e = 0.f;
+    HIP_TRY(hipEventElapsedTime(&e, r.start, r.stop), "event elapsed time");
+    ms += e;
+    n++;
+    hipEventDestroy(r.start);
+    hipEventDestroy(r.stop);
+  }
+  g_timing.swap(keep);
+  *total_ms = ms;
+  *launches = n;
+  return HSTU_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,157 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer of
+// libhstu.so. Device code targets gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hstu {
+
+// Per-sequence frame of the attention core. A "frame" is the sequence as the
+// mask sees it: frame indices [0, P) are the bidirectional prefix, [P, E) the
+// causal part, and indices >= E candidates. For the plain forward the query
+// rows are frame rows [0, L); for M-FALCON scoring the query rows are the
+// candidates, frame rows [n, n + m), and the keys are the cached history.
+struct SeqDesc {
+  int q_base;     // first query row of the sequence in Q/U/O/Y (and query timestamps)
+  int kv_base;    // first key row in K/V (and key timestamps)
+  int self_base;  // row of the first candidate in the self-term K/V arrays
+  int q_frame0;   // frame index of the first query row
+  int P, E;       // prefix end and candidate start, in frame indices
+  int qcount;     // number of query rows
+  int valid;      // 0 when the sequence failed a device-side check (treated as empty)
+};
+
+// One query tile of the work list: key tiles [0, nf) are FULL (every pair
+// visible, no mask), [nf, nk) PARTIAL (mask applied), rows [row0, row0+nrows)
+// are local query rows of sequence b.
+struct QTile {
+  int b, row0, nk, nf_nrows;  // nf | nrows << 16
+};
+
+// Workspace header words.
+constexpr int kHdrStatus = 0;    // OR of HSTU_DEV_* bits
+constexpr int kHdrFirstBad = 1;  // smallest offending sequence index
+constexpr int kHdrNQ = 2;        // number of query tiles
+constexpr int kHdrWords = 64;    // 256 bytes
+
+constexpr int kSchedThreads = 1024;
+constexpr int kSortCap = 8192;   // longest-first order up to this many query tiles
+constexpr int kMaxSeqs = 8192;   // sequences per call (query-tile offsets live in LDS)
+constexpr int kMaxKeyTiles = 16383;
+
+enum SchedMode { kSchedAttn = 0, kSchedMFalcon = 1 };
+
+struct SchedArgs {
+  int mode;
+  // attention forward: one jagged batch
+  const int *offsets, *prefix, *cand;
+  // M-FALCON: candidate offsets (query rows) and history offsets (keys)
+  const int *cand_offsets, *hist_offsets;
+  int B;
+  long long Tq, Tkv;
+  int max_len, hist_max_len;
+  int BM, BN, microbatch;
+  int max_tiles;   // capacity of `tiles`; a larger count marks the offsets bad and runs nothing
+  int *hdr;
+  SeqDesc *desc;
+  int *qoff;
+  QTile *tiles;
+};
+
+hipError_t launch_sched(const SchedArgs &a, hipStream_t s);
+
+// Forward attention kernels. Arrays are token-major with row stride H*d.
+struct FwdArgs {
+  const void *Q, *K, *V;          // query rows / key rows
+  const void *Kself, *Vself;      // rows used by a candidate's pair with itself
+  void *O;                        // [Tq, H*d] output, scaled by 1/N_max
+  const int64_t *ts_q, *ts_kv;    // timestamps of query / key rows, or NULL
+  const float *rab_p, *rab_t;
+  int n_pos, n_tb;
+  float inv_nmax;
+  int H, d;
+  const int *hdr;
+  const SeqDesc *desc;
+  const QTile *tiles;
+  int units;                      // grid size bound: max query tiles * H
+};
+
+// bf16 inputs, MFMA, tile 128 x 64
+constexpr int kFwdBM = 128, kFwdBN = 64;
+// fp32 inputs, vector ALU, tile 64 x 64
+constexpr int kF32BM = 64, kF32BN = 64;
+
+hipError_t launch_attn_fwd_bf16(const FwdArgs &a, hipStream_t s);
+hipError_t launch_attn_fwd_f32(const FwdArgs &a, hipStream_t s);
+
+// Per-token Norm(x) * u (forward) and its backward.
+struct NormArgs {
+  const void *X;        // [T, D] pre-norm attention output
+  const void *U;        // [T, D]
+  void *Y;              // [T, D]
+  float *mean, *rstd;   // [T] or NULL (norm NONE)
+  const uint8_t *group; // [T] or NULL
+  const float *gamma, *beta;  // [G, D] or NULL
+  int n_groups;
+  int mode;             // 0 none, 1 LN, 2 GLN
+  float eps;
+  long long T;
+  int D;
+  int *hdr;             // status word (group id violations)
+};
+hipError_t launch_norm_fwd(const NormArgs &a, bool bf16, hipStream_t s);
+
+struct NormBwdArgs {
+  const void *X, *U, *dY;
+  const float *mean, *rstd;
+  const uint8_t *group;
+  const float *gamma, *beta;
+  int n_groups, mode;
+  long long T;
+  int D;
+  void *dU;             // [T, D] dtype
+  void *dX;             // [T, D] dtype (gradient w.r.t. the pre-norm output)
+  float *dgamma_part, *dbeta_part;  // [nblk, G, D] partial sums or NULL
+  int nblk;
+};
+hipError_t launch_norm_bwd(const NormBwdArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_reduce_rows(const float *part, int nrows, long long width, float *out,
+                              hipStream_t s);
+
+// Backward attention kernels.
+struct BwdArgs {
+  const void *Q, *K, *V, *dO;     // dO = gradient w.r.t. the pre-norm output
+  void *dQ, *dK, *dV;
+  float *dQacc;                   // fp32 [T, H*d] accumulator (bf16 path) or NULL
+  const int64_t *ts;
+  const float *rab_p, *rab_t;
+  float *drab_p, *drab_t;         // fp32 accumulators (zeroed by the caller)
+  int n_pos, n_tb;
+  float inv_nmax;
+  int H, d;
+  const int *hdr;
+  const SeqDesc *desc;
+  const QTile *tiles;             // key tiles in the same record format (rows = keys)
+  int units;
+};
+constexpr int kBwdBM = 64, kBwdBN = 64;   // bf16 backward: key tile BN rows, query tiles of BM
+hipError_t launch_attn_bwd_bf16(const BwdArgs &a, hipStream_t s);
+hipError_t launch_attn_bwd_f32(const BwdArgs &a, hipStream_t s);
+
+// Key-major work list for the backward: one record per key tile.
+struct KSchedArgs {
+  const int *offsets, *prefix, *cand;
+  int B;
+  long long T;
+  int max_len;
+  int BM, BN;
+  int *hdr;
+  SeqDesc *desc;
+  QTile *ktiles;   // {b, key0, q-tile range begin (frame row tile), nrows | qt_end << 16}
+};
+
+hipError_t launch_fill_f32(float *p, long long n, float v, hipStream_t s);
+hipError_t launch_cast_f32_to_bf16(const float *src, void *dst, long long n, hipStream_t s);
+
+}  // namespace hstu

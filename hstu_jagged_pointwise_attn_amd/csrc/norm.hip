@@ -1,0 +1,155 @@
+// Per-token epilogue Y = Norm(X) * U over the full width D = H*d of a token
+// (HSTU blog, section 3 layer formula: Norm(A(X)V(X)) * U(X)); Norm is none,
+// LayerNorm (population variance, eps), or MTGR's Group LayerNorm (MTGR deep
+// read, section 2: normalisation grouped by token source), read as per-token
+// statistics with an affine (gamma_g, beta_g) chosen by the token's group.
+// One wave per token; the row sits in registers, the mean and the variance are
+// two wave reductions (the variance from the centred values).
+#include "hstu_internal.h"
+#include "../../include/hstu.h"
+
+namespace hstu {
+namespace {
+
+typedef unsigned short u16;
+typedef unsigned int u32;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <bool BF16>
+struct Vec;
+template <>
+struct Vec<true> {
+  static constexpr int N = 8;
+  __device__ static void load(const void *p, long long off, float *x) {
+    const uint4 v = *(const uint4 *)((const u16 *)p + off);
+    const u32 *w = (const u32 *)&v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(w[e] << 16);
+      x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
+  __device__ static void store(void *p, long long off, const float *x) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    uint4 v;
+    u32 *w = (u32 *)&v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bf16x2 t;
+      t[0] = (__bf16)x[2 * e];
+      t[1] = (__bf16)x[2 * e + 1];
+      w[e] = __builtin_bit_cast(u32, t);
+    }
+    *(uint4 *)((u16 *)p + off) = v;
+  }
+};
+template <>
+struct Vec<false> {
+  static constexpr int N = 4;
+  __device__ static void load(const void *p, long long off, float *x) {
+    const float4 v = *(const float4 *)((const float *)p + off);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  }
+  __device__ static void store(void *p, long long off, const float *x) {
+    *(float4 *)((float *)p + off) = float4{x[0], x[1], x[2], x[3]};
+  }
+};
+
+template <bool BF16, int MAXCH>
+__global__ __launch_bounds__(256) void norm_fwd_kernel(NormArgs a) {
+  using V = Vec<BF16>;
+  constexpr int N = V::N;
+  const long long t = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int lane = threadIdx.x & 63;
+  const int D = a.D, nch = D / N;
+  const long long row = t * D;
+  float x[MAXCH][N];
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < MAXCH; ++k) {
+    const int ch = lane + 64 * k;
+    if (ch < nch) {
+      V::load(a.X, row + ch * N, x[k]);
+#pragma unroll
+      for (int e = 0; e < N; ++e) s += x[k][e];
+    }
+  }
+  float mean = 0.f, rstd = 1.f;
+  int g = -1;
+  if (a.mode != HSTU_NORM_NONE) {
+    mean = wave_sum(s) / (float)D;
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < MAXCH; ++k) {
+      const int ch = lane + 64 * k;
+      if (ch < nch) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          const float c = x[k][e] - mean;
+          v += c * c;
+        }
+      }
+    }
+    const float var = wave_sum(v) / (float)D;
+    rstd = 1.0f / sqrtf(var + a.eps);
+    g = 0;
+    if (a.mode == HSTU_NORM_GLN) {
+      g = a.group[t];
+      if (g >= a.n_groups) {
+        if (lane == 0) atomicOr(&a.hdr[kHdrStatus], HSTU_DEV_BAD_GROUP);
+        g = -1;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < MAXCH; ++k) {
+    const int ch = lane + 64 * k;
+    if (ch < nch) {
+      float u[N], y[N];
+      V::load(a.U, row + ch * N, u);
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        float n = x[k][e];
+        if (a.mode != HSTU_NORM_NONE) {
+          n = (n - mean) * rstd;
+          const int c = ch * N + e;
+          if (g >= 0 && a.gamma) n *= a.gamma[(long long)g * D + c];
+          if (g >= 0 && a.beta) n += a.beta[(long long)g * D + c];
+        }
+        y[e] = n * u[e];
+      }
+      V::store(a.Y, row + ch * N, y);
+    }
+  }
+  if (lane == 0 && a.mean) {
+    a.mean[t] = mean;
+    a.rstd[t] = rstd;
+  }
+}
+
+template <bool BF16>
+hipError_t norm_fwd_dispatch(const NormArgs &a, hipStream_t s) {
+  const int nch = a.D / Vec<BF16>::N;
+  const dim3 grid((unsigned)((a.T + 3) / 4));
+  if (nch <= 64) hipLaunchKernelGGL((norm_fwd_kernel<BF16, 1>), grid, dim3(256), 0, s, a);
+  else if (nch <= 128) hipLaunchKernelGGL((norm_fwd_kernel<BF16, 2>), grid, dim3(256), 0, s, a);
+  else if (nch <= 256) hipLaunchKernelGGL((norm_fwd_kernel<BF16, 4>), grid, dim3(256), 0, s, a);
+  else if (nch <= 512) hipLaunchKernelGGL((norm_fwd_kernel<BF16, 8>), grid, dim3(256), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_norm_fwd(const NormArgs &a, bool bf16, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  return bf16 ? norm_fwd_dispatch<true>(a, s) : norm_fwd_dispatch<false>(a, s);
+}
+
+}  // namespace hstu

@@ -1,0 +1,245 @@
+// Jagged tile scheduler: one workgroup turns the offsets of a jagged batch
+// into the list of query tiles the attention kernels run, with no padding and
+// no host round trip.
+//
+// The masks of the method (causal; MTGR's static / real-time / candidate
+// mask, MTGR deep read section 2 "动态混合掩码"; M-FALCON's candidate mask,
+// HSTU blog section 4.2) all give every query row a visible key set that is a
+// prefix [0, hi(i)) of its sequence, once a candidate's pair with itself is
+// taken out (that pair is added per row by the attention kernel):
+//   hi(i) = P for i < P,  i + 1 for P <= i < E,  E for i >= E,
+// and hi is non-decreasing in i. So the key tiles a query tile [i0, i1]
+// touches are [0, ceil(hi(i1)/BN)), the first floor(hi(i0)/BN) of them fully
+// visible. Tiles with no visible pair are never listed.
+//
+// Steps: per-sequence validation and query-tile counts -> exclusive scan ->
+// one record per query tile -> longest-first order (bitonic sort in LDS on
+// the unique key (nk descending, canonical index ascending)).
+#include "hstu_internal.h"
+#include "../../include/hstu.h"
+
+namespace hstu {
+namespace {
+
+__device__ __forceinline__ int frame_hi(int i, int P, int E) {
+  return i < P ? P : (i < E ? i + 1 : E);
+}
+
+// Validated frame of sequence b (see SeqDesc). Offending sequences come back
+// with valid = 0 and qcount = 0, and their status bits in *bits.
+__device__ SeqDesc seq_info(const SchedArgs &a, int b, int *bits) {
+  SeqDesc s{};
+  *bits = 0;
+  if (a.mode == kSchedAttn) {
+    long long beg = a.offsets[b], end = a.offsets[b + 1];
+    int P = a.prefix ? a.prefix[b] : 0;
+    int C = a.cand ? a.cand[b] : 0;
+    long long L = end - beg;
+    if (beg < 0 || end < beg || end > a.Tq) *bits |= HSTU_DEV_BAD_OFFSETS;
+    else if (L > a.max_len) *bits |= HSTU_DEV_TOO_LONG;
+    else if (P < 0 || C < 0 || (long long)P + C > L) *bits |= HSTU_DEV_BAD_SEGMENTS;
+    if (*bits) return s;
+    s.q_base = (int)beg;
+    s.kv_base = (int)beg;
+    s.E = (int)L - C;
+    s.P = P;
+    s.self_base = (int)beg + s.E;
+    s.q_frame0 = 0;
+    s.qcount = (int)L;
+    s.valid = 1;
+  } else {
+    long long hb = a.hist_offsets[b], he = a.hist_offsets[b + 1];
+    long long cb = a.cand_offsets[b], ce = a.cand_offsets[b + 1];
+    if (hb < 0 || he < hb || he > a.Tkv || cb < 0 || ce < cb || ce > a.Tq)
+      *bits |= HSTU_DEV_BAD_OFFSETS;
+    else if (he - hb > a.hist_max_len || ce - cb > a.max_len)
+      *bits |= HSTU_DEV_TOO_LONG;
+    if (*bits) return s;
+    int n = (int)(he - hb);
+    s.q_base = (int)cb;
+    s.kv_base = (int)hb;
+    s.self_base = (int)cb;
+    s.q_frame0 = n;
+    s.P = 0;
+    s.E = n;
+    s.qcount = (int)(ce - cb);
+    s.valid = 1;
+  }
+  return s;
+}
+
+__device__ __forceinline__ int div_up(int x, int y) { return (x + y - 1) / y; }
+
+// Number of query tiles of a sequence with `q` query rows.
+__device__ int qtile_count(const SchedArgs &a, int q) {
+  if (q <= 0) return 0;
+  if (a.mode == kSchedAttn || a.microbatch <= 0 || a.microbatch >= q) return div_up(q, a.BM);
+  int bm = a.microbatch, tpm = div_up(bm, a.BM);
+  return (q / bm) * tpm + div_up(q % bm, a.BM);
+}
+
+// Record of the t-th query tile (canonical order) of sequence s.
+__device__ QTile make_tile(const SchedArgs &a, const SeqDesc &s, int b, int t) {
+  int row0, nrows;
+  if (a.mode == kSchedAttn || a.microbatch <= 0 || a.microbatch >= s.qcount) {
+    row0 = t * a.BM;
+    nrows = min(a.BM, s.qcount - row0);
+  } else {
+    int bm = a.microbatch, tpm = div_up(bm, a.BM);
+    int mb = t / tpm, ti = t % tpm;
+    row0 = mb * bm + ti * a.BM;
+    int end = min(s.qcount, (mb + 1) * bm);
+    nrows = min(a.BM, end - row0);
+  }
+  int i0 = s.q_frame0 + row0, i1 = i0 + nrows - 1;
+  int nk = div_up(frame_hi(i1, s.P, s.E), a.BN);
+  int nf = frame_hi(i0, s.P, s.E) / a.BN;
+  QTile r;
+  r.b = b;
+  r.row0 = row0;
+  r.nk = nk;
+  r.nf_nrows = nf | (nrows << 16);
+  return r;
+}
+
+// Exclusive scan of one value per thread across the workgroup.
+__device__ int block_exclusive_scan(int v, int *s_wsum, int *total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int NW = kSchedThreads / 64;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_wsum[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int ws = lane < NW ? s_wsum[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < NW; o <<= 1) {
+      int y = __shfl_up(ws, o, 64);
+      if (lane >= o) ws += y;
+    }
+    if (lane < NW) s_wsum[lane] = ws;
+  }
+  __syncthreads();
+  int excl = (w > 0 ? s_wsum[w - 1] : 0) + x - v;
+  *total = s_wsum[NW - 1];
+  __syncthreads();
+  return excl;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
+  __shared__ int s_qoff[kMaxSeqs + 1];
+  __shared__ unsigned s_keys[kSortCap];
+  __shared__ int s_wsum[kSchedThreads / 64];
+  const int tid = threadIdx.x;
+
+  if (tid == 0) {
+    int bits = 0;
+    if (a.mode == kSchedAttn) {
+      if (a.offsets[0] != 0 || (long long)a.offsets[a.B] != a.Tq) bits |= HSTU_DEV_BAD_OFFSETS;
+    } else {
+      if (a.cand_offsets[0] != 0 || (long long)a.cand_offsets[a.B] != a.Tq ||
+          a.hist_offsets[0] != 0 || (long long)a.hist_offsets[a.B] != a.Tkv)
+        bits |= HSTU_DEV_BAD_OFFSETS;
+    }
+    a.hdr[kHdrStatus] = bits;
+    a.hdr[kHdrFirstBad] = bits ? -1 : 0x7fffffff;
+  }
+  __syncthreads();
+
+  // Per-sequence validation, descriptors and query-tile counts; scan.
+  int carry = 0;
+  for (int base = 0; base < a.B; base += kSchedThreads) {
+    int b = base + tid, nq = 0;
+    if (b < a.B) {
+      int bits;
+      SeqDesc s = seq_info(a, b, &bits);
+      if (bits) {
+        atomicOr(&a.hdr[kHdrStatus], bits);
+        atomicMin(&a.hdr[kHdrFirstBad], b);
+      }
+      a.desc[b] = s;
+      nq = qtile_count(a, s.qcount);
+    }
+    int total;
+    int excl = block_exclusive_scan(nq, s_wsum, &total);
+    if (b < a.B) s_qoff[b] = carry + excl;
+    carry += total;
+  }
+  if (tid == 0) s_qoff[a.B] = carry;
+  __syncthreads();
+  // Sequences that overlap (possible only with inconsistent offsets) could
+  // exceed the capacity sized from the token count: then nothing runs.
+  const int NQ = carry <= a.max_tiles ? carry : 0;
+  if (tid == 0 && carry > a.max_tiles) {
+    atomicOr(&a.hdr[kHdrStatus], HSTU_DEV_BAD_OFFSETS);
+    atomicMin(&a.hdr[kHdrFirstBad], -1);
+  }
+  for (int b = tid; b <= a.B; b += kSchedThreads) a.qoff[b] = s_qoff[b];
+  if (tid == 0) a.hdr[kHdrNQ] = NQ;
+
+  const bool sorted = NQ <= kSortCap;
+  int n2 = 1;
+  while (n2 < NQ) n2 <<= 1;
+
+  // One record per query tile; sort keys when the list fits in LDS.
+  for (int g = tid; g < (sorted ? n2 : NQ); g += kSchedThreads) {
+    if (g >= NQ) {
+      s_keys[g] = 0xffffffffu;
+      continue;
+    }
+    int lo = 0, hi = a.B;  // largest b with s_qoff[b] <= g
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if (s_qoff[mid] <= g) lo = mid; else hi = mid;
+    }
+    int bits;
+    SeqDesc s = seq_info(a, lo, &bits);
+    QTile r = make_tile(a, s, lo, g - s_qoff[lo]);
+    if (sorted) s_keys[g] = ((unsigned)(kMaxKeyTiles - r.nk) << 18) | (unsigned)g;
+    else a.tiles[g] = r;
+  }
+  if (!sorted) return;
+  __syncthreads();
+
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < n2; i += kSchedThreads) {
+        int ixj = i ^ j;
+        if (ixj > i) {
+          unsigned x = s_keys[i], y = s_keys[ixj];
+          bool up = (i & k) == 0;
+          if ((x > y) == up) {
+            s_keys[i] = y;
+            s_keys[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  for (int r = tid; r < NQ; r += kSchedThreads) {
+    int g = (int)(s_keys[r] & 0x3ffffu);
+    int lo = 0, hi = a.B;
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if (s_qoff[mid] <= g) lo = mid; else hi = mid;
+    }
+    int bits;
+    SeqDesc s = seq_info(a, lo, &bits);
+    a.tiles[r] = make_tile(a, s, lo, g - s_qoff[lo]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sched(const SchedArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hstu

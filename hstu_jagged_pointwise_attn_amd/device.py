@@ -1,0 +1,74 @@
+"""Upload generated problems (``synth``) to the GPU and describe them to the
+library. Marshalling only: no arithmetic of the method happens here."""
+from __future__ import annotations
+
+from types import SimpleNamespace
+
+import numpy as np
+import torch
+
+from . import api
+
+
+def _t(a, dtype, dev):
+    return None if a is None else torch.as_tensor(np.ascontiguousarray(a)).to(dtype).to(dev)
+
+
+def upload(p, device="cuda", with_grad_inputs=False):
+    """Device tensors and the hstu_problem_t of a synth.Problem."""
+    dev = torch.device(device)
+    offsets = _t(p.offsets, torch.int32, dev)
+    ns = SimpleNamespace(src=p, device=dev)
+    ns.offsets = offsets
+    ns.prefix_len = _t(p.prefix_len, torch.int32, dev)
+    ns.cand_len = _t(p.cand_len, torch.int32, dev)
+    ns.ts = _t(p.ts, torch.int64, dev)
+    ns.rab_p = _t(p.rab_p, torch.float32, dev)
+    ns.rab_t = _t(p.rab_t, torch.float32, dev)
+    ns.group = _t(p.group, torch.uint8, dev)
+    ns.gamma = _t(p.gamma, torch.float32, dev)
+    ns.beta = _t(p.beta, torch.float32, dev)
+    ns.Q, ns.K, ns.V, ns.U = (x.contiguous().to(dev) for x in (p.Q, p.K, p.V, p.U))
+    ns.dY = None if p.dY is None else p.dY.contiguous().to(dev)
+    ns.problem = api.problem(
+        offsets, H=p.H, d=p.d, dtype=p.dtype, total_tokens=p.T, max_len=p.max_len, n_max=p.n_max,
+        prefix_len=ns.prefix_len, cand_len=ns.cand_len, timestamps=ns.ts, rab_p=ns.rab_p,
+        rab_t=ns.rab_t, norm=p.norm, eps=p.eps, token_group=ns.group, n_groups=p.n_groups,
+        gamma=ns.gamma, beta=ns.beta)
+    return ns
+
+
+def upload_mfalcon(mf, device="cuda"):
+    """Device tensors and the candidate hstu_problem_t of a synth.MFalconProblem."""
+    dev = torch.device(device)
+    ns = SimpleNamespace(src=mf, device=dev)
+    ns.hist_offsets = _t(mf.hist_offsets, torch.int32, dev)
+    ns.cand_offsets = _t(mf.cand_offsets, torch.int32, dev)
+    ns.hist_ts = _t(mf.hist_ts, torch.int64, dev)
+    ns.cand_ts = _t(mf.cand_ts, torch.int64, dev)
+    ns.rab_p = _t(mf.rab_p, torch.float32, dev)
+    ns.rab_t = _t(mf.rab_t, torch.float32, dev)
+    ns.group = _t(mf.cand_group, torch.uint8, dev)
+    ns.gamma = _t(mf.gamma, torch.float32, dev)
+    ns.beta = _t(mf.beta, torch.float32, dev)
+    for name in ("K_cache", "V_cache", "Qc", "Kc", "Vc", "Uc"):
+        setattr(ns, name, getattr(mf, name).contiguous().to(dev))
+    ns.hist_tokens = int(mf.hist_offsets[-1])
+    ns.hist_max_len = int(np.diff(mf.hist_offsets).max()) if mf.B else 0
+    cand_max = int(np.diff(mf.cand_offsets).max()) if mf.B else 0
+    ns.problem = api.problem(
+        ns.cand_offsets, H=mf.H, d=mf.d, dtype=mf.dtype, total_tokens=int(mf.cand_offsets[-1]),
+        max_len=cand_max, n_max=mf.n_max, timestamps=ns.cand_ts, rab_p=ns.rab_p, rab_t=ns.rab_t,
+        norm=mf.norm, eps=mf.eps, token_group=ns.group, n_groups=mf.n_groups, gamma=ns.gamma,
+        beta=ns.beta)
+    return ns
+
+
+def run_fwd(ns, **kw):
+    return api.attn_fwd(ns.problem, ns.Q, ns.K, ns.V, ns.U, **kw)
+
+
+def run_mfalcon(ns, microbatch=None, **kw):
+    mb = ns.src.microbatch if microbatch is None else microbatch
+    return api.mfalcon_score(ns.problem, ns.hist_offsets, ns.hist_tokens, ns.hist_max_len, ns.K_cache,
+                             ns.V_cache, ns.Qc, ns.Kc, ns.Vc, ns.Uc, hist_ts=ns.hist_ts, microbatch=mb, **kw)

@@ -1,0 +1,258 @@
+/*
+ * hstu.h — C ABI of the HSTU jagged pointwise-attention library (libhstu.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes is the pointwise-attention core of one HSTU layer
+ * (HSTU blog "Meta HSTU: 生成式推荐系统的实践", section 3, the layer formula
+ * A(X)V(X) = phi2(Q K^T + rab^{p,t}) V and O = f2(Norm(A V) * U), with phi2 =
+ * SiLU per section 3.1 and the position/time biases of section 3.2), on
+ * jagged batches (MTGR deep read, section 2: JaggedTensor, no padding), with:
+ *
+ *   s_ij = <q_i, k_j> + rab_p[min(|pos(i) - pos(j)|, n_pos - 1)]
+ *                     + rab_t[min(n_tb - 1, floor(log2(max(1, |t_i - t_j|))))]
+ *   a_ij = vis(i, j) ? SiLU(s_ij) / n_max : 0,   o_i = sum_j a_ij v_j
+ *   y    = Norm(concat_h o^h) * u                (Norm over the D = H*d values
+ *                                                 of a token: none, LayerNorm,
+ *                                                 or Group LayerNorm)
+ *
+ * per sequence b of length L with a bidirectional prefix of P tokens and a
+ * candidate tail of C tokens (E = L - C):
+ *   rows i <  P : see keys j < P                      (static/history tokens)
+ *   rows P<=i<E : see keys j <= i                     (causal)
+ *   rows i >= E : see keys j < E and themselves       (candidates)
+ * (MTGR deep read, section 2 "动态混合掩码"; fmread.com MTGR report, section
+ * 三.1 "动态掩码策略"; HSTU blog section 4.2 for the candidate mask). Every
+ * candidate sits at position E for rab_p. P = C = 0 is the plain causal mask.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host). Arrays are dense,
+ *     row-major and token-major: Q, K, V, U are [T, H, d]; Y and O are
+ *     [T, H*d]; dQ, dK, dV, dU like their inputs.
+ *   - Element type of Q, K, V, U, O, Y, dY and the gradients: bf16 or fp32,
+ *     one type per call (hstu_problem_t.dtype). rab tables, gamma/beta, the
+ *     normalisation statistics and their gradients are fp32.
+ *   - The caller owns every buffer. The library never allocates device
+ *     memory: scratch comes from the workspace `ws` of at least
+ *     hstu_workspace_size() bytes (256-byte aligned). Concurrent calls need
+ *     distinct workspaces.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = default stream)
+ *     and nothing synchronises the host, except where stated. Outputs are
+ *     valid once the stream has reached the end of the call.
+ *   - Outputs must not alias inputs.
+ *   - Errors are returned as status codes; nothing aborts and nothing throws.
+ *     Host-visible preconditions (scalars, NULL pointers, sizes) are checked
+ *     before anything is enqueued. Device-data preconditions (offsets
+ *     non-decreasing from 0 up to total_tokens, P + C <= L, group ids <
+ *     n_groups, lengths <= max_len) are checked by the kernels: the first
+ *     violation is recorded in the workspace (hstu_get_device_status), the
+ *     offending sequences are treated as empty and nothing is written out of
+ *     bounds; outputs of the offending sequences are then undefined.
+ *   - hstu_last_error() returns a thread-local message for the last failure.
+ */
+#ifndef HSTU_H
+#define HSTU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_ERR_INVALID_ARG = 1,  /* bad scalar, NULL required pointer, bad combination */
+  HSTU_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. d not in {32, 64, 128}) */
+  HSTU_ERR_WORKSPACE = 3,    /* ws NULL or smaller than hstu_workspace_size() */
+  HSTU_ERR_HIP = 4           /* a HIP runtime call or launch failed */
+} hstu_status_t;
+
+typedef enum { HSTU_BF16 = 0, HSTU_F32 = 1 } hstu_dtype_t;
+
+typedef enum { HSTU_NORM_NONE = 0, HSTU_NORM_LN = 1, HSTU_NORM_GLN = 2 } hstu_norm_t;
+
+typedef enum { HSTU_OP_FWD = 0, HSTU_OP_BWD = 1, HSTU_OP_MFALCON = 2 } hstu_op_t;
+
+/* Bits of the device status word (hstu_get_device_status). */
+enum {
+  HSTU_DEV_BAD_OFFSETS = 1,   /* offsets[0] != 0, decreasing, or offsets[B] != total_tokens */
+  HSTU_DEV_BAD_SEGMENTS = 2,  /* prefix_len/cand_len negative or P + C > L */
+  HSTU_DEV_BAD_GROUP = 4,     /* a token group id >= n_groups (that token uses gamma = 1, beta = 0) */
+  HSTU_DEV_TOO_LONG = 8       /* a sequence longer than max_len */
+};
+
+/*
+ * One jagged batch. Scalars are host values; pointers are device pointers.
+ *   B            number of sequences (>= 0)
+ *   H, d         heads and head width (d_qk = d_v = d, d in {32, 64, 128})
+ *   dtype        hstu_dtype_t of the tensors
+ *   total_tokens T = offsets[B]
+ *   max_len      an upper bound of every sequence length (sizes the grids)
+ *   offsets      int32 [B+1], non-decreasing, offsets[0] = 0
+ *   prefix_len   int32 [B] bidirectional prefix per sequence, or NULL (0)
+ *   cand_len     int32 [B] candidate tail per sequence, or NULL (0)
+ *   timestamps   int64 [T] seconds, or NULL (rab_t term off)
+ *   rab_p/n_pos  fp32 [n_pos] position bias shared by all heads, or NULL
+ *   rab_t/n_tb   fp32 [n_tb] time-bucket bias shared by all heads, or NULL
+ *   n_max        the constant N_max >= 1 of the 1/N_max scale
+ *   norm, eps    hstu_norm_t and the LayerNorm epsilon (> 0)
+ *   token_group  uint8 [T] group id per token (GLN only), n_groups in [1, 255]
+ *   gamma, beta  fp32 [n_groups, H*d] affine of the norm, or NULL (identity);
+ *                for LN only row 0 is used
+ */
+typedef struct hstu_problem {
+  int32_t B, H, d, dtype;
+  int64_t total_tokens;
+  int32_t max_len;
+  int32_t n_max;
+  const int32_t *offsets;
+  const int32_t *prefix_len;
+  const int32_t *cand_len;
+  const int64_t *timestamps;
+  const float *rab_p;
+  const float *rab_t;
+  int32_t n_pos, n_tb;
+  int32_t norm;
+  float eps;
+  const uint8_t *token_group;
+  int32_t n_groups;
+  int32_t reserved;
+  const float *gamma;
+  const float *beta;
+} hstu_problem_t;
+
+/* Library version, e.g. "0.1.0". Host only. */
+const char *hstu_version(void);
+
+/* Thread-local text of the last error returned on this thread. Host only. */
+const char *hstu_last_error(void);
+
+/*
+ * Workspace bytes needed by `op` on problem `p` (host only, touches no device
+ * memory). For HSTU_OP_MFALCON, p describes the candidates (see
+ * hstu_mfalcon_score), `microbatch` is the candidates-per-microbatch b_m
+ * (0 = all) and `hist_max_len`, `hist_tokens` bound the cached histories;
+ * the three are ignored for the other ops.
+ */
+hstu_status_t hstu_workspace_size(const hstu_problem_t *p, int32_t op, int32_t microbatch,
+                                  int32_t hist_max_len, int64_t hist_tokens, size_t *bytes);
+
+/*
+ * Forward of the attention core (see the top of this file).
+ *   Q, K, V, U   [T, H, d] inputs
+ *   Y            [T, H*d] output  Norm(O) * U
+ *   O            [T, H*d] output  the pre-norm attention output concat_h o^h
+ *                (saved for hstu_attn_bwd)
+ *   mean, rstd   fp32 [T] per-token statistics of the norm (NULL allowed when
+ *                norm == NONE; then nothing is written)
+ */
+hstu_status_t hstu_attn_fwd(const hstu_problem_t *p, const void *Q, const void *K, const void *V,
+                            const void *U, void *Y, void *O, float *mean, float *rstd, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/*
+ * Backward of hstu_attn_fwd given dY [T, H*d]. O, mean and rstd are the
+ * forward's outputs for the same inputs. Writes dQ, dK, dV, dU (overwritten,
+ * [T, H, d]), d_rab_p [n_pos] and d_rab_t [n_tb] (overwritten; required when
+ * the corresponding table is given, else ignored), d_gamma and d_beta
+ * ([n_groups, H*d], overwritten; NULL skips them; only produced when gamma
+ * resp. beta is given). Timestamps carry no gradient. The rab, gamma and
+ * beta gradients sum over all heads, tokens and sequences.
+ */
+hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *K, const void *V,
+                            const void *U, const void *O, const float *mean, const float *rstd,
+                            const void *dY, void *dQ, void *dK, void *dV, void *dU,
+                            float *d_rab_p, float *d_rab_t, float *d_gamma, float *d_beta,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * M-FALCON ranking (HSTU blog, sections 4.2 "批量推理" and 4.3 "KV Caching"):
+ * score the candidates of B users against each user's cached history K/V.
+ * For user b the result equals the candidate rows of hstu_attn_fwd over the
+ * sequence [history_b | candidates_b] with P = 0 and C = m_b: every candidate
+ * sees the whole history and itself, sits at position n_b, and no candidate
+ * sees another. Only candidate rows are computed.
+ *   cand          describes the candidates: offsets [B+1] over Tc candidate
+ *                 tokens (total_tokens = Tc, max_len = max m_b), timestamps =
+ *                 candidate timestamps (or NULL), rab/norm/group/affine as in
+ *                 hstu_problem_t; prefix_len and cand_len must be NULL.
+ *   hist_offsets  int32 [B+1] over the cached history tokens (hist_tokens
+ *                 total, hist_max_len >= every n_b), host scalars
+ *   K_cache, V_cache  [Th, H, d] cached history keys and values
+ *   hist_ts       int64 [Th] history timestamps (NULL iff cand->timestamps NULL)
+ *   Qc, Kc, Vc, Uc    [Tc, H, d] the candidates' own projections
+ *   microbatch    b_m > 0 cuts each user's candidates into microbatches of b_m
+ *                 (query tiles never span two microbatches); 0 = one
+ *                 microbatch. The result does not depend on b_m.
+ *   Yc, Oc        [Tc, H*d] outputs (Norm(O) * U and the pre-norm O)
+ *   mean, rstd    fp32 [Tc] statistics (NULL allowed when norm == NONE)
+ */
+hstu_status_t hstu_mfalcon_score(const hstu_problem_t *cand, const int32_t *hist_offsets,
+                                 int64_t hist_tokens, int32_t hist_max_len, const void *K_cache,
+                                 const void *V_cache, const int64_t *hist_ts, const void *Qc,
+                                 const void *Kc, const void *Vc, const void *Uc,
+                                 int32_t microbatch, void *Yc, void *Oc, float *mean, float *rstd,
+                                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Query/key tile shape (host only) that `op` uses for `p`'s dtype and d.
+ */
+hstu_status_t hstu_tile_shape(const hstu_problem_t *p, int32_t op, int32_t *BM, int32_t *BN);
+
+/*
+ * Runs only the tile scheduler of `op` (HSTU_OP_FWD or HSTU_OP_MFALCON; for
+ * the latter pass hist_offsets/hist_tokens/hist_max_len/microbatch as for
+ * hstu_mfalcon_score, else NULL/0) on `stream`, waits for it, and copies to
+ * host memory:
+ *   host_qtile_off  int32 [B+1] (host) first query-tile index of each sequence
+ *                   in canonical (sequence, row) order
+ *   host_tiles      int32 [cap][4] (host) one record per query tile in
+ *                   execution order: {b, row0, nk, nf | nrows << 16}, where
+ *                   key tiles [0, nf) are FULL (no mask needed), [nf, nk)
+ *                   PARTIAL, rows [row0, row0 + nrows) are local query rows
+ *                   of sequence b (candidate indices for M-FALCON).
+ *                   Execution order is longest first (nk descending, ties in
+ *                   canonical order) when there are at most 16384 query
+ *                   tiles, canonical otherwise.
+ *   count           (host) number of query tiles (records beyond cap are not
+ *                   copied)
+ * Synchronises the stream. Intended for tests and tools.
+ */
+hstu_status_t hstu_schedule_export(const hstu_problem_t *p, int32_t op,
+                                   const int32_t *hist_offsets, int64_t hist_tokens,
+                                   int32_t hist_max_len, int32_t microbatch, void *ws,
+                                   size_t ws_bytes, void *stream, int32_t *host_qtile_off,
+                                   int32_t *host_tiles, int64_t cap, int64_t *count);
+
+/*
+ * Waits for `stream` and reads the device status word that the last call on
+ * workspace `ws` left (0 = no violation, else HSTU_DEV_* bits) into
+ * *host_code. Synchronises the stream.
+ */
+hstu_status_t hstu_get_device_status(const void *ws, void *stream, int32_t *host_code);
+
+/*
+ * Kernel timing for measurement tools. While enabled (process-wide), every
+ * launch of a library kernel records a pair of HIP events on the stream it is
+ * launched on. hstu_kernel_timing_read waits for the recorded events of one
+ * kernel id, returns their summed duration in milliseconds and the number of
+ * launches, and forgets them. Enabling or disabling also forgets all pending
+ * records. Host only; not for concurrent use from several threads.
+ */
+enum {
+  HSTU_KERNEL_SCHED = 0,     /* tile scheduler */
+  HSTU_KERNEL_ATTN_FWD = 1,  /* attention forward (also M-FALCON scoring) */
+  HSTU_KERNEL_NORM_FWD = 2,  /* Norm(O) * U */
+  HSTU_KERNEL_NORM_BWD = 3,  /* backward of the norm epilogue */
+  HSTU_KERNEL_ATTN_BWD = 4,  /* attention backward (all its kernels) */
+  HSTU_KERNEL_AUX = 5,       /* fills, casts and reductions */
+  HSTU_KERNEL_COUNT = 6
+};
+hstu_status_t hstu_kernel_timing(int32_t enable);
+hstu_status_t hstu_kernel_timing_read(int32_t kernel, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H */

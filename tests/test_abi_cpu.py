@@ -1,0 +1,109 @@
+"""The C-ABI library loads, exports every symbol include/hstu.h declares,
+and rejects bad host-side arguments before touching a device (no GPU
+needed: these calls return before any HIP work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "hstu.h")).read()
+    return sorted(set(re.findall(r"\b(hstu_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from hstu_jagged_pointwise_attn_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from hstu_jagged_pointwise_attn_amd import build
+        build.build()
+    return _lib
+
+
+def test_every_declared_symbol_is_exported(L):
+    lib = L.lib()
+    names = _declared()
+    assert "hstu_attn_fwd" in names and "hstu_attn_bwd" in names and "hstu_mfalcon_score" in names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in L.SIGNATURES, n
+
+
+def test_version(L):
+    assert L.lib().hstu_version().decode().count(".") == 2
+
+
+def _problem(L, **kw):
+    p = L.Problem()
+    p.B, p.H, p.d, p.dtype = 2, 2, 64, L.HSTU_BF16
+    p.total_tokens, p.max_len, p.n_max = 10, 8, 8
+    p.offsets = ctypes.c_void_p(0x1000)  # never dereferenced by the host checks
+    p.norm, p.eps, p.n_groups = L.HSTU_NORM_LN, 1e-5, 1
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _ws(L, p, op=0):
+    n = ctypes.c_size_t(0)
+    st = L.lib().hstu_workspace_size(ctypes.byref(p), op, 0, 0, 0, ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, 0),
+    ({"d": 48}, 2),
+    ({"d": 256}, 2),
+    ({"B": -1}, 1),
+    ({"H": 0}, 1),
+    ({"dtype": 7}, 1),
+    ({"n_max": 0}, 1),
+    ({"offsets": None}, 1),
+    ({"norm": 5}, 1),
+    ({"eps": 0.0}, 1),
+    ({"norm": 2}, 1),               # GLN without token_group
+    ({"total_tokens": -3}, 1),
+    ({"max_len": 2_000_000}, 2),
+    ({"B": 100000}, 2),
+    ({"H": 64, "d": 128}, 2),        # D = 8192 wider than the norm kernel supports
+])
+def test_workspace_size_validation(L, kw, status):
+    st, n = _ws(L, _problem(L, **kw))
+    assert st == status, L.lib().hstu_last_error()
+    if status == 0:
+        assert n > 0 and n % 256 == 0
+    else:
+        assert L.lib().hstu_last_error()
+
+
+def test_fwd_rejects_null_and_small_workspace(L):
+    p = _problem(L)
+    lib = L.lib()
+    dummy = ctypes.c_void_p(0x2000)
+    args = [dummy] * 8
+    st = lib.hstu_attn_fwd(ctypes.byref(p), *args[:6], dummy, dummy, None, 0, None)
+    assert st == L.HSTU_ERR_WORKSPACE
+    st = lib.hstu_attn_fwd(ctypes.byref(p), *args[:6], dummy, dummy, ctypes.c_void_p(0x10000), 16, None)
+    assert st == L.HSTU_ERR_WORKSPACE
+    st = lib.hstu_attn_fwd(ctypes.byref(p), None, *args[:5], dummy, dummy, ctypes.c_void_p(0x10000), 1 << 30, None)
+    assert st == L.HSTU_ERR_INVALID_ARG
+    st = lib.hstu_attn_fwd(ctypes.byref(p), *args[:6], dummy, dummy, ctypes.c_void_p(0x10010), 1 << 30, None)
+    assert st == L.HSTU_ERR_INVALID_ARG  # misaligned workspace
+
+
+def test_mfalcon_rejects_prefix_and_cand_len(L):
+    p = _problem(L, prefix_len=ctypes.c_void_p(0x3000))
+    n = ctypes.c_size_t(0)
+    lib = L.lib()
+    dummy = ctypes.c_void_p(0x2000)
+    st = lib.hstu_mfalcon_score(ctypes.byref(p), dummy, 16, 8, *([dummy] * 7), 0, *([dummy] * 5), 1 << 20, None)
+    assert st == L.HSTU_ERR_INVALID_ARG
+    p = _problem(L)
+    st = lib.hstu_mfalcon_score(ctypes.byref(p), dummy, 16, 8, dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                -1, *([dummy] * 5), 1 << 20, None)
+    assert st == L.HSTU_ERR_INVALID_ARG
+    del n
