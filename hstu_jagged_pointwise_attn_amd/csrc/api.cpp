@@ -303,7 +303,7 @@ hstu_status_t hstu_attn_fwd(const hstu_problem_t *p, const void *Q, const void *
   if (s) return s;
   if (p->total_tokens > 0 && (!Q || !K || !V || !U || !Y || !O))
     return fail(HSTU_ERR_INVALID_ARG, "Q/K/V/U/Y/O must not be NULL");
-  if (p->norm != HSTU_NORM_NONE && (!mean || !rstd))
+  if (p->norm != HSTU_NORM_NONE && p->total_tokens > 0 && (!mean || !rstd))
     return fail(HSTU_ERR_INVALID_ARG, "mean/rstd must not be NULL with a norm");
   Layout L = layout(p, HSTU_OP_FWD, 0, 0);
   s = check_ws(ws, ws_bytes, L.total);
@@ -335,7 +335,7 @@ hstu_status_t hstu_mfalcon_score(const hstu_problem_t *cand, const int32_t *hist
     return fail(HSTU_ERR_INVALID_ARG, "Qc/Kc/Vc/Uc/Yc/Oc must not be NULL");
   if (hist_tokens > 0 && (!K_cache || !V_cache))
     return fail(HSTU_ERR_INVALID_ARG, "K_cache/V_cache must not be NULL");
-  if (cand->norm != HSTU_NORM_NONE && (!mean || !rstd))
+  if (cand->norm != HSTU_NORM_NONE && cand->total_tokens > 0 && (!mean || !rstd))
     return fail(HSTU_ERR_INVALID_ARG, "mean/rstd must not be NULL with a norm");
   Layout L = layout(cand, HSTU_OP_MFALCON, microbatch, hist_max_len);
   s = check_ws(ws, ws_bytes, L.total);
