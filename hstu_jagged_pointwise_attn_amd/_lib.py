@@ -18,6 +18,7 @@ HSTU_OP_FWD, HSTU_OP_BWD, HSTU_OP_MFALCON = 0, 1, 2
 (HSTU_KERNEL_SCHED, HSTU_KERNEL_ATTN_FWD, HSTU_KERNEL_NORM_FWD, HSTU_KERNEL_NORM_BWD, HSTU_KERNEL_ATTN_BWD,
  HSTU_KERNEL_AUX) = range(6)
 HSTU_DEV_BAD_OFFSETS, HSTU_DEV_BAD_SEGMENTS, HSTU_DEV_BAD_GROUP, HSTU_DEV_TOO_LONG = 1, 2, 4, 8
+HSTU_DEV_BAD_TIMESTAMPS = 16
 
 _STATUS_NAMES = {1: "HSTU_ERR_INVALID_ARG", 2: "HSTU_ERR_UNSUPPORTED", 3: "HSTU_ERR_WORKSPACE",
                  4: "HSTU_ERR_HIP"}

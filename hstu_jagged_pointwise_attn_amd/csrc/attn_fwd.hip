@@ -7,24 +7,30 @@
 // bf16 kernel (gfx950 MFMA, v_mfma_f32_16x16x32_bf16, fp32 accumulation):
 //   workgroup = 4 waves = one (query tile of 128 rows, head); each wave owns
 //   32 query rows whose Q fragments stay in registers for the whole key loop.
-//   Per key tile of 64 keys: K is staged row-major in LDS and V transposed
-//   (V^T, so that the A.V operand holds consecutive keys per lane); the wave
-//   computes S^T = K Q^T, whose accumulator layout (lane = query row, 4
-//   consecutive keys per register group) is directly the A operand of
-//   O += P V once the keys of the contraction are taken in the matching
-//   permuted order. The bias gather, SiLU and mask stay in registers; FULL
-//   tiles skip the mask. A candidate's pair with itself is added per row after
-//   the key loop.
+//   Key tiles of 64 keys are double-buffered in LDS (row-major K and V, the
+//   next tile prefetched into registers while the current one is computed,
+//   one barrier per tile). The wave computes S^T = bias + K Q^T with the
+//   accumulator initialised from an LDS window of rab_p; that accumulator
+//   layout (lane = query row, 4 consecutive keys per register group) is
+//   directly the A operand of O += P V once the keys of the contraction are
+//   taken in the matching permuted order, and the V operand comes from the
+//   row-major tile through gfx950's transposing LDS read. SiLU, rab_t and the
+//   mask stay in registers; FULL tiles skip the mask. A candidate's pair with
+//   itself is added per row after the key loop; O leaves through LDS as
+//   16-byte rows.
 // fp32 kernel (vector ALU, fp32 throughout) for the fp32 problems.
 #include "hstu_internal.h"
+#include "../../include/hstu.h"
 
 namespace hstu {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16;
 typedef unsigned int u32;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -51,17 +57,180 @@ __device__ __forceinline__ int pos_bucket(int dp, int n_pos) {
   return dp < n_pos - 1 ? dp : n_pos - 1;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdArgs a) {
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// gfx950 transposing LDS read: within each group of 16 lanes, output lane j,
+// element e is the 16-bit value at (address of source lane 4e + j/4) + j%4.
+__device__ __forceinline__ s16x4 lds_read_tr16(const u16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+}
+
+// |a - b| of two unsigned values (one instruction).
+__device__ __forceinline__ unsigned absdiff_u32(unsigned a, unsigned b) {
+  unsigned d;
+  asm("v_sad_u32 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// Index of the highest set bit counted from the top (0..31), -1 for 0.
+__device__ __forceinline__ int ffbh_u32(unsigned x) {
+  int c;
+  asm("v_ffbh_u32 %0, %1" : "=v"(c) : "v"(x));
+  return c;
+}
+
+__device__ __forceinline__ int bucket_u32(unsigned x, int n_tb) {
+  const int b = x <= 1u ? 0 : 31 - __builtin_clz(x);
+  return b < n_tb - 1 ? b : n_tb - 1;
+}
+
+__device__ __forceinline__ unsigned wave_min_u32(unsigned v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (unsigned)__shfl_xor((int)v, o, 64));
+  return v;
+}
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+// One key tile of K and V (and its rab_p window entry and key timestamp)
+// held in registers between its global load and its LDS store.
+template <int NCH>
+struct TilePrefetch {
+  u32x4 k[NCH], v[NCH];
+  float r;
+  long long t;
+};
+
+// Per-workgroup constants of the key loop.
+struct FwdTileCtx {
+  const u16 *K, *V;
+  const float *rab_p;
+  const int64_t *ts_kv;
+  long long ld;
+  int kv_base, kv_limit, hd, pos_max, n_pos, tid;
+};
+
+template <int D, int BN, bool USE_P, bool USE_T, int NCH>
+__device__ __forceinline__ void fwd_load_tile(TilePrefetch<NCH> &pf, const FwdTileCtx &c, int t) {
+  constexpr int CH = D / 8, WIN = kFwdBM + BN;
+  const int c0 = t * BN;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int chunk = c.tid + i * 256;
+    const int row = chunk / CH, col = (chunk % CH) * 8;
+    const int key = min(c0 + row, c.kv_limit - 1);
+    const long long g = (long long)(c.kv_base + key) * c.ld + c.hd + col;
+    pf.k[i] = *(const u32x4 *)(c.K + g);
+    pf.v[i] = *(const u32x4 *)(c.V + g);
+  }
+  if (USE_P && c.tid < WIN) pf.r = c.rab_p[pos_bucket(c.pos_max - c0 - c.tid, c.n_pos)];
+  if (USE_T && c.tid < BN) pf.t = c.ts_kv[c.kv_base + min(c0 + c.tid, c.kv_limit - 1)];
+}
+
+template <int D, int BN, bool USE_P, bool USE_T, int NCH>
+__device__ __forceinline__ void fwd_store_tile(const TilePrefetch<NCH> &pf, int tid, u16 *Kb, u16 *Vb,
+                                               float *rw, unsigned *tk, unsigned *tst, long long t_ref,
+                                               bool &bad_t) {
+  constexpr int CH = D / 8, WIN = kFwdBM + BN, KST = D + 8, VST = D + 16;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int chunk = tid + c * 256;
+    const int row = chunk / CH, col = (chunk % CH) * 8;
+    *(u32x4 *)(Kb + row * KST + col) = pf.k[c];
+    *(u32x4 *)(Vb + row * VST + col) = pf.v[c];
+  }
+  if (USE_P && tid < WIN) rw[tid] = pf.r;
+  if (USE_T && tid < BN) {  // exactly wave 0
+    const long long dk = pf.t - t_ref;
+    bad_t |= dk < -2147483648LL || dk > 2147483647LL;
+    const unsigned u = (unsigned)(dk + 2147483648LL);
+    tk[tid] = u;
+    const unsigned mn = wave_min_u32(u), mx = wave_max_u32(u);
+    if (tid == 0) {
+      tst[0] = mn;
+      tst[1] = mx;
+    }
+  }
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(u32, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// P = SiLU(S + rab_t) (masked on PARTIAL tiles) as the bf16 A operands of
+// P V: pa[nq][kk] holds keys kk*32 + {lg*4 + 0..3, 16 + lg*4 + 0..3}.
+// FULL: every pair of the tile is visible. TCONST: rab_t is the scalar tcv
+// for the whole block, else it is gathered per element.
+template <bool FULL, bool USE_T, bool TCONST>
+__device__ __forceinline__ void fwd_epilogue(const f32x4 (&st)[4][2], bf16x8 (&pa)[2][2],
+                                             const int (&hirel)[2], const unsigned (&tq)[2],
+                                             const unsigned *tkb, const float *t2tab, float tcv,
+                                             int lg) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    u32x4 w[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int mk = kk * 2 + h2;
+      u32x4 tk4 = {0u, 0u, 0u, 0u};
+      if (USE_T && !TCONST) tk4 = *(const u32x4 *)(tkb + mk * 16 + lg * 4);
+#pragma unroll
+      for (int nq = 0; nq < 2; ++nq) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = st[mk][nq][i];
+          if (USE_T) x += TCONST ? tcv : t2tab[ffbh_u32(absdiff_u32(tq[nq], tk4[i])) + 1];
+          p[i] = silu_fast(x);
+          if (!FULL) p[i] = hirel[nq] > mk * 16 + i ? p[i] : 0.f;
+        }
+        w[nq][h2 * 2] = pack_bf16x2(p[0], p[1]);
+        w[nq][h2 * 2 + 1] = pack_bf16x2(p[2], p[3]);
+      }
+    }
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq) pa[nq][kk] = __builtin_bit_cast(bf16x8, w[nq]);
+  }
+}
+
+// Timestamps enter the kernel as int64 and are used as 32-bit values biased
+// by 2^31 around a per-tile reference t_ref (the first query row's time):
+// u = (t - t_ref) + 2^31. For any two tokens of a sequence whose times are
+// within 2^31 s of each other, |u_i - u_j| is exactly |t_i - t_j|; a larger
+// span is flagged in the status word.
+//
+// Per key tile and wave the time bucket of all (row, key) pairs is checked
+// for being one constant (times usually grow along a sequence, so the bucket
+// of a distant key tile rarely changes); then rab_t is one scalar for the
+// whole block, else it is gathered per element from a 33-entry LDS table
+// indexed by ffbh(|dt|) + 1.
+template <int D, bool USE_P, bool USE_T>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
-  constexpr int KS = D / 32;     // k-steps of the K Q^T contraction
-  constexpr int ND = D / 16;     // 16-column blocks of O
-  constexpr int KPAD = D + 8;    // LDS row stride of K (elements)
-  constexpr int VPAD = BN + 4;   // LDS row stride of V^T (elements)
-  static_assert(BM == 128 && BN == 64, "wave layout assumes 4 waves x 32 rows, 64 keys");
-  __shared__ __attribute__((aligned(16))) u16 Ks[BN * KPAD];
-  __shared__ __attribute__((aligned(16))) u16 Vt[D * VPAD];
-  __shared__ long long tsk[BN];
+  constexpr int KS = D / 32;          // k-steps of the K Q^T contraction
+  constexpr int ND = D / 16;          // 16-column blocks of O
+  constexpr int KST = D + 8;          // LDS row stride of K (elements)
+  constexpr int VST = D + 16;         // LDS row stride of V (elements)
+  constexpr int OST = D + 8;          // LDS row stride of the staged output
+  constexpr int CH = D / 8;           // 16-byte chunks per row
+  constexpr int NCH = BN * CH / 256;  // chunks per thread per matrix and tile
+  constexpr int WIN = BM + BN;        // rab_p window entries per key tile
+  static_assert(BM == 128 && BN == 64, "4 waves x 32 rows, 64 keys");
+  static_assert(BM * OST <= 2 * BN * KST, "output staging reuses the K buffers");
+  __shared__ __attribute__((aligned(16))) u16 Ks[2 * BN * KST];
+  __shared__ __attribute__((aligned(16))) u16 Vs[2 * BN * VST];
+  __shared__ float rabw[USE_P ? 2 * WIN : 1];
+  __shared__ __attribute__((aligned(16))) unsigned tkey[USE_T ? 2 * BN : 4];
+  __shared__ unsigned tkst[4];
+  __shared__ float t2tab[33];
+  __shared__ int s_bad;
 
   const int H = a.H;
   const int unit = blockIdx.x;
@@ -73,24 +242,41 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int row0 = tile.row0;
   const long long ld = (long long)H * D;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-
   const u16 *Q = (const u16 *)a.Q, *K = (const u16 *)a.K, *V = (const u16 *)a.V;
-  const bool use_p = a.rab_p != nullptr;
-  const bool use_t = a.rab_t != nullptr;
 
-  // Rows of this lane in the S^T layout: local rows w*32 + nq*16 + lr.
-  int hi_r[2], pos_r[2];
-  long long ts_r[2];
+  const int fi0 = sd.q_frame0 + row0;
+  const int fil = fi0 + nrows - 1;
+  const int kv_limit = frame_hi(fil, sd.P, sd.E);  // keys >= kv_limit are seen by no row here
+  const int pos_max = fil < sd.E ? fil : sd.E;
+  const long long t_ref = USE_T ? a.ts_q[sd.q_base + row0] : 0;
+
+  if (tid == 0) s_bad = 0;
+  if (USE_T && tid < 33) {
+    const int c = tid - 1;
+    const int bkt = c < 0 ? 0 : 31 - c;
+    t2tab[tid] = a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1];
+  }
+  __syncthreads();
+
+  // This lane's query rows in the S^T layout: local rows w*32 + nq*16 + lr.
+  int hi_r[2], vb_r[2];
+  unsigned tq_r[2] = {0u, 0u};
   bool ok_r[2];
   bf16x8 qf[2][KS];
+  bool bad_t = false;
 #pragma unroll
   for (int nq = 0; nq < 2; ++nq) {
     const int lrow = w * 32 + nq * 16 + lr;
     ok_r[nq] = lrow < nrows;
-    const int fi = sd.q_frame0 + row0 + lrow;
+    const int crow = ok_r[nq] ? lrow : nrows - 1;
+    const int fi = fi0 + crow;
     hi_r[nq] = ok_r[nq] ? frame_hi(fi, sd.P, sd.E) : 0;
-    pos_r[nq] = fi < sd.E ? fi : sd.E;
-    ts_r[nq] = (use_t && ok_r[nq]) ? a.ts_q[sd.q_base + row0 + lrow] : 0;
+    vb_r[nq] = pos_max - (fi < sd.E ? fi : sd.E) + lg * 4;
+    if (USE_T) {
+      const long long dq = a.ts_q[sd.q_base + row0 + crow] - t_ref;
+      bad_t |= dq < -2147483648LL || dq > 2147483647LL;
+      tq_r[nq] = (unsigned)(dq + 2147483648LL);
+    }
     const u16 *qp = Q + (long long)(sd.q_base + row0 + lrow) * ld + h * D + lg * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -99,114 +285,138 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdArgs a) {
       qf[nq][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  unsigned qmin = 0, qmax = 0;
+  if (USE_T) {
+    qmin = __builtin_amdgcn_readfirstlane(wave_min_u32(min(tq_r[0], tq_r[1])));
+    qmax = __builtin_amdgcn_readfirstlane(wave_max_u32(max(tq_r[0], tq_r[1])));
+  }
 
+  // Global -> register prefetch of one key tile, and register -> LDS store.
+  TilePrefetch<NCH> pf;
+  pf.r = 0.f;
+  pf.t = 0;
+  FwdTileCtx cx;
+  cx.K = K; cx.V = V; cx.rab_p = a.rab_p; cx.ts_kv = a.ts_kv; cx.ld = ld;
+  cx.kv_base = sd.kv_base; cx.kv_limit = kv_limit; cx.hd = h * D; cx.pos_max = pos_max;
+  cx.n_pos = a.n_pos; cx.tid = tid;
   f32x4 acc[2][ND];
 #pragma unroll
   for (int nq = 0; nq < 2; ++nq)
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) acc[nq][nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 st[4][2];
+  bf16x8 pa[2][2];
 
-  // Keys at or beyond kv_limit are never visible to any row of this tile and
-  // are zero-filled instead of loaded.
-  const int kv_limit = frame_hi(sd.q_frame0 + row0 + nrows - 1, sd.P, sd.E);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int c0 = kt * BN;
-    __syncthreads();
-    for (int c = tid; c < BN * (D / 8); c += 256) {
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (c0 + row < kv_limit)
-        v = *(const uint4 *)(K + (long long)(sd.kv_base + c0 + row) * ld + h * D + col);
-      *(uint4 *)(Ks + row * KPAD + col) = v;
-    }
-    for (int c = tid; c < (BN / 4) * (D / 8); c += 256) {
-      const int kq = c % (BN / 4), dc = c / (BN / 4);
-      uint4 v[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int row = kq * 4 + k;
-        v[k] = uint4{0u, 0u, 0u, 0u};
-        if (c0 + row < kv_limit)
-          v[k] = *(const uint4 *)(V + (long long)(sd.kv_base + c0 + row) * ld + h * D + dc * 8);
-      }
-      const u32 *w0 = (const u32 *)&v[0], *w1 = (const u32 *)&v[1];
-      const u32 *w2 = (const u32 *)&v[2], *w3 = (const u32 *)&v[3];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        const u32 x0 = (w0[e >> 1] >> sh) & 0xffffu, x1 = (w1[e >> 1] >> sh) & 0xffffu;
-        const u32 x2 = (w2[e >> 1] >> sh) & 0xffffu, x3 = (w3[e >> 1] >> sh) & 0xffffu;
-        uint2 o = {x0 | (x1 << 16), x2 | (x3 << 16)};
-        *(uint2 *)(Vt + (dc * 8 + e) * VPAD + kq * 4) = o;
-      }
-    }
-    if (tid < BN) tsk[tid] = (use_t && c0 + tid < kv_limit) ? a.ts_kv[sd.kv_base + c0 + tid] : 0;
-    __syncthreads();
-
-    // S^T = K Q^T : st[mk][nq] lane holds S(row nq*16+lr, key c0+mk*16+lg*4+i)
-    f32x4 st[4][2];
+  // S^T = bias + K Q^T for the key tile in buffer buf.
+  auto qk = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int mk = 0; mk < 4; ++mk)
 #pragma unroll
-      for (int nq = 0; nq < 2; ++nq) st[mk][nq] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nq = 0; nq < 2; ++nq) {
+        if (USE_P) {
+          const float *rw = rabw + buf * WIN + vb_r[nq] + mk * 16;
+          st[mk][nq] = f32x4{rw[0], rw[1], rw[2], rw[3]};
+        } else {
+          st[mk][nq] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    const u16 *kb = Ks + buf * BN * KST;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int mk = 0; mk < 4; ++mk) {
-        const bf16x8 kf = *(const bf16x8 *)(Ks + (mk * 16 + lr) * KPAD + ks * 32 + lg * 8);
+        const bf16x8 kf = *(const bf16x8 *)(kb + (mk * 16 + lr) * KST + ks * 32 + lg * 8);
 #pragma unroll
         for (int nq = 0; nq < 2; ++nq)
           st[mk][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[nq][ks], st[mk][nq], 0, 0, 0);
       }
     }
+  };
 
-    // Bias, SiLU, mask, and the bf16 A operands of P V.
-    const bool full = kt < nf;
-    bf16x8 pa[2][2];
-#pragma unroll
-    for (int mk = 0; mk < 4; ++mk) {
-#pragma unroll
-      for (int nq = 0; nq < 2; ++nq) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int jl = mk * 16 + lg * 4 + i;
-          const int j = c0 + jl;
-          float x = st[mk][nq][i];
-          if (use_p) x += a.rab_p[pos_bucket(pos_r[nq] - j, a.n_pos)];
-          if (use_t) x += a.rab_t[time_bucket(ts_r[nq] - tsk[jl], a.n_tb)];
-          float p = silu_fast(x);
-          if (!full && j >= hi_r[nq]) p = 0.f;
-          pa[nq][mk >> 1][(mk & 1) * 4 + i] = (__bf16)p;
-        }
-      }
-    }
-
-    // O += P V with the contraction keys in the order of the S^T layout.
+  // O += P V with V read transposed from its row-major LDS tile.
+  auto pv = [&](int buf) __attribute__((always_inline)) {
+    const u16 *vb = Vs + buf * BN * VST;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) {
-        const u16 *vp = Vt + (nd * 16 + lr) * VPAD + kk * 32 + lg * 4;
-        const uint2 v0 = *(const uint2 *)vp, v1 = *(const uint2 *)(vp + 16);
-        const bf16x8 vb = __builtin_bit_cast(bf16x8, uint4{v0.x, v0.y, v1.x, v1.y});
+        const u16 *p0 = vb + (kk * 32 + lg * 4 + (lr >> 2)) * VST + nd * 16 + (lr & 3) * 4;
+        const s16x4 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * VST);
+        const bf16x8 vbf = __builtin_bit_cast(
+            bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
         for (int nq = 0; nq < 2; ++nq)
-          acc[nq][nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[nq][kk], vb, acc[nq][nd], 0, 0, 0);
+          acc[nq][nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[nq][kk], vbf, acc[nq][nd], 0, 0, 0);
       }
+    }
+  };
+
+  if (nk > 0) {
+    fwd_load_tile<D, BN, USE_P, USE_T>(pf, cx, 0);
+    fwd_store_tile<D, BN, USE_P, USE_T>(pf, tid, Ks, Vs, rabw, tkey, tkst, t_ref, bad_t);
+    if (nk > 1) fwd_load_tile<D, BN, USE_P, USE_T>(pf, cx, 1);
+    __syncthreads();
+    qk(0);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int b = kt & 1;
+    const int c0 = kt * BN;
+    const bool full = kt < nf;
+    int hirel[2];
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq) hirel[nq] = hi_r[nq] - (c0 + lg * 4);
+
+    // rab_t: one constant for the block when all its pairs share a bucket.
+    bool tconst = true;
+    float tcv = 0.f;
+    if (USE_T) {
+      const unsigned kmin = __builtin_amdgcn_readfirstlane(tkst[b * 2]);
+      const unsigned kmax = __builtin_amdgcn_readfirstlane(tkst[b * 2 + 1]);
+      unsigned dlo, dhi;
+      if (qmin >= kmax) {
+        dlo = qmin - kmax;
+        dhi = qmax - kmin;
+      } else if (kmin >= qmax) {
+        dlo = kmin - qmax;
+        dhi = kmax - qmin;
+      } else {
+        dlo = 0u;
+        dhi = max(qmax - kmin, kmax - qmin);
+      }
+      const int blo = bucket_u32(dlo, a.n_tb), bhi = bucket_u32(dhi, a.n_tb);
+      tconst = blo == bhi;
+      tcv = a.rab_t[blo];
+    }
+
+    const unsigned *tkb = tkey + b * (USE_T ? BN : 0);
+    if (USE_T && !tconst) {
+      if (full) fwd_epilogue<true, USE_T, false>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
+      else fwd_epilogue<false, USE_T, false>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
+    } else {
+      if (full) fwd_epilogue<true, USE_T, true>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
+      else fwd_epilogue<false, USE_T, true>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
+    }
+    pv(b);
+    if (kt + 1 < nk) {
+      fwd_store_tile<D, BN, USE_P, USE_T>(pf, tid, Ks + (b ^ 1) * BN * KST, Vs + (b ^ 1) * BN * VST,
+                                          rabw + (b ^ 1) * (USE_P ? WIN : 0), tkey + (b ^ 1) * (USE_T ? BN : 0),
+                                          tkst + (b ^ 1) * 2, t_ref, bad_t);
+      if (kt + 2 < nk) fwd_load_tile<D, BN, USE_P, USE_T>(pf, cx, kt + 2);
+      __syncthreads();
+      qk(b ^ 1);
     }
   }
 
   // A candidate's pair with itself: o_i += SiLU(q_i.k_i + rab_p[0] + rab_t[0]) v_i.
-  const bool any_cand = sd.q_frame0 + row0 + nrows - 1 >= sd.E;
+  const bool any_cand = fil >= sd.E;
   if (any_cand) {
     const u16 *Ksf = (const u16 *)a.Kself, *Vsf = (const u16 *)a.Vself;
-    const float bias0 = (use_p ? a.rab_p[0] : 0.f) + (use_t ? a.rab_t[0] : 0.f);
+    const float bias0 = (USE_P ? a.rab_p[0] : 0.f) + (USE_T ? a.rab_t[0] : 0.f);
     float as[2];
 #pragma unroll
     for (int nq = 0; nq < 2; ++nq) {
       const int lrow = w * 32 + nq * 16 + lr;
-      const int fi = sd.q_frame0 + row0 + lrow;
+      const int fi = fi0 + lrow;
       const bool cand = ok_r[nq] && fi >= sd.E;
       float part = 0.f;
       if (cand) {
@@ -229,7 +439,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdArgs a) {
       for (int i = 0; i < 4; ++i) {
         const float av = __shfl(as[nq], lg * 4 + i, 64);
         const int lrow = w * 32 + nq * 16 + lg * 4 + i;
-        const int fi = sd.q_frame0 + row0 + lrow;
+        const int fi = fi0 + lrow;
         if (lrow < nrows && fi >= sd.E) {
           const u16 *vp = Vsf + (long long)(sd.self_base + fi - sd.E) * ld + h * D + lr;
 #pragma unroll
@@ -239,22 +449,31 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdArgs a) {
     }
   }
 
-  u16 *O = (u16 *)a.O;
+  if (USE_T && bad_t) atomicOr(&s_bad, 1);
+  // Stage O through LDS (the K buffers) so that global stores are 16-byte rows.
+  __syncthreads();
+  u16 *os = Ks;
 #pragma unroll
   for (int nq = 0; nq < 2; ++nq) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int lrow = w * 32 + nq * 16 + lg * 4 + i;
-      if (lrow < nrows) {
-        u16 *op = O + (long long)(sd.q_base + row0 + lrow) * ld + h * D + lr;
 #pragma unroll
-        for (int nd = 0; nd < ND; ++nd) {
-          const __bf16 v = (__bf16)(acc[nq][nd][i] * a.inv_nmax);
-          op[nd * 16] = __builtin_bit_cast(u16, v);
-        }
+      for (int nd = 0; nd < ND; ++nd) {
+        const __bf16 v = (__bf16)(acc[nq][nd][i] * a.inv_nmax);
+        os[lrow * OST + nd * 16 + lr] = __builtin_bit_cast(u16, v);
       }
     }
   }
+  __syncthreads();
+  u16 *O = (u16 *)a.O;
+  for (int c = tid; c < BM * CH; c += 256) {
+    const int row = c / CH, col = (c % CH) * 8;
+    if (row < nrows)
+      *(uint4 *)(O + (long long)(sd.q_base + row0 + row) * ld + h * D + col) =
+          *(const uint4 *)(os + row * OST + col);
+  }
+  if (USE_T && tid == 0 && s_bad) atomicOr(&a.hdr[kHdrStatus], HSTU_DEV_BAD_TIMESTAMPS);
 }
 
 // fp32: 256 threads = 64 rows x 4 column slices of D/4; keys staged in LDS.
@@ -344,15 +563,24 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
 
 }  // namespace
 
+template <int D>
+hipError_t launch_bf16_d(const FwdArgs &a, hipStream_t s) {
+  const bool p = a.rab_p != nullptr, t = a.rab_t != nullptr;
+  if (p && t) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true>), dim3(a.units), dim3(256), 0, s, a);
+  else if (p) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false>), dim3(a.units), dim3(256), 0, s, a);
+  else if (t) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, true>), dim3(a.units), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false>), dim3(a.units), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_fwd_bf16(const FwdArgs &a, hipStream_t s) {
   if (a.units <= 0) return hipSuccess;
   switch (a.d) {
-    case 32: hipLaunchKernelGGL(attn_fwd_bf16_kernel<32>, dim3(a.units), dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3(a.units), dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3(a.units), dim3(256), 0, s, a); break;
+    case 32: return launch_bf16_d<32>(a, s);
+    case 64: return launch_bf16_d<64>(a, s);
+    case 128: return launch_bf16_d<128>(a, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_f32(const FwdArgs &a, hipStream_t s) {

@@ -71,7 +71,7 @@ struct FwdArgs {
   int n_pos, n_tb;
   float inv_nmax;
   int H, d;
-  const int *hdr;
+  int *hdr;                       // header words (tile count in, status bits out)
   const SeqDesc *desc;
   const QTile *tiles;
   int units;                      // grid size bound: max query tiles * H

@@ -43,7 +43,8 @@
  *     Host-visible preconditions (scalars, NULL pointers, sizes) are checked
  *     before anything is enqueued. Device-data preconditions (offsets
  *     non-decreasing from 0 up to total_tokens, P + C <= L, group ids <
- *     n_groups, lengths <= max_len) are checked by the kernels: the first
+ *     n_groups, lengths <= max_len, timestamps of a sequence within 2^31 s
+ *     of each other) are checked by the kernels: the first
  *     violation is recorded in the workspace (hstu_get_device_status), the
  *     offending sequences are treated as empty and nothing is written out of
  *     bounds; outputs of the offending sequences are then undefined.
@@ -78,7 +79,9 @@ enum {
   HSTU_DEV_BAD_OFFSETS = 1,   /* offsets[0] != 0, decreasing, or offsets[B] != total_tokens */
   HSTU_DEV_BAD_SEGMENTS = 2,  /* prefix_len/cand_len negative or P + C > L */
   HSTU_DEV_BAD_GROUP = 4,     /* a token group id >= n_groups (that token uses gamma = 1, beta = 0) */
-  HSTU_DEV_TOO_LONG = 8       /* a sequence longer than max_len */
+  HSTU_DEV_TOO_LONG = 8,      /* a sequence longer than max_len */
+  HSTU_DEV_BAD_TIMESTAMPS = 16 /* timestamps of one sequence span 2^31 s or more (rab_t terms of
+                                  that sequence are then undefined) */
 };
 
 /*
