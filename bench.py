@@ -234,8 +234,6 @@ def main():
     log(f"[bench] {ms:.4f} ms/step, {value:.2f} useful TFLOP/s")
 
     # Dominant kernel: timed per launch with HIP events on its launch stream.
-    dom = _lib.HSTU_KERNEL_ATTN_BWD if kind == "fwdbwd" else _lib.HSTU_KERNEL_ATTN_FWD
-    dom_name = "attn_bwd" if kind == "fwdbwd" else "attn_fwd"
     api.kernel_timing(True)
     for _ in range(args.steps):
         step()
@@ -243,14 +241,20 @@ def main():
     per = {}
     for kid, kname in ((_lib.HSTU_KERNEL_SCHED, "sched"), (_lib.HSTU_KERNEL_ATTN_FWD, "attn_fwd"),
                        (_lib.HSTU_KERNEL_NORM_FWD, "norm_fwd"), (_lib.HSTU_KERNEL_NORM_BWD, "norm_bwd"),
-                       (_lib.HSTU_KERNEL_ATTN_BWD, "attn_bwd"), (_lib.HSTU_KERNEL_AUX, "aux")):
+                       (_lib.HSTU_KERNEL_ATTN_BWD_DQ, "attn_bwd_dq"),
+                       (_lib.HSTU_KERNEL_ATTN_BWD_DKDV, "attn_bwd_dkdv"), (_lib.HSTU_KERNEL_AUX, "aux")):
         tms, n = api.kernel_timing_read(kid)
         if n:
             per[kname] = tms / n
     api.kernel_timing(False)
     log("[bench] per-launch ms: " + ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
+    # Dominant kernel: the longest one; each attention kernel carries 4*d
+    # useful FLOPs per visible pair and head (forward: Q.K and A.V; backward
+    # query pass: dA and dQ; key pass: dV and dK).
+    cands = ["attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"]
+    dom_name = max((k for k in cands if k in per), key=lambda k: per[k])
     dom_ms = per.get(dom_name)
-    dom_flops = (8.0 if kind == "fwdbwd" else 4.0) * (src.d) * pairs
+    dom_flops = 4.0 * src.d * pairs
     peak = PEAK_F32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms else None
     roofline = {"bound": "mfma" if dtype == "bf16" else "alu", "achieved": achieved, "peak": peak,

@@ -89,14 +89,16 @@ struct Tiles {
 
 Tiles tiles_for(const hstu_problem_t *p, int op) {
   if (p->dtype == HSTU_F32) return {kF32BM, kF32BN};
-  (void)op;
-  return {kFwdBM, kFwdBN};
+  return {kFwdBM, kFwdBN};  // the backward's query-major pass uses the forward's tiles
 }
 
 // Workspace sections (byte offsets from ws).
 struct Layout {
   size_t hdr, desc, qoff, tiles, total;
   long long max_tiles;
+  // backward only: key-major schedule and the gradient of the pre-norm output
+  size_t khdr, kdesc, kqoff, ktiles, dO, dO32;
+  long long max_ktiles;
 };
 
 Layout layout(const hstu_problem_t *p, int op, int microbatch, int hist_max_len) {
@@ -116,6 +118,18 @@ Layout layout(const hstu_problem_t *p, int op, int microbatch, int hist_max_len)
   L.desc = off;  off += align256(sizeof(SeqDesc) * (size_t)(p->B > 0 ? p->B : 1));
   L.qoff = off;  off += align256(sizeof(int) * (size_t)(p->B + 1));
   L.tiles = off; off += align256(sizeof(QTile) * (size_t)(nq > 0 ? nq : 1));
+  if (op == HSTU_OP_BWD) {
+    const long long nk = div_up(p->total_tokens, kBwdKBN) + p->B;
+    L.max_ktiles = nk;
+    L.khdr = off;   off += align256(kHdrWords * sizeof(int));
+    L.kdesc = off;  off += align256(sizeof(SeqDesc) * (size_t)(p->B > 0 ? p->B : 1));
+    L.kqoff = off;  off += align256(sizeof(int) * (size_t)(p->B + 1));
+    L.ktiles = off; off += align256(sizeof(QTile) * (size_t)(nk > 0 ? nk : 1));
+    const size_t esz = p->dtype == HSTU_BF16 ? 2 : 4;
+    L.dO = off;     off += align256(esz * (size_t)p->total_tokens * p->H * p->d + 16);
+    L.dO32 = off;
+    if (p->dtype == HSTU_BF16) off += align256(4 * (size_t)p->total_tokens * p->H * p->d + 16);
+  }
   L.total = off;
   return L;
 }
@@ -283,7 +297,6 @@ hstu_status_t hstu_workspace_size(const hstu_problem_t *p, int32_t op, int32_t m
     if (microbatch < 0) return fail(HSTU_ERR_INVALID_ARG, "microbatch = %d < 0", microbatch);
     (void)hist_tokens;
   }
-  if (op == HSTU_OP_BWD) return fail(HSTU_ERR_UNSUPPORTED, "backward not built yet");
   *bytes = layout(p, op, microbatch, hist_max_len).total;
   return HSTU_OK;
 }
@@ -356,12 +369,104 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
                             const void *dY, void *dQ, void *dK, void *dV, void *dU,
                             float *d_rab_p, float *d_rab_t, float *d_gamma, float *d_beta,
                             void *ws, size_t ws_bytes, void *stream) {
-  (void)Q; (void)K; (void)V; (void)U; (void)O; (void)mean; (void)rstd; (void)dY; (void)dQ;
-  (void)dK; (void)dV; (void)dU; (void)d_rab_p; (void)d_rab_t; (void)d_gamma; (void)d_beta;
-  (void)ws; (void)ws_bytes; (void)stream;
   hstu_status_t s = check_problem(p, HSTU_OP_BWD);
   if (s) return s;
-  return fail(HSTU_ERR_UNSUPPORTED, "backward not built yet");
+  const long long T = p->total_tokens;
+  if (T > 0 && (!Q || !K || !V || !U || !O || !dY || !dQ || !dK || !dV || !dU))
+    return fail(HSTU_ERR_INVALID_ARG, "Q/K/V/U/O/dY/dQ/dK/dV/dU must not be NULL");
+  if (p->norm != HSTU_NORM_NONE && T > 0 && (!mean || !rstd))
+    return fail(HSTU_ERR_INVALID_ARG, "mean/rstd must not be NULL with a norm");
+  const bool use_t = p->rab_t && p->timestamps;
+  if (p->rab_p && !d_rab_p) return fail(HSTU_ERR_INVALID_ARG, "d_rab_p must not be NULL when rab_p is given");
+  if (use_t && !d_rab_t) return fail(HSTU_ERR_INVALID_ARG, "d_rab_t must not be NULL when rab_t is used");
+  Layout L = layout(p, HSTU_OP_BWD, 0, 0);
+  s = check_ws(ws, ws_bytes, L.total);
+  if (s) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const int D = p->H * p->d;
+  const bool bf16 = p->dtype == HSTU_BF16;
+
+  // Query-major and key-major schedules.
+  SchedArgs qa;
+  fill_sched(qa, p, HSTU_OP_BWD, L, ws, nullptr, 0, 0, 0);
+  SchedArgs ka = qa;
+  ka.mode = kSchedKeys;
+  ka.BM = kBwdKBM;
+  ka.BN = kBwdKBN;
+  ka.max_tiles = (int)L.max_ktiles;
+  ka.hdr = at<int>(ws, L.khdr);
+  ka.desc = at<SeqDesc>(ws, L.kdesc);
+  ka.qoff = at<int>(ws, L.kqoff);
+  ka.tiles = at<QTile>(ws, L.ktiles);
+  {
+    Timed t_(HSTU_KERNEL_SCHED, st);
+    HIP_TRY(launch_sched(qa, st), "scheduler launch");
+    HIP_TRY(launch_sched(ka, st), "key scheduler launch");
+  }
+  const int G = p->norm == HSTU_NORM_GLN ? p->n_groups : 1;
+  float *dg = (p->gamma && p->norm != HSTU_NORM_NONE) ? d_gamma : nullptr;
+  float *db = (p->beta && p->norm != HSTU_NORM_NONE) ? d_beta : nullptr;
+  {
+    Timed t_(HSTU_KERNEL_AUX, st);
+    if (p->rab_p) HIP_TRY(launch_fill_f32(d_rab_p, p->n_pos, 0.f, st), "fill");
+    if (use_t) HIP_TRY(launch_fill_f32(d_rab_t, p->n_tb, 0.f, st), "fill");
+    else if (p->rab_t && d_rab_t) HIP_TRY(launch_fill_f32(d_rab_t, p->n_tb, 0.f, st), "fill");
+    if (dg) HIP_TRY(launch_fill_f32(dg, (long long)G * D, 0.f, st), "fill");
+    if (db) HIP_TRY(launch_fill_f32(db, (long long)G * D, 0.f, st), "fill");
+  }
+  void *dO = at<char>(ws, L.dO);
+  {
+    NormBwdArgs n;
+    std::memset(&n, 0, sizeof n);
+    n.X = O; n.U = U; n.dY = dY; n.mean = mean; n.rstd = rstd;
+    n.group = p->norm == HSTU_NORM_GLN ? p->token_group : nullptr;
+    n.gamma = p->gamma; n.beta = p->beta;
+    n.n_groups = G;
+    n.mode = p->norm;
+    n.T = T;
+    n.D = D;
+    n.tokens_per_wave = 32;
+    n.dU = dU; n.dX = dO;
+    n.dX32 = bf16 ? at<float>(ws, L.dO32) : nullptr;
+    n.dgamma = dg; n.dbeta = db;
+    Timed t_(HSTU_KERNEL_NORM_BWD, st);
+    HIP_TRY(launch_norm_bwd(n, bf16, st), "norm backward launch");
+  }
+  BwdArgs b;
+  std::memset(&b, 0, sizeof b);
+  b.Q = Q; b.K = K; b.V = V; b.dO = dO;
+  b.dO32 = bf16 ? at<float>(ws, L.dO32) : (const float *)dO;
+  b.dQ = dQ; b.dK = dK; b.dV = dV;
+  b.ts = use_t ? p->timestamps : nullptr;
+  b.rab_p = p->rab_p;
+  b.rab_t = use_t ? p->rab_t : nullptr;
+  b.drab_p = d_rab_p;
+  b.drab_t = d_rab_t;
+  b.n_pos = p->n_pos;
+  b.n_tb = p->n_tb;
+  b.inv_nmax = 1.0f / (float)p->n_max;
+  b.H = p->H;
+  b.d = p->d;
+  b.hdr = qa.hdr;
+  b.desc = qa.desc;
+  b.tiles = qa.tiles;
+  long long units = L.max_tiles * p->H;
+  if (units >= (1ll << 31) || L.max_ktiles * p->H >= (1ll << 31))
+    return fail(HSTU_ERR_UNSUPPORTED, "too many work units");
+  b.units = (int)units;
+  {
+    Timed t_(HSTU_KERNEL_ATTN_BWD_DQ, st);
+    HIP_TRY(bf16 ? launch_attn_bwd_dq_bf16(b, st) : launch_attn_bwd_dq_f32(b, st), "dq launch");
+  }
+  b.hdr = ka.hdr;
+  b.desc = ka.desc;
+  b.tiles = ka.tiles;
+  b.units = (int)(L.max_ktiles * p->H);
+  {
+    Timed t_(HSTU_KERNEL_ATTN_BWD_DKDV, st);
+    HIP_TRY(bf16 ? launch_attn_bwd_dkdv_bf16(b, st) : launch_attn_bwd_dkdv_f32(b, st), "dkdv launch");
+  }
+  return HSTU_OK;
 }
 
 hstu_status_t hstu_schedule_export(const hstu_problem_t *p, int32_t op,

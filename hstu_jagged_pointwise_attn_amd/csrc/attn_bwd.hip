@@ -1,2 +1,982 @@
-// Backward attention kernels (filled in with the backward pass).
+// Backward of the HSTU pointwise-attention core. With s_ij the logit,
+// a_ij = SiLU(s_ij)/N_max on visible pairs and dO the gradient of the
+// pre-norm output (HSTU blog, section 3 layer formula; SiLU from 3.1):
+//   dV_j += a_ij dO_i,   dA_ij = <dO_i, v_j>,
+//   dS_ij = dA_ij * SiLU'(s_ij) / N_max,   SiLU'(x) = sig(x) (1 + x (1 - sig(x))),
+//   dQ_i += dS_ij k_j,   dK_j += dS_ij q_i,
+//   d rab_p[min(|pos_i - pos_j|, n_pos-1)] += dS_ij,  d rab_t[bucket(t_i - t_j)] += dS_ij.
+// Nothing of size O(n^2) is kept from the forward: S is recomputed (the
+// activation-memory design of the HSTU blog, section 3.3).
+//
+// Two passes, no atomics on dQ/dK/dV:
+//  * query-major (dq kernel): the forward's loop with dO next to Q in
+//    registers; per key tile S^T = bias + K Q^T and dP^T = V dO^T, then
+//    dS and dQ += dS K (K read transposed from LDS). It also accumulates
+//    d rab in LDS (rab_p by signed diagonal pos_i - j, reduced per wave
+//    through a skewed LDS block and kept in a ring that slides with the key
+//    tiles; rab_t by bucket) and handles a candidate's pair with itself,
+//    including the candidate rows of dK and dV, which no other row sees.
+//  * key-major (dkdv kernel): per tile of 64 non-candidate keys, K and V in
+//    registers, the rows that see them streamed from LDS; S = Q K^T and
+//    dP = dO V^T, then dV += P^T dO and dK += dS^T Q with dO and Q read
+//    transposed from LDS.
 #include "hstu_internal.h"
+#include "../../include/hstu.h"
+#include "device_common.h"
+
+namespace hstu {
+namespace {
+
+using namespace dev;
+
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
+
+template <int NCH>
+struct PairPrefetch {
+  u32x4 a[NCH], b[NCH];
+  float r;
+  long long t;
+};
+
+// ---------------------------------------------------------------------------
+// dQ kernel (query-major): 8 waves x 16 rows (the forward's 128-row query
+// tiles), key tiles of 64.
+//
+// d rab_p: each wave writes its 16 x 64 block of dS into a private LDS area
+// with row r shifted left by its position offset s_r (so column c holds the
+// diagonal pos_i - j = pos_w0 - c0 + 15 - c); one column sum per lane then
+// gives the wave's diagonal sums, which go into a per-workgroup ring indexed
+// by the signed diagonal. Cells outside a row's 64 written columns stay zero
+// for the whole query tile, because the shifts do not change between key
+// tiles. Diagonals that no later key tile can touch are flushed to global
+// memory after every tile.
+// ---------------------------------------------------------------------------
+template <int D, bool USE_P, bool USE_T>
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int BM = kFwdBM, BN = kFwdBN, NWV = 8;
+  constexpr int KS = D / 32, ND = D / 16;
+  constexpr int ST = D + 8;            // LDS row stride of K and V
+  constexpr int CH = D / 8;
+  constexpr int NT = NWV * 64;
+  constexpr int NCHUNK = BN * CH;
+  constexpr int NCH = (NCHUNK + NT - 1) / NT;
+  constexpr int WIN = BM + BN;         // 191 window entries used
+  constexpr int RING = 512;
+  constexpr int SKW = 80;              // skewed row: 64 keys + 15 shifts (+1 pad)
+  static_assert(BM == 128 && BN == 64 && NCH >= 1, "8 waves x 16 rows, 64 keys");
+  static_assert(BM * ST <= 2 * BN * ST, "output staging reuses the K buffers");
+  __shared__ __attribute__((aligned(16))) u16 Ks[2 * BN * ST];
+  __shared__ __attribute__((aligned(16))) u16 Vs[2 * BN * ST];
+  __shared__ float rabw[USE_P ? 2 * WIN : 1];
+  __shared__ __attribute__((aligned(16))) unsigned tkey[USE_T ? 2 * BN : 4];
+  __shared__ unsigned tkst[4];
+  __shared__ float t2tab[33];
+  __shared__ float ring[USE_P ? RING : 1];
+  __shared__ float skew[USE_P ? NWV * 16 * SKW : 1];
+  __shared__ float hts[USE_T ? 33 : 1];   // per-element path: by ffbh(|dt|) + 1
+  __shared__ float htb[USE_T ? 32 : 1];   // constant blocks: by bucket
+  __shared__ float self_acc;
+  __shared__ int s_bad;
+
+  const int H = a.H;
+  const int r = blockIdx.x / H, h = blockIdx.x % H;
+  if (r >= a.hdr[kHdrNQ]) return;
+  const QTile tile = a.tiles[r];
+  const SeqDesc sd = a.desc[tile.b];
+  const int nk = tile.nk, nf = tile.nf_nrows & 0xffff, nrows = tile.nf_nrows >> 16;
+  const int row0 = tile.row0;
+  const long long ld = (long long)H * D;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const u16 *Q = (const u16 *)a.Q, *K = (const u16 *)a.K, *V = (const u16 *)a.V;
+
+  const int fi0 = sd.q_frame0 + row0;
+  const int fil = fi0 + nrows - 1;
+  const int kv_limit = frame_hi(fil, sd.P, sd.E);
+  const int pos_max = fil < sd.E ? fil : sd.E;
+  const long long t_ref = USE_T ? a.ts[sd.q_base + row0] : 0;
+
+  if (tid == 0) {
+    s_bad = 0;
+    self_acc = 0.f;
+  }
+  if (USE_T && tid < 33) {
+    const int c = tid - 1;
+    const int bkt = c < 0 ? 0 : 31 - c;
+    t2tab[tid] = a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1];
+    hts[tid] = 0.f;
+    if (tid < 32) htb[tid] = 0.f;
+  }
+  if (USE_P) {
+    ring[tid] = 0.f;  // RING == blockDim
+    for (int c = tid; c < NWV * 16 * SKW; c += NT) skew[c] = 0.f;
+  }
+  __syncthreads();
+
+  // This lane's query row (S^T layout): local row w*16 + lr.
+  const int lrow = w * 16 + lr;
+  const bool ok = lrow < nrows;
+  const int crow = ok ? lrow : nrows - 1;
+  const int fi = fi0 + crow;
+  const int hi_r = ok ? frame_hi(fi, sd.P, sd.E) : 0;
+  const int pos_r = fi < sd.E ? fi : sd.E;
+  const int vb = pos_max - pos_r + lg * 4;
+  // position offset of this row inside its wave (0..15): the skew shift
+  const int wrow0 = min(w * 16, nrows - 1);
+  const int pos_w0 = min(fi0 + wrow0, sd.E);
+  const int sh = pos_r - pos_w0;
+  unsigned tq = 0u;
+  bool bad_t = false;
+  if (USE_T) {
+    const long long dq = a.ts[sd.q_base + row0 + crow] - t_ref;
+    bad_t |= dq < -2147483648LL || dq > 2147483647LL;
+    tq = (unsigned)(dq + 2147483648LL);
+  }
+  // dO enters as fp32 and is split into two bf16 terms (hi + lo) so that
+  // dP = dO V^T keeps close to fp32 precision: d rab sums dS over very many
+  // pairs with heavy cancellation, and one bf16 rounding of dO alone would
+  // cost about 1e-2 relative error there.
+  bf16x8 qf[KS], dof[KS], dol[KS];
+  {
+    const long long off = (long long)(sd.q_base + row0 + lrow) * ld + h * D + lg * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      float g[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[e] = 0.f;
+      if (ok) {
+        v = *(const u32x4 *)(Q + off + ks * 32);
+        const float4 g0 = *(const float4 *)(a.dO32 + off + ks * 32);
+        const float4 g1 = *(const float4 *)(a.dO32 + off + ks * 32 + 4);
+        g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+        g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+      }
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+      u32x4 hw, lw;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hw[e] = pack_bf16x2(g[2 * e], g[2 * e + 1]);
+        const float h0 = __uint_as_float(hw[e] << 16), h1 = __uint_as_float(hw[e] & 0xffff0000u);
+        lw[e] = pack_bf16x2(g[2 * e] - h0, g[2 * e + 1] - h1);
+      }
+      dof[ks] = __builtin_bit_cast(bf16x8, hw);
+      dol[ks] = __builtin_bit_cast(bf16x8, lw);
+    }
+  }
+  unsigned qmin = 0, qmax = 0;
+  if (USE_T) {
+    qmin = __builtin_amdgcn_readfirstlane(wave_min_u32(tq));
+    qmax = __builtin_amdgcn_readfirstlane(wave_max_u32(tq));
+  }
+
+  PairPrefetch<NCH> pf;
+  pf.r = 0.f;
+  pf.t = 0;
+  auto load = [&](int t) __attribute__((always_inline)) {
+    const int c0 = t * BN;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int chunk = tid + c * NT;
+      if (NCHUNK % NT != 0 && chunk >= NCHUNK) break;
+      const int row = chunk / CH, col = (chunk % CH) * 8;
+      const int key = min(c0 + row, kv_limit - 1);
+      const long long g = (long long)(sd.kv_base + key) * ld + h * D + col;
+      pf.a[c] = *(const u32x4 *)(K + g);
+      pf.b[c] = *(const u32x4 *)(V + g);
+    }
+    if (USE_P && tid < WIN) pf.r = a.rab_p[pos_bucket(pos_max - c0 - tid, a.n_pos)];
+    if (USE_T && tid < BN) pf.t = a.ts[sd.kv_base + min(c0 + tid, kv_limit - 1)];
+  };
+  auto store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int chunk = tid + c * NT;
+      if (NCHUNK % NT != 0 && chunk >= NCHUNK) break;
+      const int row = chunk / CH, col = (chunk % CH) * 8;
+      *(u32x4 *)(Ks + buf * BN * ST + row * ST + col) = pf.a[c];
+      *(u32x4 *)(Vs + buf * BN * ST + row * ST + col) = pf.b[c];
+    }
+    if (USE_P && tid < WIN) rabw[buf * WIN + tid] = pf.r;
+    if (USE_T && tid < BN) {
+      const long long dk = pf.t - t_ref;
+      bad_t |= dk < -2147483648LL || dk > 2147483647LL;
+      const unsigned u = (unsigned)(dk + 2147483648LL);
+      tkey[buf * BN + tid] = u;
+      const unsigned mn = wave_min_u32(u), mx = wave_max_u32(u);
+      if (tid == 0) {
+        tkst[buf * 2] = mn;
+        tkst[buf * 2 + 1] = mx;
+      }
+    }
+  };
+
+  f32x4 acc[ND];
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd) acc[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 st[4], dpt[4];
+  bf16x8 dsa[2];
+
+  auto gemms = [&](int buf) __attribute__((always_inline)) {
+    const u16 *kb = Ks + buf * BN * ST, *vbuf = Vs + buf * BN * ST;
+#pragma unroll
+    for (int mk = 0; mk < 4; ++mk) {
+      if (USE_P) {
+        const float *rw = rabw + buf * WIN + vb + mk * 16;
+        st[mk] = f32x4{rw[0], rw[1], rw[2], rw[3]};
+      } else {
+        st[mk] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      dpt[mk] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mk = 0; mk < 4; ++mk) {
+        const bf16x8 kf = *(const bf16x8 *)(kb + (mk * 16 + lr) * ST + ks * 32 + lg * 8);
+        st[mk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], st[mk], 0, 0, 0);
+        const bf16x8 vf = *(const bf16x8 *)(vbuf + (mk * 16 + lr) * ST + ks * 32 + lg * 8);
+        dpt[mk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, dof[ks], dpt[mk], 0, 0, 0);
+        dpt[mk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, dol[ks], dpt[mk], 0, 0, 0);
+      }
+    }
+  };
+
+  float *skw = skew + w * 16 * SKW;
+  if (nk > 0) {
+    load(0);
+    store(0);
+    if (nk > 1) load(1);
+    __syncthreads();
+    gemms(0);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int b = kt & 1;
+    const int c0 = kt * BN;
+    const bool full = kt < nf;
+    const int hirel = hi_r - (c0 + lg * 4);
+
+    bool tconst = true;
+    float tcv = 0.f;
+    int tcidx = 0;
+    if (USE_T) {
+      const unsigned kmin = __builtin_amdgcn_readfirstlane(tkst[b * 2]);
+      const unsigned kmax = __builtin_amdgcn_readfirstlane(tkst[b * 2 + 1]);
+      unsigned dlo, dhi;
+      if (qmin >= kmax) {
+        dlo = qmin - kmax;
+        dhi = qmax - kmin;
+      } else if (kmin >= qmax) {
+        dlo = kmin - qmax;
+        dhi = kmax - qmin;
+      } else {
+        dlo = 0u;
+        dhi = max(qmax - kmin, kmax - qmin);
+      }
+      const int blo = bucket_u32(dlo, a.n_tb), bhi = bucket_u32(dhi, a.n_tb);
+      tconst = blo == bhi;
+      tcv = a.rab_t[blo];
+      tcidx = blo;
+    }
+    float tsum = 0.f;
+    int run_b = -1;
+    float run_s = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 wds;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int mk = kk * 2 + h2;
+        u32x4 tk4 = {0u, 0u, 0u, 0u};
+        if (USE_T && !tconst) tk4 = *(const u32x4 *)(tkey + b * BN + mk * 16 + lg * 4);
+        float dsv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = st[mk][i];
+          int tix = 0;
+          if (USE_T) {
+            if (tconst) {
+              x += tcv;
+            } else {
+              tix = ffbh_u32(absdiff_u32(tq, tk4[i])) + 1;
+              x += t2tab[tix];
+            }
+          }
+          const float sg = sigmoid_fast(x);
+          float ds = dpt[mk][i] * sg * (1.0f + x * (1.0f - sg));
+          if (!full && !(hirel > mk * 16 + i)) ds = 0.f;
+          dsv[i] = ds;
+          if (USE_P) skw[lr * SKW + mk * 16 + lg * 4 + i + 15 - sh] = ds;
+          if (USE_T) {
+            if (tconst) {
+              tsum += ds;
+            } else {
+              // keys ascend along (mk, i): merge runs of equal buckets
+              if (tix != run_b) {
+                if (run_b >= 0) atomicAdd(&hts[run_b], run_s);
+                run_b = tix;
+                run_s = 0.f;
+              }
+              run_s += ds;
+            }
+          }
+        }
+        wds[h2 * 2] = pack_bf16x2(dsv[0], dsv[1]);
+        wds[h2 * 2 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+      }
+      dsa[kk] = __builtin_bit_cast(bf16x8, wds);
+    }
+    if (USE_T) {
+      if (tconst) {
+        float s = tsum;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+        if (lane == 0) atomicAdd(&htb[tcidx], s);
+      } else if (run_b >= 0) {
+        atomicAdd(&hts[run_b], run_s);
+      }
+    }
+    if (USE_P) {
+      // column sums of the skewed block = this wave's diagonal sums
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float c1 = 0.f, c2 = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        c1 += skw[rr * SKW + lane];
+        if (lane < 15) c2 += skw[rr * SKW + 64 + lane];
+      }
+      const int tbase = pos_w0 - c0 + 15;  // diagonal of column c is tbase - c
+      if (c1 != 0.f) atomicAdd(&ring[(tbase - lane) & (RING - 1)], c1);
+      if (lane < 15 && c2 != 0.f) atomicAdd(&ring[(tbase - 64 - lane) & (RING - 1)], c2);
+      __builtin_amdgcn_wave_barrier();
+    }
+    // dQ += dS K with K read transposed from its row-major tile.
+    {
+      const u16 *kbuf = Ks + b * BN * ST;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd) {
+          const u16 *p0 = kbuf + (kk * 32 + lg * 4 + (lr >> 2)) * ST + nd * 16 + (lr & 3) * 4;
+          const s16x4 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * ST);
+          const bf16x8 kb = __builtin_bit_cast(
+              bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          acc[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[kk], kb, acc[nd], 0, 0, 0);
+        }
+      }
+    }
+    if (kt + 1 < nk) {
+      store(b ^ 1);
+      if (kt + 2 < nk) load(kt + 2);
+    }
+    __syncthreads();
+    // Diagonals above the next tile's window are complete: flush them.
+    if (USE_P && tid < 64) {
+      const int t = (pos_max - c0) - tid;
+      float *slot = &ring[t & (RING - 1)];
+      const float v = *slot;
+      if (v != 0.f) atomicAdd(a.drab_p + pos_bucket(t, a.n_pos), v * a.inv_nmax);
+      *slot = 0.f;
+    }
+    if (kt + 1 < nk) gemms(b ^ 1);
+  }
+  if (USE_P && nk > 0 && tid < WIN - 64) {
+    // the rest of the last window: diagonals [pos_max - c_last - 190, pos_max - c_last - 64]
+    const int t = (pos_max - (nk - 1) * BN) - 64 - tid;
+    const float v = ring[t & (RING - 1)];
+    if (v != 0.f) atomicAdd(a.drab_p + pos_bucket(t, a.n_pos), v * a.inv_nmax);
+  }
+
+  // A candidate's pair with itself (|pos| and |dt| are 0).
+  const bool any_cand = fil >= sd.E;
+  if (any_cand) {
+    const float bias0 = (USE_P ? a.rab_p[0] : 0.f) + (USE_T ? a.rab_t[0] : 0.f);
+    const bool cand = ok && fi0 + lrow >= sd.E;
+    float qk = 0.f, dov = 0.f;
+    const long long srow = (long long)(sd.self_base + fi0 + lrow - sd.E) * ld + h * D + lg * 8;
+    if (cand) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 kv = *(const u32x4 *)(K + srow + ks * 32);
+        const u32x4 vv = *(const u32x4 *)(V + srow + ks * 32);
+        const u16 *ke = (const u16 *)&kv, *ve = (const u16 *)&vv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          qk += (float)qf[ks][e] * bf2f(ke[e]);
+          dov += ((float)dof[ks][e] + (float)dol[ks][e]) * bf2f(ve[e]);
+        }
+      }
+    }
+    qk += __shfl_xor(qk, 16, 64);
+    qk += __shfl_xor(qk, 32, 64);
+    dov += __shfl_xor(dov, 16, 64);
+    dov += __shfl_xor(dov, 32, 64);
+    const float x = qk + bias0;
+    const float sg = sigmoid_fast(x);
+    const float dss = cand ? dov * sg * (1.0f + x * (1.0f - sg)) : 0.f;  // unscaled
+    const float as = cand ? x * sg : 0.f;
+    if (cand) {
+      // dK_i = dS_ii q_i / N_max and dV_i = a_ii dO_i / N_max (rows no other row sees)
+      u16 *dK = (u16 *)a.dK, *dV = (u16 *)a.dV;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 wk, wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wk[e] = pack_bf16x2((float)qf[ks][2 * e] * dss * a.inv_nmax,
+                              (float)qf[ks][2 * e + 1] * dss * a.inv_nmax);
+          wv[e] = pack_bf16x2(((float)dof[ks][2 * e] + (float)dol[ks][2 * e]) * as * a.inv_nmax,
+                              ((float)dof[ks][2 * e + 1] + (float)dol[ks][2 * e + 1]) * as * a.inv_nmax);
+        }
+        *(u32x4 *)(dK + srow + ks * 32) = wk;
+        *(u32x4 *)(dV + srow + ks * 32) = wv;
+      }
+      if (lg == 0) atomicAdd(&self_acc, dss);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float dv = __shfl(dss, lg * 4 + i, 64);
+      const int orow = w * 16 + lg * 4 + i;
+      if (orow < nrows && fi0 + orow >= sd.E) {
+        const u16 *kp = K + (long long)(sd.self_base + fi0 + orow - sd.E) * ld + h * D + lr;
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd) acc[nd][i] += dv * bf2f(kp[nd * 16]);
+      }
+    }
+  }
+  if (USE_T && bad_t) atomicOr(&s_bad, 1);
+  __syncthreads();
+  if (tid == 0 && any_cand) {
+    if (USE_P) atomicAdd(a.drab_p, self_acc * a.inv_nmax);
+    if (USE_T) atomicAdd(a.drab_t, self_acc * a.inv_nmax);
+  }
+  if (USE_T && tid < 33) {
+    const float v = hts[tid];
+    if (v != 0.f) {
+      const int c = tid - 1;
+      const int bkt = c < 0 ? 0 : 31 - c;
+      atomicAdd(a.drab_t + (bkt < a.n_tb - 1 ? bkt : a.n_tb - 1), v * a.inv_nmax);
+    }
+    if (tid < 32 && htb[tid] != 0.f) atomicAdd(a.drab_t + tid, htb[tid] * a.inv_nmax);
+  }
+  // Stage dQ through LDS for 16-byte row stores.
+  u16 *os = Ks;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int orow = w * 16 + lg * 4 + i;
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) {
+      const __bf16 v = (__bf16)(acc[nd][i] * a.inv_nmax);
+      os[orow * ST + nd * 16 + lr] = __builtin_bit_cast(u16, v);
+    }
+  }
+  __syncthreads();
+  u16 *dQ = (u16 *)a.dQ;
+  for (int c = tid; c < BM * CH; c += NT) {
+    const int row = c / CH, col = (c % CH) * 8;
+    if (row < nrows)
+      *(u32x4 *)(dQ + (long long)(sd.q_base + row0 + row) * ld + h * D + col) =
+          *(const u32x4 *)(os + row * ST + col);
+  }
+  if (USE_T && tid == 0 && s_bad) atomicOr(&a.hdr[kHdrStatus], HSTU_DEV_BAD_TIMESTAMPS);
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV kernel (key-major): 4 waves x 16 keys, query steps of 64 rows.
+// ---------------------------------------------------------------------------
+template <int D, bool USE_P, bool USE_T>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int BN = kBwdKBN, BM = kBwdKBM;
+  constexpr int KS = D / 32, ND = D / 16;
+  constexpr int ST = D + 8;            // LDS row stride of the Q and dO tiles
+  constexpr int CH = D / 8;
+  constexpr int NCH = BM * CH / 256;
+  constexpr int WIN = BM + BN;
+  static_assert(BN == 64 && BM == 64, "4 waves x 16 keys, 64 rows");
+  __shared__ __attribute__((aligned(16))) u16 Qs[2 * BM * ST];
+  __shared__ __attribute__((aligned(16))) u16 Os[2 * BM * ST];
+  __shared__ float rabw[USE_P ? 2 * WIN : 1];
+  __shared__ __attribute__((aligned(16))) unsigned trow[USE_T ? 2 * BM : 4];
+  __shared__ unsigned trst[4];
+  __shared__ float t2tab[33];
+
+  const int H = a.H;
+  const int r = blockIdx.x / H, h = blockIdx.x % H;
+  if (r >= a.hdr[kHdrNQ]) return;
+  const QTile tile = a.tiles[r];
+  const SeqDesc sd = a.desc[tile.b];
+  const int k0 = tile.row0;
+  const int qt_lo = tile.nf_nrows & 0xffff, nkeys = tile.nf_nrows >> 16;
+  const int nq = tile.nk;
+  const int L = sd.qcount;
+  const long long ld = (long long)H * D;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const u16 *Q = (const u16 *)a.Q, *K = (const u16 *)a.K, *V = (const u16 *)a.V;
+  const u16 *dO = (const u16 *)a.dO;
+
+  if (USE_T && tid < 33) {
+    const int c = tid - 1;
+    const int bkt = c < 0 ? 0 : 31 - c;
+    t2tab[tid] = a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1];
+  }
+
+  // This lane's key (B-operand and C-column layout): k0 + w*16 + lr.
+  const int lkey = w * 16 + lr;
+  const bool kok = lkey < nkeys;
+  const int key = k0 + (kok ? lkey : nkeys - 1);
+  const int rmin = kok ? (key < sd.P ? 0 : key) : 0x7fffffff;  // first row that sees the key
+  const int kmax_valid = k0 + nkeys - 1;
+  const int rmin_tile = kmax_valid < sd.P ? 0 : kmax_valid;      // rows >= it see every key
+  const long long t_ref = USE_T ? a.ts[sd.kv_base + k0] : 0;
+  unsigned tk = 0u;
+  if (USE_T) tk = (unsigned)(a.ts[sd.kv_base + key] - t_ref + 2147483648LL);
+  unsigned kmin = 0, kmax = 0;
+  if (USE_T) {
+    kmin = __builtin_amdgcn_readfirstlane(wave_min_u32(tk));
+    kmax = __builtin_amdgcn_readfirstlane(wave_max_u32(tk));
+  }
+  bf16x8 kf[KS], vf[KS];
+  {
+    const long long off = (long long)(sd.kv_base + key) * ld + h * D + lg * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(K + off + ks * 32));
+      vf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(V + off + ks * 32));
+    }
+  }
+
+  PairPrefetch<NCH> pf;
+  pf.r = 0.f;
+  pf.t = 0;
+  // rows [fr0, fr0 + 64) of the frame; rows past the end load as zeros.
+  auto load = [&](int qt) __attribute__((always_inline)) {
+    const int fr0 = qt * BM;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int chunk = tid + c * 256;
+      const int row = chunk / CH, col = (chunk % CH) * 8;
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (fr0 + row < L) {
+        const long long g = (long long)(sd.q_base + fr0 + row) * ld + h * D + col;
+        x = *(const u32x4 *)(Q + g);
+        y = *(const u32x4 *)(dO + g);
+      }
+      pf.a[c] = x;
+      pf.b[c] = y;
+    }
+    if (USE_P && tid < WIN) {
+      // window of t = pos(row) - key: t_lo = pos(fr0) - (k0 + 63)
+      const int p0 = fr0 < sd.E ? fr0 : sd.E;
+      pf.r = a.rab_p[pos_bucket(p0 - (k0 + BN - 1) + tid, a.n_pos)];
+    }
+    if (USE_T && tid < BM) pf.t = a.ts[sd.q_base + min(fr0 + tid, L - 1)];
+  };
+  auto store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int chunk = tid + c * 256;
+      const int row = chunk / CH, col = (chunk % CH) * 8;
+      *(u32x4 *)(Qs + buf * BM * ST + row * ST + col) = pf.a[c];
+      *(u32x4 *)(Os + buf * BM * ST + row * ST + col) = pf.b[c];
+    }
+    if (USE_P && tid < WIN) rabw[buf * WIN + tid] = pf.r;
+    if (USE_T && tid < BM) {
+      const unsigned u = (unsigned)(pf.t - t_ref + 2147483648LL);
+      trow[buf * BM + tid] = u;
+      const unsigned mn = wave_min_u32(u), mx = wave_max_u32(u);
+      if (tid == 0) {
+        trst[buf * 2] = mn;
+        trst[buf * 2 + 1] = mx;
+      }
+    }
+  };
+
+  f32x4 dk[ND], dv[ND];
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd) dk[nd] = dv[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nq > 0) {
+    load(qt_lo);
+    store(0);
+    if (nq > 1) load(qt_lo + 1);
+  }
+  __syncthreads();
+  for (int it = 0; it < nq; ++it) {
+    const int b = it & 1;
+    const int fr0 = (qt_lo + it) * BM;
+    const u16 *qb = Qs + b * BM * ST, *ob = Os + b * BM * ST;
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int mr = 0; mr < 4; ++mr) s[mr] = dp[mr] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (USE_P) {
+      // bias of element (mr, i): rabw[min(A + 16 mr + i, Bc)]
+      const int tlo = (fr0 < sd.E ? fr0 : sd.E) - (k0 + BN - 1);
+      const int A = fr0 + lg * 4 - key - tlo, Bc = sd.E - key - tlo;
+#pragma unroll
+      for (int mr = 0; mr < 4; ++mr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[mr][i] = rabw[b * WIN + min(A + mr * 16 + i, Bc)];
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mr = 0; mr < 4; ++mr) {
+        const bf16x8 qa = *(const bf16x8 *)(qb + (mr * 16 + lr) * ST + ks * 32 + lg * 8);
+        s[mr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[ks], s[mr], 0, 0, 0);
+        const bf16x8 oa = *(const bf16x8 *)(ob + (mr * 16 + lr) * ST + ks * 32 + lg * 8);
+        dp[mr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[ks], dp[mr], 0, 0, 0);
+      }
+    }
+    bool tconst = true;
+    float tcv = 0.f;
+    if (USE_T) {
+      const unsigned rmn = __builtin_amdgcn_readfirstlane(trst[b * 2]);
+      const unsigned rmx = __builtin_amdgcn_readfirstlane(trst[b * 2 + 1]);
+      unsigned dlo, dhi;
+      if (rmn >= kmax) {
+        dlo = rmn - kmax;
+        dhi = rmx - kmin;
+      } else if (kmin >= rmx) {
+        dlo = kmin - rmx;
+        dhi = kmax - rmn;
+      } else {
+        dlo = 0u;
+        dhi = max(rmx - kmin, kmax - rmn);
+      }
+      const int blo = bucket_u32(dlo, a.n_tb), bhi = bucket_u32(dhi, a.n_tb);
+      tconst = blo == bhi;
+      tcv = a.rab_t[blo];
+    }
+    const bool full = fr0 >= rmin_tile;
+    const int rrel = rmin - (fr0 + lg * 4);  // element (mr, i) visible iff 16 mr + i >= rrel
+    bf16x8 pa[2], da[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 wp, wd;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int mr = kk * 2 + h2;
+        u32x4 tr4 = {0u, 0u, 0u, 0u};
+        if (USE_T && !tconst) tr4 = *(const u32x4 *)(trow + b * BM + mr * 16 + lg * 4);
+        float pv[4], dv4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = s[mr][i];
+          if (USE_T) x += tconst ? tcv : t2tab[ffbh_u32(absdiff_u32(tr4[i], tk)) + 1];
+          const float sg = sigmoid_fast(x);
+          float p = x * sg;
+          float d = dp[mr][i] * sg * (1.0f + x * (1.0f - sg));
+          if (!full && !(mr * 16 + i >= rrel)) {
+            p = 0.f;
+            d = 0.f;
+          }
+          pv[i] = p;
+          dv4[i] = d;
+        }
+        wp[h2 * 2] = pack_bf16x2(pv[0], pv[1]);
+        wp[h2 * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
+        wd[h2 * 2] = pack_bf16x2(dv4[0], dv4[1]);
+        wd[h2 * 2 + 1] = pack_bf16x2(dv4[2], dv4[3]);
+      }
+      pa[kk] = __builtin_bit_cast(bf16x8, wp);
+      da[kk] = __builtin_bit_cast(bf16x8, wd);
+    }
+    // dV += P^T dO and dK += dS^T Q with dO and Q read transposed.
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        const int off = (kk * 32 + lg * 4 + (lr >> 2)) * ST + nd * 16 + (lr & 3) * 4;
+        const s16x4 o0 = lds_read_tr16(ob + off), o1 = lds_read_tr16(ob + off + 16 * ST);
+        const s16x4 q0 = lds_read_tr16(qb + off), q1 = lds_read_tr16(qb + off + 16 * ST);
+        const bf16x8 ot = __builtin_bit_cast(bf16x8, s16x8{o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]});
+        const bf16x8 qt = __builtin_bit_cast(bf16x8, s16x8{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]});
+        dv[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[kk], ot, dv[nd], 0, 0, 0);
+        dk[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[kk], qt, dk[nd], 0, 0, 0);
+      }
+    }
+    if (it + 1 < nq) {
+      store(b ^ 1);
+      if (it + 2 < nq) load(qt_lo + it + 2);
+    }
+    __syncthreads();
+  }
+
+  // Stage dK and dV (C layout: key 4 lg + i, column 16 nd + lr) through LDS.
+  u16 *sk = Qs, *sv = Os;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kr = w * 16 + lg * 4 + i;
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) {
+      sk[kr * ST + nd * 16 + lr] = __builtin_bit_cast(u16, (__bf16)(dk[nd][i] * a.inv_nmax));
+      sv[kr * ST + nd * 16 + lr] = __builtin_bit_cast(u16, (__bf16)(dv[nd][i] * a.inv_nmax));
+    }
+  }
+  __syncthreads();
+  u16 *dK = (u16 *)a.dK, *dV = (u16 *)a.dV;
+  for (int c = tid; c < BN * CH; c += 256) {
+    const int row = c / CH, col = (c % CH) * 8;
+    if (row < nkeys) {
+      const long long g = (long long)(sd.kv_base + k0 + row) * ld + h * D + col;
+      *(u32x4 *)(dK + g) = *(const u32x4 *)(sk + row * ST + col);
+      *(u32x4 *)(dV + g) = *(const u32x4 *)(sv + row * ST + col);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernels (vector ALU): 4 threads per row (dQ) or per key (dK/dV).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a) {
+  constexpr int BN = 64, DP = D / 4;
+  __shared__ float Ks[BN][D];
+  __shared__ float Vs[BN][D];
+  __shared__ long long tsk[BN];
+  const int H = a.H;
+  const int r = blockIdx.x / H, h = blockIdx.x % H;
+  if (r >= a.hdr[kHdrNQ]) return;
+  const QTile tile = a.tiles[r];
+  const SeqDesc sd = a.desc[tile.b];
+  const int nk = tile.nk, nrows = tile.nf_nrows >> 16, row0 = tile.row0;
+  const long long ld = (long long)H * D;
+  const int tid = threadIdx.x, lrow = tid >> 2, part = tid & 3;
+  const float *Q = (const float *)a.Q, *K = (const float *)a.K, *V = (const float *)a.V;
+  const float *dO = (const float *)a.dO;
+  const bool use_p = a.rab_p != nullptr, use_t = a.rab_t != nullptr;
+  const bool ok = lrow < nrows;
+  const int fi = sd.q_frame0 + row0 + lrow;
+  const int hi = ok ? frame_hi(fi, sd.P, sd.E) : 0;
+  const int pos = fi < sd.E ? fi : sd.E;
+  const long long tq = (use_t && ok) ? a.ts[sd.q_base + row0 + lrow] : 0;
+  const long long roff = (long long)(sd.q_base + row0 + lrow) * ld + h * D + part * DP;
+  float q[DP], g[DP], dq[DP];
+#pragma unroll
+  for (int c = 0; c < DP; ++c) {
+    q[c] = ok ? Q[roff + c] : 0.f;
+    g[c] = ok ? dO[roff + c] : 0.f;
+    dq[c] = 0.f;
+  }
+  const int kv_limit = frame_hi(sd.q_frame0 + row0 + nrows - 1, sd.P, sd.E);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int c0 = kt * BN;
+    __syncthreads();
+    for (int c = tid; c < BN * D; c += 256) {
+      const int row = c / D, col = c % D;
+      const bool in = c0 + row < kv_limit;
+      const long long gi = (long long)(sd.kv_base + c0 + row) * ld + h * D + col;
+      Ks[row][col] = in ? K[gi] : 0.f;
+      Vs[row][col] = in ? V[gi] : 0.f;
+    }
+    if (tid < BN) tsk[tid] = (use_t && c0 + tid < kv_limit) ? a.ts[sd.kv_base + c0 + tid] : 0;
+    __syncthreads();
+    const int jend = min(BN, kv_limit - c0);
+    for (int jl = 0; jl < jend; ++jl) {
+      const int j = c0 + jl;
+      float s = 0.f, da = 0.f;
+#pragma unroll
+      for (int c = 0; c < DP; ++c) {
+        s = fmaf(q[c], Ks[jl][part * DP + c], s);
+        da = fmaf(g[c], Vs[jl][part * DP + c], da);
+      }
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      da += __shfl_xor(da, 1, 64);
+      da += __shfl_xor(da, 2, 64);
+      int pidx = 0, tidx = 0;
+      if (use_p) {
+        pidx = pos_bucket(pos - j, a.n_pos);
+        s += a.rab_p[pidx];
+      }
+      if (use_t) {
+        tidx = time_bucket(tq - tsk[jl], a.n_tb);
+        s += a.rab_t[tidx];
+      }
+      if (j < hi) {
+        const float sg = 1.0f / (1.0f + expf(-s));
+        const float ds = da * sg * (1.0f + s * (1.0f - sg));
+#pragma unroll
+        for (int c = 0; c < DP; ++c) dq[c] = fmaf(ds, Ks[jl][part * DP + c], dq[c]);
+        if (part == 0) {
+          if (use_p) atomicAdd(a.drab_p + pidx, ds * a.inv_nmax);
+          if (use_t) atomicAdd(a.drab_t + tidx, ds * a.inv_nmax);
+        }
+      }
+    }
+  }
+  if (ok && fi >= sd.E) {
+    const long long srow = (long long)(sd.self_base + fi - sd.E) * ld + h * D + part * DP;
+    float s = 0.f, da = 0.f;
+#pragma unroll
+    for (int c = 0; c < DP; ++c) {
+      s = fmaf(q[c], K[srow + c], s);
+      da = fmaf(g[c], V[srow + c], da);
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    da += __shfl_xor(da, 1, 64);
+    da += __shfl_xor(da, 2, 64);
+    s += (use_p ? a.rab_p[0] : 0.f) + (use_t ? a.rab_t[0] : 0.f);
+    const float sg = 1.0f / (1.0f + expf(-s));
+    const float ds = da * sg * (1.0f + s * (1.0f - sg));
+    float *dK = (float *)a.dK, *dV = (float *)a.dV;
+#pragma unroll
+    for (int c = 0; c < DP; ++c) {
+      dq[c] = fmaf(ds, K[srow + c], dq[c]);
+      dK[srow + c] = ds * q[c] * a.inv_nmax;
+      dV[srow + c] = s * sg * g[c] * a.inv_nmax;
+    }
+    if (part == 0) {
+      if (use_p) atomicAdd(a.drab_p, ds * a.inv_nmax);
+      if (use_t) atomicAdd(a.drab_t, ds * a.inv_nmax);
+    }
+  }
+  if (ok) {
+    float *dQ = (float *)a.dQ;
+#pragma unroll
+    for (int c = 0; c < DP; ++c) dQ[roff + c] = dq[c] * a.inv_nmax;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a) {
+  constexpr int BM = 64, DP = D / 4;
+  __shared__ float Qs[BM][D];
+  __shared__ float Gs[BM][D];
+  __shared__ long long tsr[BM];
+  const int H = a.H;
+  const int r = blockIdx.x / H, h = blockIdx.x % H;
+  if (r >= a.hdr[kHdrNQ]) return;
+  const QTile tile = a.tiles[r];
+  const SeqDesc sd = a.desc[tile.b];
+  const int k0 = tile.row0, qt_lo = tile.nf_nrows & 0xffff, nkeys = tile.nf_nrows >> 16;
+  const int nq = tile.nk, L = sd.qcount;
+  const long long ld = (long long)H * D;
+  const int tid = threadIdx.x, lkey = tid >> 2, part = tid & 3;
+  const float *Q = (const float *)a.Q, *K = (const float *)a.K, *V = (const float *)a.V;
+  const float *dO = (const float *)a.dO;
+  const bool use_p = a.rab_p != nullptr, use_t = a.rab_t != nullptr;
+  const bool kok = lkey < nkeys;
+  const int key = k0 + (kok ? lkey : 0);
+  const int rmin = kok ? (key < sd.P ? 0 : key) : 0x7fffffff;
+  const long long koff = (long long)(sd.kv_base + key) * ld + h * D + part * DP;
+  const long long tk = use_t ? a.ts[sd.kv_base + key] : 0;
+  float k[DP], v[DP], dk[DP], dv[DP];
+#pragma unroll
+  for (int c = 0; c < DP; ++c) {
+    k[c] = K[koff + c];
+    v[c] = V[koff + c];
+    dk[c] = dv[c] = 0.f;
+  }
+  for (int it = 0; it < nq; ++it) {
+    const int fr0 = (qt_lo + it) * BM;
+    __syncthreads();
+    for (int c = tid; c < BM * D; c += 256) {
+      const int row = c / D, col = c % D;
+      const bool in = fr0 + row < L;
+      const long long gi = (long long)(sd.q_base + fr0 + row) * ld + h * D + col;
+      Qs[row][col] = in ? Q[gi] : 0.f;
+      Gs[row][col] = in ? dO[gi] : 0.f;
+    }
+    if (tid < BM) tsr[tid] = (use_t && fr0 + tid < L) ? a.ts[sd.q_base + fr0 + tid] : 0;
+    __syncthreads();
+    const int rend = min(BM, L - fr0);
+    for (int rl = 0; rl < rend; ++rl) {
+      const int i = fr0 + rl;
+      float s = 0.f, da = 0.f;
+#pragma unroll
+      for (int c = 0; c < DP; ++c) {
+        s = fmaf(Qs[rl][part * DP + c], k[c], s);
+        da = fmaf(Gs[rl][part * DP + c], v[c], da);
+      }
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      da += __shfl_xor(da, 1, 64);
+      da += __shfl_xor(da, 2, 64);
+      if (use_p) s += a.rab_p[pos_bucket((i < sd.E ? i : sd.E) - key, a.n_pos)];
+      if (use_t) s += a.rab_t[time_bucket(tsr[rl] - tk, a.n_tb)];
+      if (i >= rmin) {
+        const float sg = 1.0f / (1.0f + expf(-s));
+        const float p = s * sg;
+        const float ds = da * sg * (1.0f + s * (1.0f - sg));
+#pragma unroll
+        for (int c = 0; c < DP; ++c) {
+          dv[c] = fmaf(p, Gs[rl][part * DP + c], dv[c]);
+          dk[c] = fmaf(ds, Qs[rl][part * DP + c], dk[c]);
+        }
+      }
+    }
+  }
+  if (kok) {
+    float *dK = (float *)a.dK, *dV = (float *)a.dV;
+#pragma unroll
+    for (int c = 0; c < DP; ++c) {
+      dK[koff + c] = dk[c] * a.inv_nmax;
+      dV[koff + c] = dv[c] * a.inv_nmax;
+    }
+  }
+}
+
+}  // namespace
+
+#define HSTU_BWD_BF16_LAUNCH(KERNEL, NTHR)                                                      \
+  template <int D>                                                                              \
+  hipError_t launch_##KERNEL##_d(const BwdArgs &a, hipStream_t s) {                             \
+    const bool p = a.rab_p != nullptr, t = a.rab_t != nullptr;                                  \
+    if (p && t) hipLaunchKernelGGL((KERNEL<D, true, true>), dim3(a.units), dim3(NTHR), 0, s, a); \
+    else if (p) hipLaunchKernelGGL((KERNEL<D, true, false>), dim3(a.units), dim3(NTHR), 0, s, a); \
+    else if (t) hipLaunchKernelGGL((KERNEL<D, false, true>), dim3(a.units), dim3(NTHR), 0, s, a); \
+    else hipLaunchKernelGGL((KERNEL<D, false, false>), dim3(a.units), dim3(NTHR), 0, s, a);     \
+    return hipGetLastError();                                                                   \
+  }
+
+HSTU_BWD_BF16_LAUNCH(bwd_dq_kernel, 512)
+HSTU_BWD_BF16_LAUNCH(bwd_dkdv_kernel, 256)
+
+hipError_t launch_attn_bwd_dq_bf16(const BwdArgs &a, hipStream_t s) {
+  if (a.units <= 0) return hipSuccess;
+  switch (a.d) {
+    case 32: return launch_bwd_dq_kernel_d<32>(a, s);
+    case 64: return launch_bwd_dq_kernel_d<64>(a, s);
+    case 128: return launch_bwd_dq_kernel_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs &a, hipStream_t s) {
+  if (a.units <= 0) return hipSuccess;
+  switch (a.d) {
+    case 32: return launch_bwd_dkdv_kernel_d<32>(a, s);
+    case 64: return launch_bwd_dkdv_kernel_d<64>(a, s);
+    case 128: return launch_bwd_dkdv_kernel_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attn_bwd_dq_f32(const BwdArgs &a, hipStream_t s) {
+  if (a.units <= 0) return hipSuccess;
+  switch (a.d) {
+    case 32: hipLaunchKernelGGL(bwd_dq_f32_kernel<32>, dim3(a.units), dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, dim3(a.units), dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, dim3(a.units), dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dkdv_f32(const BwdArgs &a, hipStream_t s) {
+  if (a.units <= 0) return hipSuccess;
+  switch (a.d) {
+    case 32: hipLaunchKernelGGL(bwd_dkdv_f32_kernel<32>, dim3(a.units), dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL(bwd_dkdv_f32_kernel<64>, dim3(a.units), dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(bwd_dkdv_f32_kernel<128>, dim3(a.units), dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hstu

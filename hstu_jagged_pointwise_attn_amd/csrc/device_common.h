@@ -1,0 +1,90 @@
+// Device helpers shared by the attention kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hstu {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16;
+typedef unsigned int u32;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf2f(u16 x) { return __uint_as_float((u32)x << 16); }
+
+__device__ __forceinline__ int frame_hi(int i, int P, int E) {
+  return i < P ? P : (i < E ? i + 1 : E);
+}
+
+// SiLU(x) = x * sigmoid(x) with the hardware exp2 and reciprocal.
+__device__ __forceinline__ float silu_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
+
+// floor(log2(max(1, |dt|))) clamped to n_tb - 1.
+__device__ __forceinline__ int time_bucket(long long dt, int n_tb) {
+  unsigned long long m = dt < 0 ? 0ull - (unsigned long long)dt : (unsigned long long)dt;
+  int b = m <= 1ull ? 0 : 63 - __clzll((long long)m);
+  return b < n_tb - 1 ? b : n_tb - 1;
+}
+
+__device__ __forceinline__ int pos_bucket(int dp, int n_pos) {
+  dp = dp < 0 ? -dp : dp;
+  return dp < n_pos - 1 ? dp : n_pos - 1;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// gfx950 transposing LDS read: within each group of 16 lanes, output lane j,
+// element e is the 16-bit value at (address of source lane 4e + j/4) + j%4.
+__device__ __forceinline__ s16x4 lds_read_tr16(const u16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+}
+
+// |a - b| of two unsigned values (one instruction).
+__device__ __forceinline__ unsigned absdiff_u32(unsigned a, unsigned b) {
+  unsigned d;
+  asm("v_sad_u32 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// Index of the highest set bit counted from the top (0..31), -1 for 0.
+__device__ __forceinline__ int ffbh_u32(unsigned x) {
+  int c;
+  asm("v_ffbh_u32 %0, %1" : "=v"(c) : "v"(x));
+  return c;
+}
+
+__device__ __forceinline__ int bucket_u32(unsigned x, int n_tb) {
+  const int b = x <= 1u ? 0 : 31 - __builtin_clz(x);
+  return b < n_tb - 1 ? b : n_tb - 1;
+}
+
+__device__ __forceinline__ unsigned wave_min_u32(unsigned v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (unsigned)__shfl_xor((int)v, o, 64));
+  return v;
+}
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(u32, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+
+}  // namespace dev
+}  // namespace hstu

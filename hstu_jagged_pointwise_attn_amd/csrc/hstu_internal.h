@@ -40,7 +40,7 @@ constexpr int kSortCap = 8192;   // longest-first order up to this many query ti
 constexpr int kMaxSeqs = 8192;   // sequences per call (query-tile offsets live in LDS)
 constexpr int kMaxKeyTiles = 16383;
 
-enum SchedMode { kSchedAttn = 0, kSchedMFalcon = 1 };
+enum SchedMode { kSchedAttn = 0, kSchedMFalcon = 1, kSchedKeys = 2 };
 
 struct SchedArgs {
   int mode;
@@ -103,55 +103,46 @@ struct NormArgs {
 hipError_t launch_norm_fwd(const NormArgs &a, bool bf16, hipStream_t s);
 
 struct NormBwdArgs {
-  const void *X, *U, *dY;
-  const float *mean, *rstd;
-  const uint8_t *group;
-  const float *gamma, *beta;
+  const void *X, *U, *dY;         // [T, D] pre-norm output, gate, output gradient
+  const float *mean, *rstd;       // [T]
+  const uint8_t *group;           // [T] or NULL
+  const float *gamma, *beta;      // [G, D] or NULL
   int n_groups, mode;
   long long T;
   int D;
-  void *dU;             // [T, D] dtype
-  void *dX;             // [T, D] dtype (gradient w.r.t. the pre-norm output)
-  float *dgamma_part, *dbeta_part;  // [nblk, G, D] partial sums or NULL
-  int nblk;
+  int tokens_per_wave;            // contiguous tokens handled by one wave
+  void *dU;                       // [T, D]
+  void *dX;                       // [T, D] gradient w.r.t. the pre-norm output
+  float *dX32;                    // [T, D] the same in fp32, or NULL
+  float *dgamma, *dbeta;          // [G, D] accumulated with atomics (zeroed by the caller), or NULL
 };
 hipError_t launch_norm_bwd(const NormBwdArgs &a, bool bf16, hipStream_t s);
-hipError_t launch_reduce_rows(const float *part, int nrows, long long width, float *out,
-                              hipStream_t s);
 
-// Backward attention kernels.
+// Backward attention kernels. dO is the gradient w.r.t. the pre-norm output
+// (computed by the norm backward into the workspace).
 struct BwdArgs {
-  const void *Q, *K, *V, *dO;     // dO = gradient w.r.t. the pre-norm output
+  const void *Q, *K, *V, *dO;
+  const float *dO32;               // fp32 dO (bf16 path: split into two bf16 terms for dP)
   void *dQ, *dK, *dV;
-  float *dQacc;                   // fp32 [T, H*d] accumulator (bf16 path) or NULL
-  const int64_t *ts;
-  const float *rab_p, *rab_t;
-  float *drab_p, *drab_t;         // fp32 accumulators (zeroed by the caller)
+  const int64_t *ts;               // timestamps or NULL
+  const float *rab_p, *rab_t;      // tables or NULL
+  float *drab_p, *drab_t;          // fp32 accumulators (zeroed by the caller)
   int n_pos, n_tb;
   float inv_nmax;
   int H, d;
-  const int *hdr;
+  int *hdr;                        // header of the schedule this kernel runs
   const SeqDesc *desc;
-  const QTile *tiles;             // key tiles in the same record format (rows = keys)
-  int units;
+  const QTile *tiles;
+  int units;                       // grid bound: records * H
 };
-constexpr int kBwdBM = 64, kBwdBN = 64;   // bf16 backward: key tile BN rows, query tiles of BM
-hipError_t launch_attn_bwd_bf16(const BwdArgs &a, hipStream_t s);
-hipError_t launch_attn_bwd_f32(const BwdArgs &a, hipStream_t s);
-
-// Key-major work list for the backward: one record per key tile.
-struct KSchedArgs {
-  const int *offsets, *prefix, *cand;
-  int B;
-  long long T;
-  int max_len;
-  int BM, BN;
-  int *hdr;
-  SeqDesc *desc;
-  QTile *ktiles;   // {b, key0, q-tile range begin (frame row tile), nrows | qt_end << 16}
-};
+// bf16: the query-major dQ kernel runs the forward's query tiles (kFwdBM x
+// kFwdBN); the key-major dK/dV kernel runs 64-key tiles x 64-row query steps.
+constexpr int kBwdKBN = 64, kBwdKBM = 64;
+hipError_t launch_attn_bwd_dq_bf16(const BwdArgs &a, hipStream_t s);
+hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs &a, hipStream_t s);
+hipError_t launch_attn_bwd_dq_f32(const BwdArgs &a, hipStream_t s);
+hipError_t launch_attn_bwd_dkdv_f32(const BwdArgs &a, hipStream_t s);
 
 hipError_t launch_fill_f32(float *p, long long n, float v, hipStream_t s);
-hipError_t launch_cast_f32_to_bf16(const float *src, void *dst, long long n, hipStream_t s);
 
 }  // namespace hstu

@@ -58,6 +58,12 @@ struct Vec<false> {
   __device__ static void store(void *p, long long off, const float *x) {
     *(float4 *)((float *)p + off) = float4{x[0], x[1], x[2], x[3]};
   }
+  // n consecutive fp32 values (n a multiple of 4)
+  template <int n>
+  __device__ static void store4n(float *p, long long off, const float *x) {
+#pragma unroll
+    for (int e = 0; e < n; e += 4) *(float4 *)(p + off + e) = float4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+  }
 };
 
 template <bool BF16, int MAXCH>
@@ -145,11 +151,172 @@ hipError_t norm_fwd_dispatch(const NormArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Backward of Y = Norm(X) * U for one token per wave:
+//   dU = n * dY, dN = dY * u,
+//   LN/GLN: xhat = (x - mean) * rstd, g = dN * gamma,
+//           dX = rstd * (g - mean(g) - xhat * mean(g * xhat)),
+//           dgamma += dN * xhat, dbeta += dN   (row of the token's group)
+//   NONE:   dX = dN.
+// Each wave walks a contiguous run of tokens and keeps the affine gradients
+// of the current group in registers, flushing them with atomics only when
+// the group changes and at the end of its run.
+template <bool BF16, int MAXCH>
+__global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
+  using V = Vec<BF16>;
+  constexpr int N = V::N;
+  const int lane = threadIdx.x & 63;
+  const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long t0 = wave * a.tokens_per_wave;
+  if (t0 >= a.T) return;
+  const long long t1 = min(a.T, t0 + a.tokens_per_wave);
+  const int D = a.D, nch = D / N;
+  const bool affine = a.mode != HSTU_NORM_NONE && (a.dgamma || a.dbeta);
+  float dg[MAXCH][N], db[MAXCH][N];
+#pragma unroll
+  for (int k = 0; k < MAXCH; ++k)
+#pragma unroll
+    for (int e = 0; e < N; ++e) dg[k][e] = db[k][e] = 0.f;
+  int gcur = -1;
+  auto flush = [&](int g) __attribute__((always_inline)) {
+    if (g < 0) return;
+#pragma unroll
+    for (int k = 0; k < MAXCH; ++k) {
+      const int ch = lane + 64 * k;
+      if (ch < nch) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          const long long c = (long long)g * D + ch * N + e;
+          if (a.dgamma) atomicAdd(a.dgamma + c, dg[k][e]);
+          if (a.dbeta) atomicAdd(a.dbeta + c, db[k][e]);
+          dg[k][e] = db[k][e] = 0.f;
+        }
+      }
+    }
+  };
+  for (long long t = t0; t < t1; ++t) {
+    const long long row = t * D;
+    float x[MAXCH][N], dy[MAXCH][N], u[MAXCH][N];
+#pragma unroll
+    for (int k = 0; k < MAXCH; ++k) {
+      const int ch = lane + 64 * k;
+      if (ch < nch) {
+        V::load(a.X, row + ch * N, x[k]);
+        V::load(a.dY, row + ch * N, dy[k]);
+        V::load(a.U, row + ch * N, u[k]);
+      }
+    }
+    if (a.mode == HSTU_NORM_NONE) {
+#pragma unroll
+      for (int k = 0; k < MAXCH; ++k) {
+        const int ch = lane + 64 * k;
+        if (ch < nch) {
+          float du[N], dx[N];
+#pragma unroll
+          for (int e = 0; e < N; ++e) {
+            du[e] = x[k][e] * dy[k][e];
+            dx[e] = dy[k][e] * u[k][e];
+          }
+          V::store(a.dU, row + ch * N, du);
+          V::store(a.dX, row + ch * N, dx);
+          if (a.dX32) Vec<false>::store4n<N>(a.dX32, row + ch * N, dx);
+        }
+      }
+      continue;
+    }
+    const float mean = a.mean[t], rstd = a.rstd[t];
+    int g = 0;
+    if (a.mode == HSTU_NORM_GLN) {
+      g = a.group[t];
+      if (g >= a.n_groups) g = -1;
+    }
+    const float *gm = (g >= 0 && a.gamma) ? a.gamma + (long long)g * D : nullptr;
+    const float *bt = (g >= 0 && a.beta) ? a.beta + (long long)g * D : nullptr;
+    if (affine && g != gcur) {
+      flush(gcur);
+      gcur = g;
+    }
+    float s1 = 0.f, s2 = 0.f;
+    float xh[MAXCH][N], gh[MAXCH][N];
+#pragma unroll
+    for (int k = 0; k < MAXCH; ++k) {
+      const int ch = lane + 64 * k;
+      if (ch < nch) {
+        float du[N];
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          const int c = ch * N + e;
+          xh[k][e] = (x[k][e] - mean) * rstd;
+          const float gam = gm ? gm[c] : 1.f;
+          const float n = xh[k][e] * gam + (bt ? bt[c] : 0.f);
+          du[e] = n * dy[k][e];
+          const float dn = dy[k][e] * u[k][e];
+          if (affine && g >= 0) {
+            dg[k][e] += dn * xh[k][e];
+            db[k][e] += dn;
+          }
+          gh[k][e] = dn * gam;
+          s1 += gh[k][e];
+          s2 += gh[k][e] * xh[k][e];
+        }
+        V::store(a.dU, row + ch * N, du);
+      }
+    }
+    const float m1 = wave_sum(s1) / (float)D, m2 = wave_sum(s2) / (float)D;
+#pragma unroll
+    for (int k = 0; k < MAXCH; ++k) {
+      const int ch = lane + 64 * k;
+      if (ch < nch) {
+        float dx[N];
+#pragma unroll
+        for (int e = 0; e < N; ++e) dx[e] = rstd * (gh[k][e] - m1 - xh[k][e] * m2);
+        V::store(a.dX, row + ch * N, dx);
+        if (a.dX32) Vec<false>::store4n<N>(a.dX32, row + ch * N, dx);
+      }
+    }
+  }
+  if (affine) flush(gcur);
+}
+
+template <bool BF16>
+hipError_t norm_bwd_dispatch(const NormBwdArgs &a, hipStream_t s) {
+  const int nch = a.D / Vec<BF16>::N;
+  const long long waves = (a.T + a.tokens_per_wave - 1) / a.tokens_per_wave;
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  if (nch <= 64) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 1>), grid, dim3(256), 0, s, a);
+  else if (nch <= 128) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 2>), grid, dim3(256), 0, s, a);
+  else if (nch <= 256) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 4>), grid, dim3(256), 0, s, a);
+  else if (nch <= 512) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 8>), grid, dim3(256), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+__global__ void fill_f32_kernel(float *p, long long n, float v) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
 }  // namespace
 
 hipError_t launch_norm_fwd(const NormArgs &a, bool bf16, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   return bf16 ? norm_fwd_dispatch<true>(a, s) : norm_fwd_dispatch<false>(a, s);
+}
+
+}  // namespace hstu
+
+namespace hstu {
+
+hipError_t launch_norm_bwd(const NormBwdArgs &a, bool bf16, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  return bf16 ? norm_bwd_dispatch<true>(a, s) : norm_bwd_dispatch<false>(a, s);
+}
+
+hipError_t launch_fill_f32(float *p, long long n, float v, hipStream_t s) {
+  if (n <= 0 || !p) return hipSuccess;
+  const long long blocks = min((n + 255) / 256, 4096LL);
+  hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
 }
 
 }  // namespace hstu

@@ -15,6 +15,12 @@
 // Steps: per-sequence validation and query-tile counts -> exclusive scan ->
 // one record per query tile -> longest-first order (bitonic sort in LDS on
 // the unique key (nk descending, canonical index ascending)).
+//
+// Key-major mode (the dK/dV backward): one record per key tile [k0, k0+BN)
+// of the non-candidate keys [0, E) (a candidate key is seen only by itself);
+// the rows that see key j form the suffix i >= (j < P ? 0 : j), so the
+// record lists the query tiles [qt_lo, qt_hi) of BM rows from
+// (k0 < P ? 0 : k0) to the end of the sequence.
 #include "hstu_internal.h"
 #include "../../include/hstu.h"
 
@@ -30,7 +36,7 @@ __device__ __forceinline__ int frame_hi(int i, int P, int E) {
 __device__ SeqDesc seq_info(const SchedArgs &a, int b, int *bits) {
   SeqDesc s{};
   *bits = 0;
-  if (a.mode == kSchedAttn) {
+  if (a.mode != kSchedMFalcon) {
     long long beg = a.offsets[b], end = a.offsets[b + 1];
     int P = a.prefix ? a.prefix[b] : 0;
     int C = a.cand ? a.cand[b] : 0;
@@ -70,9 +76,11 @@ __device__ SeqDesc seq_info(const SchedArgs &a, int b, int *bits) {
 
 __device__ __forceinline__ int div_up(int x, int y) { return (x + y - 1) / y; }
 
-// Number of query tiles of a sequence with `q` query rows.
-__device__ int qtile_count(const SchedArgs &a, int q) {
+// Number of work records (query tiles, or key tiles in key-major mode) of a sequence.
+__device__ int qtile_count(const SchedArgs &a, const SeqDesc &s) {
+  const int q = s.qcount;
   if (q <= 0) return 0;
+  if (a.mode == kSchedKeys) return div_up(s.E, a.BN);
   if (a.mode == kSchedAttn || a.microbatch <= 0 || a.microbatch >= q) return div_up(q, a.BM);
   int bm = a.microbatch, tpm = div_up(bm, a.BM);
   return (q / bm) * tpm + div_up(q % bm, a.BM);
@@ -81,6 +89,18 @@ __device__ int qtile_count(const SchedArgs &a, int q) {
 // Record of the t-th query tile (canonical order) of sequence s.
 __device__ QTile make_tile(const SchedArgs &a, const SeqDesc &s, int b, int t) {
   int row0, nrows;
+  if (a.mode == kSchedKeys) {
+    const int k0 = t * a.BN;
+    const int nkeys = min(a.BN, s.E - k0);
+    const int qt_lo = (k0 < s.P ? 0 : k0) / a.BM;
+    const int qt_hi = div_up(s.qcount, a.BM);
+    QTile r;
+    r.b = b;
+    r.row0 = k0;
+    r.nk = qt_hi - qt_lo;
+    r.nf_nrows = qt_lo | (nkeys << 16);
+    return r;
+  }
   if (a.mode == kSchedAttn || a.microbatch <= 0 || a.microbatch >= s.qcount) {
     row0 = t * a.BM;
     nrows = min(a.BM, s.qcount - row0);
@@ -138,7 +158,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
 
   if (tid == 0) {
     int bits = 0;
-    if (a.mode == kSchedAttn) {
+    if (a.mode != kSchedMFalcon) {
       if (a.offsets[0] != 0 || (long long)a.offsets[a.B] != a.Tq) bits |= HSTU_DEV_BAD_OFFSETS;
     } else {
       if (a.cand_offsets[0] != 0 || (long long)a.cand_offsets[a.B] != a.Tq ||
@@ -162,7 +182,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
         atomicMin(&a.hdr[kHdrFirstBad], b);
       }
       a.desc[b] = s;
-      nq = qtile_count(a, s.qcount);
+      nq = qtile_count(a, s);
     }
     int total;
     int excl = block_exclusive_scan(nq, s_wsum, &total);

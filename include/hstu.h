@@ -246,10 +246,11 @@ enum {
   HSTU_KERNEL_SCHED = 0,     /* tile scheduler */
   HSTU_KERNEL_ATTN_FWD = 1,  /* attention forward (also M-FALCON scoring) */
   HSTU_KERNEL_NORM_FWD = 2,  /* Norm(O) * U */
-  HSTU_KERNEL_NORM_BWD = 3,  /* backward of the norm epilogue */
-  HSTU_KERNEL_ATTN_BWD = 4,  /* attention backward (all its kernels) */
-  HSTU_KERNEL_AUX = 5,       /* fills, casts and reductions */
-  HSTU_KERNEL_COUNT = 6
+  HSTU_KERNEL_NORM_BWD = 3,       /* backward of the norm epilogue */
+  HSTU_KERNEL_ATTN_BWD_DQ = 4,    /* attention backward, query-major pass (dQ, d rab) */
+  HSTU_KERNEL_AUX = 5,            /* fills */
+  HSTU_KERNEL_ATTN_BWD_DKDV = 6,  /* attention backward, key-major pass (dK, dV) */
+  HSTU_KERNEL_COUNT = 7
 };
 hstu_status_t hstu_kernel_timing(int32_t enable);
 hstu_status_t hstu_kernel_timing_read(int32_t kernel, double *total_ms, int64_t *launches);

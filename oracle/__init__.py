@@ -123,7 +123,8 @@ def bwd(offsets, Q, K, V, U, dY, *, H, d, prefix_len=None, cand_len=None, ts=Non
         rab_t=None, n_max=1.0, norm=NORM_LN, eps=1e-5, group=None, n_groups=1, gamma=None,
         beta=None, nthreads=0):
     """Backward pass (recomputes the forward). Returns dict with dQ, dK, dV,
-    dU ([T, H*d]), drab_p, drab_t, dgamma, dbeta (None when not applicable)."""
+    dU ([T, H*d]), drab_p, drab_t, dgamma, dbeta (None when not applicable),
+    and drab_p_abs / drab_t_abs: the sums of |dS| that enter each rab entry."""
     lib = _load()
     offsets = _i32(offsets)
     B = len(offsets) - 1
@@ -138,6 +139,8 @@ def bwd(offsets, Q, K, V, U, dY, *, H, d, prefix_len=None, cand_len=None, ts=Non
     drt = np.zeros(len(rt)) if rt is not None else None
     dgm = np.zeros((G, D)) if gm is not None else None
     dbt = np.zeros((G, D)) if bt is not None else None
+    drpa = np.zeros(len(rp)) if rp is not None else None
+    drta = np.zeros(len(rt)) if rt is not None else None
     pl, cl, ts_, grp = _i32(prefix_len), _i32(cand_len), _i64(ts), _u8(group)
     rc = lib.oracle_bwd(
         ctypes.c_int(B), ctypes.c_int(H), ctypes.c_int(d), _p(offsets), _p(pl), _p(cl),
@@ -146,12 +149,12 @@ def bwd(offsets, Q, K, V, U, dY, *, H, d, prefix_len=None, cand_len=None, ts=Non
         _p(rt), ctypes.c_int(0 if rt is None else len(rt)),
         ctypes.c_double(n_max), ctypes.c_int(norm), ctypes.c_double(eps),
         _p(grp), ctypes.c_int(n_groups), _p(gm), _p(bt), _p(dY),
-        _p(dQ), _p(dK), _p(dV), _p(dU), _p(drp), _p(drt), _p(dgm), _p(dbt),
+        _p(dQ), _p(dK), _p(dV), _p(dU), _p(drp), _p(drt), _p(dgm), _p(dbt), _p(drpa), _p(drta),
         ctypes.c_int(_threads(nthreads)))
     if rc != 0:
         raise ValueError(f"oracle_bwd rejected its input (code {rc})")
     return {"dQ": dQ, "dK": dK, "dV": dV, "dU": dU, "drab_p": drp, "drab_t": drt,
-            "dgamma": dgm, "dbeta": dbt}
+            "dgamma": dgm, "dbeta": dbt, "drab_p_abs": drpa, "drab_t_abs": drta}
 
 
 def mfalcon(hist_offsets, cand_offsets, K_cache, V_cache, Qc, Kc, Vc, Uc, *, H, d, hist_ts=None,

@@ -232,6 +232,8 @@ int oracle_fwd(int B, int H, int d, const int32_t *offsets, const int32_t *prefi
 /*
  * Backward of oracle_fwd with respect to Q, K, V, U, the rab tables and the
  * affine parameters, given dY [T, D]. The forward is recomputed internally.
+ * drab_p_abs / drab_t_abs (or NULL) receive the sums of |dS| that enter each
+ * table entry.
  * Every gradient output is overwritten. dgamma/dbeta ([n_groups, D]) may be
  * NULL; they are only produced when gamma/beta are given. Timestamps have no
  * gradient.
@@ -242,7 +244,8 @@ int oracle_bwd(int B, int H, int d, const int32_t *offsets, const int32_t *prefi
                const double *rab_t, int n_tb, double n_max, int norm, double eps,
                const uint8_t *group, int n_groups, const double *gamma, const double *beta,
                const double *dY, double *dQ, double *dK, double *dV, double *dU,
-               double *drab_p, double *drab_t, double *dgamma, double *dbeta, int nthreads) {
+               double *drab_p, double *drab_t, double *dgamma, double *dbeta,
+               double *drab_p_abs, double *drab_t_abs, int nthreads) {
   int err = check_common(B, H, d, offsets, prefix_len, cand_len);
   if (err) return err;
   const int D = H * d;
@@ -273,6 +276,10 @@ int oracle_bwd(int B, int H, int d, const int32_t *offsets, const int32_t *prefi
   double *pb = (double *)calloc((size_t)nth * G * D + 1, sizeof(double));
   double *pp = (double *)calloc((size_t)nth * (n_pos > 0 ? n_pos : 1), sizeof(double));
   double *pt = (double *)calloc((size_t)nth * (n_tb > 0 ? n_tb : 1), sizeof(double));
+  /* sums of |dS| per table entry: the scale against which the cancelling
+   * sums drab_p / drab_t are measured */
+  double *ppa = (double *)calloc((size_t)nth * (n_pos > 0 ? n_pos : 1), sizeof(double));
+  double *pta = (double *)calloc((size_t)nth * (n_tb > 0 ? n_tb : 1), sizeof(double));
 
   /* Norm backward, per token:
    *   dU = n * dY,  dN = dY * u
@@ -370,8 +377,14 @@ int oracle_bwd(int B, int H, int d, const int32_t *offsets, const int32_t *prefi
             dqi[c] += ds * kj[c];
             dkj[c] += ds * qi[c];
           }
-          if (pidx >= 0) pp[(long)tid * n_pos + pidx] += ds;
-          if (tidx >= 0) pt[(long)tid * n_tb + tidx] += ds;
+          if (pidx >= 0) {
+            pp[(long)tid * n_pos + pidx] += ds;
+            ppa[(long)tid * n_pos + pidx] += fabs(ds);
+          }
+          if (tidx >= 0) {
+            pt[(long)tid * n_tb + tidx] += ds;
+            pta[(long)tid * n_tb + tidx] += fabs(ds);
+          }
         }
       }
     }
@@ -390,6 +403,20 @@ int oracle_bwd(int B, int H, int d, const int32_t *offsets, const int32_t *prefi
       drab_t[p] = s;
     }
   }
+  if (drab_p_abs) {
+    for (int p = 0; p < n_pos; p++) {
+      double s = 0.0;
+      for (int t = 0; t < nth; t++) s += ppa[(long)t * n_pos + p];
+      drab_p_abs[p] = s;
+    }
+  }
+  if (drab_t_abs) {
+    for (int p = 0; p < n_tb; p++) {
+      double s = 0.0;
+      for (int t = 0; t < nth; t++) s += pta[(long)t * n_tb + p];
+      drab_t_abs[p] = s;
+    }
+  }
   if (dgamma && gamma) {
     for (long e = 0; e < (long)G * D; e++) {
       double s = 0.0;
@@ -405,7 +432,7 @@ int oracle_bwd(int B, int H, int d, const int32_t *offsets, const int32_t *prefi
     }
   }
   free(O); free(Yt); free(mean); free(rstd); free(dO);
-  free(pg); free(pb); free(pp); free(pt);
+  free(pg); free(pb); free(pp); free(pt); free(ppa); free(pta);
   return 0;
 }
 

@@ -450,3 +450,25 @@ def test_generators_are_deterministic():
     assert abs(t.lengths.mean() - 776) < 150
     lit = synth.train_bf16(True)
     assert lit.lengths.max() <= 776
+
+
+@pytest.mark.parametrize("p", _grad_problems()[:2], ids=lambda p: p.name)
+def test_rab_gradient_absolute_mass(oracle_mod, p):
+    """drab_*_abs are sums of |dS|: they bound |drab_*| entrywise, both
+    tables see the same total mass (each visible pair hits one entry of
+    each), and with dY = 0 everything is zero."""
+    r = oracle_mod.bwd(p.offsets, p.Q.numpy(), p.K.numpy(), p.V.numpy(), p.U.numpy(), p.dY.numpy(),
+                       **_oracle_opts(p))
+    assert np.all(r["drab_p_abs"] >= np.abs(r["drab_p"]) - 1e-12)
+    assert np.all(r["drab_t_abs"] >= np.abs(r["drab_t"]) - 1e-12)
+    assert r["drab_p_abs"].sum() == pytest.approx(r["drab_t_abs"].sum(), rel=1e-12)
+    # a single visible pair: L = 1, the mass is |dS| of that pair in entry 0
+    q = synth.custom("one", [1], H=1, d=4, dtype=torch.float32, wid=61, std=0.7, n_max=1,
+                     norm=synth.NORM_NONE, n_pos=3, n_tb=3, with_dy=True)
+    o = oracle_mod.bwd(q.offsets, q.Q.numpy(), q.K.numpy(), q.V.numpy(), q.U.numpy(), q.dY.numpy(),
+                       **_oracle_opts(q))
+    assert o["drab_p_abs"][0] == pytest.approx(abs(o["drab_p"][0]), rel=1e-14)
+    assert np.all(o["drab_p_abs"][1:] == 0)
+    z = oracle_mod.bwd(p.offsets, p.Q.numpy(), p.K.numpy(), p.V.numpy(), p.U.numpy(),
+                       np.zeros_like(p.dY.numpy()), **_oracle_opts(p))
+    assert np.all(z["drab_p_abs"] == 0) and np.all(z["drab_t_abs"] == 0)
