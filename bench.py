@@ -154,6 +154,9 @@ def main():
     ap.add_argument("--workload", default="train", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB 3 times (calibrates the HBM "
+                         "byte counters of a profiler run against a transfer of known size)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -261,6 +264,17 @@ def main():
                 "unit": "TFLOP/s", "frac": (achieved / peak) if achieved else None,
                 "traffic": traffic_from_profiles(wl, dom_name), "kernel": dom_name,
                 "kernel_ms": dom_ms, "per_kernel_ms": per}
+
+    if args.copy_probe_mb > 0:
+        n = args.copy_probe_mb << 20
+        src_buf = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst_buf = torch.empty_like(src_buf)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 3 x {n} bytes")
+        del src_buf, dst_buf
 
     cpu = None
     if not args.no_cpu_baseline:
