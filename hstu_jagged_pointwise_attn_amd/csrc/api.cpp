@@ -97,7 +97,7 @@ struct Layout {
   size_t hdr, desc, qoff, tiles, total;
   long long max_tiles;
   // backward only: key-major schedule and the gradient of the pre-norm output
-  size_t khdr, kdesc, kqoff, ktiles, dO, dO32;
+  size_t khdr, kdesc, kqoff, ktiles, dO;
   long long max_ktiles;
 };
 
@@ -127,8 +127,6 @@ Layout layout(const hstu_problem_t *p, int op, int microbatch, int hist_max_len)
     L.ktiles = off; off += align256(sizeof(QTile) * (size_t)(nk > 0 ? nk : 1));
     const size_t esz = p->dtype == HSTU_BF16 ? 2 : 4;
     L.dO = off;     off += align256(esz * (size_t)p->total_tokens * p->H * p->d + 16);
-    L.dO32 = off;
-    if (p->dtype == HSTU_BF16) off += align256(4 * (size_t)p->total_tokens * p->H * p->d + 16);
   }
   L.total = off;
   return L;
@@ -427,7 +425,6 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
     n.D = D;
     n.tokens_per_wave = 32;
     n.dU = dU; n.dX = dO;
-    n.dX32 = bf16 ? at<float>(ws, L.dO32) : nullptr;
     n.dgamma = dg; n.dbeta = db;
     Timed t_(HSTU_KERNEL_NORM_BWD, st);
     HIP_TRY(launch_norm_bwd(n, bf16, st), "norm backward launch");
@@ -435,7 +432,6 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
   BwdArgs b;
   std::memset(&b, 0, sizeof b);
   b.Q = Q; b.K = K; b.V = V; b.dO = dO;
-  b.dO32 = bf16 ? at<float>(ws, L.dO32) : (const float *)dO;
   b.dQ = dQ; b.dK = dK; b.dV = dV;
   b.ts = use_t ? p->timestamps : nullptr;
   b.rab_p = p->rab_p;

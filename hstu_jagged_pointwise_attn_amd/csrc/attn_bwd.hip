@@ -24,10 +24,15 @@
 #include "../../include/hstu.h"
 #include "device_common.h"
 
+#include <type_traits>
+
 namespace hstu {
 namespace {
 
 using namespace dev;
+
+template <bool B>
+using bc = std::integral_constant<bool, B>;
 
 __device__ __forceinline__ float sigmoid_fast(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
@@ -41,51 +46,51 @@ struct PairPrefetch {
 };
 
 // ---------------------------------------------------------------------------
-// dQ kernel (query-major): 8 waves x 16 rows (the forward's 128-row query
-// tiles), key tiles of 64.
+// dQ kernel (query-major): the forward's 128-row query tiles, 4 waves x 32
+// rows (Q and dO of a lane's two rows stay in registers), key tiles of 32.
 //
-// d rab_p: each wave writes its 16 x 64 block of dS into a private LDS area
+// d rab_p: each wave writes its 32 x 32 block of dS into a private LDS area
 // with row r shifted left by its position offset s_r (so column c holds the
-// diagonal pos_i - j = pos_w0 - c0 + 15 - c); one column sum per lane then
+// diagonal pos_i - j = pos_w0 - c0 + 31 - c); one column sum per lane then
 // gives the wave's diagonal sums, which go into a per-workgroup ring indexed
-// by the signed diagonal. Cells outside a row's 64 written columns stay zero
+// by the signed diagonal. Cells outside a row's 32 written columns stay zero
 // for the whole query tile, because the shifts do not change between key
 // tiles. Diagonals that no later key tile can touch are flushed to global
 // memory after every tile.
 // ---------------------------------------------------------------------------
 template <int D, bool USE_P, bool USE_T>
-__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int BM = kFwdBM, BN = kFwdBN, NWV = 8;
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int BM = kFwdBM, BN = 32, NWV = 4;
   constexpr int KS = D / 32, ND = D / 16;
-  constexpr int ST = D + 8;            // LDS row stride of K and V
+  constexpr int ST = D + 8;            // LDS row stride of K, V and the staged dQ
   constexpr int CH = D / 8;
   constexpr int NT = NWV * 64;
   constexpr int NCHUNK = BN * CH;
   constexpr int NCH = (NCHUNK + NT - 1) / NT;
-  constexpr int WIN = BM + BN;         // 191 window entries used
+  constexpr int WIN = BM + BN;         // 159 window entries used
   constexpr int RING = 512;
-  constexpr int SKW = 80;              // skewed row: 64 keys + 15 shifts (+1 pad)
-  static_assert(BM == 128 && BN == 64 && NCH >= 1, "8 waves x 16 rows, 64 keys");
-  static_assert(BM * ST <= 2 * BN * ST, "output staging reuses the K buffers");
-  __shared__ __attribute__((aligned(16))) u16 Ks[2 * BN * ST];
-  __shared__ __attribute__((aligned(16))) u16 Vs[2 * BN * ST];
+  constexpr int SKW = 64;              // skewed row: 32 keys + 31 shifts (+1 pad)
+  static_assert(BM == 128 && NCH >= 1, "4 waves x 32 rows");
+  static_assert(BM * ST <= 4 * BN * ST, "dQ staging reuses the K/V buffers");
+  __shared__ __attribute__((aligned(16))) u16 KV[4 * BN * ST];  // K[2 stages], V[2 stages]
   __shared__ float rabw[USE_P ? 2 * WIN : 1];
   __shared__ __attribute__((aligned(16))) unsigned tkey[USE_T ? 2 * BN : 4];
   __shared__ unsigned tkst[4];
   __shared__ float t2tab[33];
   __shared__ float ring[USE_P ? RING : 1];
-  __shared__ float skew[USE_P ? NWV * 16 * SKW : 1];
+  __shared__ float skew[USE_P ? NWV * 32 * SKW : 1];
   __shared__ float hts[USE_T ? 33 : 1];   // per-element path: by ffbh(|dt|) + 1
   __shared__ float htb[USE_T ? 32 : 1];   // constant blocks: by bucket
   __shared__ float self_acc;
   __shared__ int s_bad;
+  u16 *const Ks = KV, *const Vs = KV + 2 * BN * ST;
 
   const int H = a.H;
   const int r = blockIdx.x / H, h = blockIdx.x % H;
   if (r >= a.hdr[kHdrNQ]) return;
   const QTile tile = a.tiles[r];
   const SeqDesc sd = a.desc[tile.b];
-  const int nk = tile.nk, nf = tile.nf_nrows & 0xffff, nrows = tile.nf_nrows >> 16;
+  const int nrows = tile.nf_nrows >> 16;
   const int row0 = tile.row0;
   const long long ld = (long long)H * D;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -94,6 +99,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
   const int fi0 = sd.q_frame0 + row0;
   const int fil = fi0 + nrows - 1;
   const int kv_limit = frame_hi(fil, sd.P, sd.E);
+  const int nk = (kv_limit + BN - 1) / BN;       // key tiles of 32
+  const int nf = frame_hi(fi0, sd.P, sd.E) / BN;  // the first nf are fully visible
   const int pos_max = fil < sd.E ? fil : sd.E;
   const long long t_ref = USE_T ? a.ts[sd.q_base + row0] : 0;
 
@@ -109,66 +116,51 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
     if (tid < 32) htb[tid] = 0.f;
   }
   if (USE_P) {
-    ring[tid] = 0.f;  // RING == blockDim
-    for (int c = tid; c < NWV * 16 * SKW; c += NT) skew[c] = 0.f;
+    for (int c = tid; c < RING; c += NT) ring[c] = 0.f;
+    for (int c = tid; c < NWV * 32 * SKW; c += NT) skew[c] = 0.f;
   }
   __syncthreads();
 
-  // This lane's query row (S^T layout): local row w*16 + lr.
-  const int lrow = w * 16 + lr;
-  const bool ok = lrow < nrows;
-  const int crow = ok ? lrow : nrows - 1;
-  const int fi = fi0 + crow;
-  const int hi_r = ok ? frame_hi(fi, sd.P, sd.E) : 0;
-  const int pos_r = fi < sd.E ? fi : sd.E;
-  const int vb = pos_max - pos_r + lg * 4;
-  // position offset of this row inside its wave (0..15): the skew shift
-  const int wrow0 = min(w * 16, nrows - 1);
+  // This lane's query rows (S^T layout): local rows w*32 + nq*16 + lr.
+  const int wrow0 = min(w * 32, nrows - 1);
   const int pos_w0 = min(fi0 + wrow0, sd.E);
-  const int sh = pos_r - pos_w0;
-  unsigned tq = 0u;
+  int hi_r[2], vb_r[2], sh_r[2];
+  bool ok_r[2];
+  unsigned tq[2] = {0u, 0u};
   bool bad_t = false;
-  if (USE_T) {
-    const long long dq = a.ts[sd.q_base + row0 + crow] - t_ref;
-    bad_t |= dq < -2147483648LL || dq > 2147483647LL;
-    tq = (unsigned)(dq + 2147483648LL);
-  }
-  // dO enters as fp32 and is split into two bf16 terms (hi + lo) so that
-  // dP = dO V^T keeps close to fp32 precision: d rab sums dS over very many
-  // pairs with heavy cancellation, and one bf16 rounding of dO alone would
-  // cost about 1e-2 relative error there.
-  bf16x8 qf[KS], dof[KS], dol[KS];
-  {
+  bf16x8 qf[2][KS], dof[2][KS];
+  const u16 *dO = (const u16 *)a.dO;
+#pragma unroll
+  for (int nq = 0; nq < 2; ++nq) {
+    const int lrow = w * 32 + nq * 16 + lr;
+    ok_r[nq] = lrow < nrows;
+    const int crow = ok_r[nq] ? lrow : nrows - 1;
+    const int fi = fi0 + crow;
+    const int pos_r = fi < sd.E ? fi : sd.E;
+    hi_r[nq] = ok_r[nq] ? frame_hi(fi, sd.P, sd.E) : 0;
+    vb_r[nq] = pos_max - pos_r + lg * 4;
+    sh_r[nq] = pos_r - pos_w0;  // 0..31 for the rows of this wave
+    if (USE_T) {
+      const long long dq = a.ts[sd.q_base + row0 + crow] - t_ref;
+      bad_t |= dq < -2147483648LL || dq > 2147483647LL;
+      tq[nq] = (unsigned)(dq + 2147483648LL);
+    }
     const long long off = (long long)(sd.q_base + row0 + lrow) * ld + h * D + lg * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      float g[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) g[e] = 0.f;
-      if (ok) {
+      u32x4 v = {0u, 0u, 0u, 0u}, g = {0u, 0u, 0u, 0u};
+      if (ok_r[nq]) {
         v = *(const u32x4 *)(Q + off + ks * 32);
-        const float4 g0 = *(const float4 *)(a.dO32 + off + ks * 32);
-        const float4 g1 = *(const float4 *)(a.dO32 + off + ks * 32 + 4);
-        g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
-        g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+        g = *(const u32x4 *)(dO + off + ks * 32);
       }
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-      u32x4 hw, lw;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hw[e] = pack_bf16x2(g[2 * e], g[2 * e + 1]);
-        const float h0 = __uint_as_float(hw[e] << 16), h1 = __uint_as_float(hw[e] & 0xffff0000u);
-        lw[e] = pack_bf16x2(g[2 * e] - h0, g[2 * e + 1] - h1);
-      }
-      dof[ks] = __builtin_bit_cast(bf16x8, hw);
-      dol[ks] = __builtin_bit_cast(bf16x8, lw);
+      qf[nq][ks] = __builtin_bit_cast(bf16x8, v);
+      dof[nq][ks] = __builtin_bit_cast(bf16x8, g);
     }
   }
   unsigned qmin = 0, qmax = 0;
   if (USE_T) {
-    qmin = __builtin_amdgcn_readfirstlane(wave_min_u32(tq));
-    qmax = __builtin_amdgcn_readfirstlane(wave_max_u32(tq));
+    qmin = __builtin_amdgcn_readfirstlane(wave_min_u32(min(tq[0], tq[1])));
+    qmax = __builtin_amdgcn_readfirstlane(wave_max_u32(max(tq[0], tq[1])));
   }
 
   PairPrefetch<NCH> pf;
@@ -199,12 +191,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
       *(u32x4 *)(Vs + buf * BN * ST + row * ST + col) = pf.b[c];
     }
     if (USE_P && tid < WIN) rabw[buf * WIN + tid] = pf.r;
-    if (USE_T && tid < BN) {
-      const long long dk = pf.t - t_ref;
-      bad_t |= dk < -2147483648LL || dk > 2147483647LL;
-      const unsigned u = (unsigned)(dk + 2147483648LL);
-      tkey[buf * BN + tid] = u;
-      const unsigned mn = wave_min_u32(u), mx = wave_max_u32(u);
+    if (USE_T && tid < 64) {  // wave 0; keys are lanes 0..31
+      unsigned u = 0u;
+      if (tid < BN) {
+        const long long dk = pf.t - t_ref;
+        bad_t |= dk < -2147483648LL || dk > 2147483647LL;
+        u = (unsigned)(dk + 2147483648LL);
+        tkey[buf * BN + tid] = u;
+      }
+      const unsigned mn = wave_min_u32(tid < BN ? u : 0xffffffffu);
+      const unsigned mx = wave_max_u32(tid < BN ? u : 0u);
       if (tid == 0) {
         tkst[buf * 2] = mn;
         tkst[buf * 2 + 1] = mx;
@@ -212,38 +208,45 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  f32x4 acc[ND];
+  f32x4 acc[2][ND];
 #pragma unroll
-  for (int nd = 0; nd < ND; ++nd) acc[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 st[4], dpt[4];
+  for (int nq = 0; nq < 2; ++nq)
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) acc[nq][nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 st[2][2], dpt[2][2];
   bf16x8 dsa[2];
 
+  // S^T = bias + K Q^T and dP^T = V dO^T for the key tile in buffer buf.
   auto gemms = [&](int buf) __attribute__((always_inline)) {
     const u16 *kb = Ks + buf * BN * ST, *vbuf = Vs + buf * BN * ST;
 #pragma unroll
-    for (int mk = 0; mk < 4; ++mk) {
-      if (USE_P) {
-        const float *rw = rabw + buf * WIN + vb + mk * 16;
-        st[mk] = f32x4{rw[0], rw[1], rw[2], rw[3]};
-      } else {
-        st[mk] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+      for (int nq = 0; nq < 2; ++nq) {
+        if (USE_P) {
+          const float *rw = rabw + buf * WIN + vb_r[nq] + mk * 16;
+          st[mk][nq] = f32x4{rw[0], rw[1], rw[2], rw[3]};
+        } else {
+          st[mk][nq] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        dpt[mk][nq] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      dpt[mk] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int mk = 0; mk < 4; ++mk) {
+      for (int mk = 0; mk < 2; ++mk) {
         const bf16x8 kf = *(const bf16x8 *)(kb + (mk * 16 + lr) * ST + ks * 32 + lg * 8);
-        st[mk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], st[mk], 0, 0, 0);
         const bf16x8 vf = *(const bf16x8 *)(vbuf + (mk * 16 + lr) * ST + ks * 32 + lg * 8);
-        dpt[mk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, dof[ks], dpt[mk], 0, 0, 0);
-        dpt[mk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, dol[ks], dpt[mk], 0, 0, 0);
+#pragma unroll
+        for (int nq = 0; nq < 2; ++nq) {
+          st[mk][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[nq][ks], st[mk][nq], 0, 0, 0);
+          dpt[mk][nq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, dof[nq][ks], dpt[mk][nq], 0, 0, 0);
+        }
       }
     }
   };
 
-  float *skw = skew + w * 16 * SKW;
+  float *skw = skew + w * 32 * SKW;
   if (nk > 0) {
     load(0);
     store(0);
@@ -254,8 +257,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
   for (int kt = 0; kt < nk; ++kt) {
     const int b = kt & 1;
     const int c0 = kt * BN;
-    const bool full = kt < nf;
-    const int hirel = hi_r - (c0 + lg * 4);
+    const bool full = __builtin_amdgcn_readfirstlane(kt < nf ? 1 : 0) != 0;
+    int hirel[2];
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq) hirel[nq] = hi_r[nq] - (c0 + lg * 4);
 
     bool tconst = true;
     float tcv = 0.f;
@@ -275,97 +280,104 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
         dhi = max(qmax - kmin, kmax - qmin);
       }
       const int blo = bucket_u32(dlo, a.n_tb), bhi = bucket_u32(dhi, a.n_tb);
-      tconst = blo == bhi;
+      tconst = __builtin_amdgcn_readfirstlane(blo == bhi ? 1 : 0) != 0;
       tcv = a.rab_t[blo];
       tcidx = blo;
     }
-    float tsum = 0.f;
-    int run_b = -1;
-    float run_s = 0.f;
+
+    // dS of this wave's 32 rows x 32 keys (fp32, masked), its bf16 copy as the
+    // A operand of dQ += dS K, and its rab contributions. FULL: every pair is
+    // visible; TC: one rab_t bucket for the whole block. On the per-element
+    // rab_t path a lane's keys ascend along (mk, i) for each row, so equal
+    // buckets come in runs that are merged before they go to the histogram.
+    auto epilogue = [&](auto fullc, auto tconstc) __attribute__((always_inline)) {
+      constexpr bool FULL = decltype(fullc)::value, TC = decltype(tconstc)::value;
+      float tsum = 0.f, run_s = 0.f;
+      int run_b = -1;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      u32x4 wds;
+      for (int nq = 0; nq < 2; ++nq) {
+        u32x4 wds;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int mk = kk * 2 + h2;
-        u32x4 tk4 = {0u, 0u, 0u, 0u};
-        if (USE_T && !tconst) tk4 = *(const u32x4 *)(tkey + b * BN + mk * 16 + lg * 4);
-        float dsv[4];
+        for (int mk = 0; mk < 2; ++mk) {
+          u32x4 tk4 = {0u, 0u, 0u, 0u};
+          if (USE_T && !TC) tk4 = *(const u32x4 *)(tkey + b * BN + mk * 16 + lg * 4);
+          float dsv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = st[mk][i];
-          int tix = 0;
-          if (USE_T) {
-            if (tconst) {
-              x += tcv;
-            } else {
-              tix = ffbh_u32(absdiff_u32(tq, tk4[i])) + 1;
-              x += t2tab[tix];
-            }
-          }
-          const float sg = sigmoid_fast(x);
-          float ds = dpt[mk][i] * sg * (1.0f + x * (1.0f - sg));
-          if (!full && !(hirel > mk * 16 + i)) ds = 0.f;
-          dsv[i] = ds;
-          if (USE_P) skw[lr * SKW + mk * 16 + lg * 4 + i + 15 - sh] = ds;
-          if (USE_T) {
-            if (tconst) {
-              tsum += ds;
-            } else {
-              // keys ascend along (mk, i): merge runs of equal buckets
-              if (tix != run_b) {
-                if (run_b >= 0) atomicAdd(&hts[run_b], run_s);
-                run_b = tix;
-                run_s = 0.f;
+          for (int i = 0; i < 4; ++i) {
+            float x = st[mk][nq][i];
+            int tix = 0;
+            if (USE_T) {
+              if (TC) {
+                x += tcv;
+              } else {
+                tix = ffbh_u32(absdiff_u32(tq[nq], tk4[i])) + 1;
+                x += t2tab[tix];
               }
-              run_s += ds;
+            }
+            const float sg = sigmoid_fast(x);
+            float ds = dpt[mk][nq][i] * sg * (1.0f + x * (1.0f - sg));
+            if (!FULL) ds = hirel[nq] > mk * 16 + i ? ds : 0.f;
+            dsv[i] = ds;
+            if (USE_P) skw[(nq * 16 + lr) * SKW + mk * 16 + lg * 4 + i + 31 - sh_r[nq]] = ds;
+            if (USE_T) {
+              if (TC) {
+                tsum += ds;
+              } else {
+                if (tix != run_b) {
+                  if (run_b >= 0) atomicAdd(&hts[run_b], run_s);
+                  run_b = tix;
+                  run_s = 0.f;
+                }
+                run_s += ds;
+              }
             }
           }
+          wds[mk * 2] = pack_bf16x2(dsv[0], dsv[1]);
+          wds[mk * 2 + 1] = pack_bf16x2(dsv[2], dsv[3]);
         }
-        wds[h2 * 2] = pack_bf16x2(dsv[0], dsv[1]);
-        wds[h2 * 2 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+        dsa[nq] = __builtin_bit_cast(bf16x8, wds);
       }
-      dsa[kk] = __builtin_bit_cast(bf16x8, wds);
-    }
-    if (USE_T) {
-      if (tconst) {
-        float s = tsum;
+      if (USE_T && TC) {
+        float t = tsum;
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-        if (lane == 0) atomicAdd(&htb[tcidx], s);
-      } else if (run_b >= 0) {
-        atomicAdd(&hts[run_b], run_s);
+        for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+        if (lane == 0) atomicAdd(&htb[tcidx], t);
       }
+      if (USE_T && !TC && run_b >= 0) atomicAdd(&hts[run_b], run_s);
+    };
+    if (USE_T && !tconst) {
+      if (full) epilogue(bc<true>(), bc<false>());
+      else epilogue(bc<false>(), bc<false>());
+    } else {
+      if (full) epilogue(bc<true>(), bc<true>());
+      else epilogue(bc<false>(), bc<true>());
     }
     if (USE_P) {
       // column sums of the skewed block = this wave's diagonal sums
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      float c1 = 0.f, c2 = 0.f;
+      if (lane < 2 * BN - 1) {
+        float c1 = 0.f;
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        c1 += skw[rr * SKW + lane];
-        if (lane < 15) c2 += skw[rr * SKW + 64 + lane];
+        for (int rr = 0; rr < 32; ++rr) c1 += skw[rr * SKW + lane];
+        const int tbase = pos_w0 - c0 + 31;  // diagonal of column c is tbase - c
+        atomicAdd(&ring[(tbase - lane) & (RING - 1)], c1);
       }
-      const int tbase = pos_w0 - c0 + 15;  // diagonal of column c is tbase - c
-      if (c1 != 0.f) atomicAdd(&ring[(tbase - lane) & (RING - 1)], c1);
-      if (lane < 15 && c2 != 0.f) atomicAdd(&ring[(tbase - 64 - lane) & (RING - 1)], c2);
       __builtin_amdgcn_wave_barrier();
     }
     // dQ += dS K with K read transposed from its row-major tile.
     {
       const u16 *kbuf = Ks + b * BN * ST;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int nd = 0; nd < ND; ++nd) {
+        const u16 *p0 = kbuf + (lg * 4 + (lr >> 2)) * ST + nd * 16 + (lr & 3) * 4;
+        const s16x4 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * ST);
+        const bf16x8 kb = __builtin_bit_cast(
+            bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
-        for (int nd = 0; nd < ND; ++nd) {
-          const u16 *p0 = kbuf + (kk * 32 + lg * 4 + (lr >> 2)) * ST + nd * 16 + (lr & 3) * 4;
-          const s16x4 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * ST);
-          const bf16x8 kb = __builtin_bit_cast(
-              bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-          acc[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[kk], kb, acc[nd], 0, 0, 0);
-        }
+        for (int nq = 0; nq < 2; ++nq)
+          acc[nq][nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[nq], kb, acc[nq][nd], 0, 0, 0);
       }
     }
     if (kt + 1 < nk) {
@@ -374,7 +386,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
     }
     __syncthreads();
     // Diagonals above the next tile's window are complete: flush them.
-    if (USE_P && tid < 64) {
+    if (USE_P && tid < BN) {
       const int t = (pos_max - c0) - tid;
       float *slot = &ring[t & (RING - 1)];
       const float v = *slot;
@@ -383,9 +395,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
     }
     if (kt + 1 < nk) gemms(b ^ 1);
   }
-  if (USE_P && nk > 0 && tid < WIN - 64) {
-    // the rest of the last window: diagonals [pos_max - c_last - 190, pos_max - c_last - 64]
-    const int t = (pos_max - (nk - 1) * BN) - 64 - tid;
+  if (USE_P && nk > 0 && tid < WIN - BN) {
+    // the rest of the last window: diagonals [pos_max - c_last - 159, pos_max - c_last - 32]
+    const int t = (pos_max - (nk - 1) * BN) - BN - tid;
     const float v = ring[t & (RING - 1)];
     if (v != 0.f) atomicAdd(a.drab_p + pos_bucket(t, a.n_pos), v * a.inv_nmax);
   }
@@ -394,56 +406,60 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
   const bool any_cand = fil >= sd.E;
   if (any_cand) {
     const float bias0 = (USE_P ? a.rab_p[0] : 0.f) + (USE_T ? a.rab_t[0] : 0.f);
-    const bool cand = ok && fi0 + lrow >= sd.E;
-    float qk = 0.f, dov = 0.f;
-    const long long srow = (long long)(sd.self_base + fi0 + lrow - sd.E) * ld + h * D + lg * 8;
-    if (cand) {
+    u16 *dK = (u16 *)a.dK, *dV = (u16 *)a.dV;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kv = *(const u32x4 *)(K + srow + ks * 32);
-        const u32x4 vv = *(const u32x4 *)(V + srow + ks * 32);
-        const u16 *ke = (const u16 *)&kv, *ve = (const u16 *)&vv;
+    for (int nq = 0; nq < 2; ++nq) {
+      const int lrow = w * 32 + nq * 16 + lr;
+      const bool cand = ok_r[nq] && fi0 + lrow >= sd.E;
+      float qk = 0.f, dov = 0.f;
+      const long long srow = (long long)(sd.self_base + fi0 + lrow - sd.E) * ld + h * D + lg * 8;
+      if (cand) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qk += (float)qf[ks][e] * bf2f(ke[e]);
-          dov += ((float)dof[ks][e] + (float)dol[ks][e]) * bf2f(ve[e]);
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 kv = *(const u32x4 *)(K + srow + ks * 32);
+          const u32x4 vv = *(const u32x4 *)(V + srow + ks * 32);
+          const u16 *ke = (const u16 *)&kv, *ve = (const u16 *)&vv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            qk += (float)qf[nq][ks][e] * bf2f(ke[e]);
+            dov += (float)dof[nq][ks][e] * bf2f(ve[e]);
+          }
         }
       }
-    }
-    qk += __shfl_xor(qk, 16, 64);
-    qk += __shfl_xor(qk, 32, 64);
-    dov += __shfl_xor(dov, 16, 64);
-    dov += __shfl_xor(dov, 32, 64);
-    const float x = qk + bias0;
-    const float sg = sigmoid_fast(x);
-    const float dss = cand ? dov * sg * (1.0f + x * (1.0f - sg)) : 0.f;  // unscaled
-    const float as = cand ? x * sg : 0.f;
-    if (cand) {
-      // dK_i = dS_ii q_i / N_max and dV_i = a_ii dO_i / N_max (rows no other row sees)
-      u16 *dK = (u16 *)a.dK, *dV = (u16 *)a.dV;
+      qk += __shfl_xor(qk, 16, 64);
+      qk += __shfl_xor(qk, 32, 64);
+      dov += __shfl_xor(dov, 16, 64);
+      dov += __shfl_xor(dov, 32, 64);
+      const float x = qk + bias0;
+      const float sg = sigmoid_fast(x);
+      const float dss = cand ? dov * sg * (1.0f + x * (1.0f - sg)) : 0.f;  // unscaled
+      const float as = cand ? x * sg : 0.f;
+      if (cand) {
+        // dK_i = dS_ii q_i / N_max and dV_i = a_ii dO_i / N_max (rows no other row sees)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4 wk, wv;
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4 wk, wv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wk[e] = pack_bf16x2((float)qf[ks][2 * e] * dss * a.inv_nmax,
-                              (float)qf[ks][2 * e + 1] * dss * a.inv_nmax);
-          wv[e] = pack_bf16x2(((float)dof[ks][2 * e] + (float)dol[ks][2 * e]) * as * a.inv_nmax,
-                              ((float)dof[ks][2 * e + 1] + (float)dol[ks][2 * e + 1]) * as * a.inv_nmax);
+          for (int e = 0; e < 4; ++e) {
+            wk[e] = pack_bf16x2((float)qf[nq][ks][2 * e] * dss * a.inv_nmax,
+                                (float)qf[nq][ks][2 * e + 1] * dss * a.inv_nmax);
+            wv[e] = pack_bf16x2((float)dof[nq][ks][2 * e] * as * a.inv_nmax,
+                                (float)dof[nq][ks][2 * e + 1] * as * a.inv_nmax);
+          }
+          *(u32x4 *)(dK + srow + ks * 32) = wk;
+          *(u32x4 *)(dV + srow + ks * 32) = wv;
         }
-        *(u32x4 *)(dK + srow + ks * 32) = wk;
-        *(u32x4 *)(dV + srow + ks * 32) = wv;
+        if (lg == 0) atomicAdd(&self_acc, dss);
       }
-      if (lg == 0) atomicAdd(&self_acc, dss);
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float dv = __shfl(dss, lg * 4 + i, 64);
-      const int orow = w * 16 + lg * 4 + i;
-      if (orow < nrows && fi0 + orow >= sd.E) {
-        const u16 *kp = K + (long long)(sd.self_base + fi0 + orow - sd.E) * ld + h * D + lr;
+      for (int i = 0; i < 4; ++i) {
+        const float dv = __shfl(dss, lg * 4 + i, 64);
+        const int orow = w * 32 + nq * 16 + lg * 4 + i;
+        if (orow < nrows && fi0 + orow >= sd.E) {
+          const u16 *kp = K + (long long)(sd.self_base + fi0 + orow - sd.E) * ld + h * D + lr;
 #pragma unroll
-        for (int nd = 0; nd < ND; ++nd) acc[nd][i] += dv * bf2f(kp[nd * 16]);
+          for (int nd = 0; nd < ND; ++nd) acc[nq][nd][i] += dv * bf2f(kp[nd * 16]);
+        }
       }
     }
   }
@@ -463,16 +479,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
     if (tid < 32 && htb[tid] != 0.f) atomicAdd(a.drab_t + tid, htb[tid] * a.inv_nmax);
   }
   // Stage dQ through LDS for 16-byte row stores.
-  u16 *os = Ks;
+  u16 *os = KV;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int orow = w * 16 + lg * 4 + i;
+  for (int nq = 0; nq < 2; ++nq)
 #pragma unroll
-    for (int nd = 0; nd < ND; ++nd) {
-      const __bf16 v = (__bf16)(acc[nd][i] * a.inv_nmax);
-      os[orow * ST + nd * 16 + lr] = __builtin_bit_cast(u16, v);
+    for (int i = 0; i < 4; ++i) {
+      const int orow = w * 32 + nq * 16 + lg * 4 + i;
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        const __bf16 v = (__bf16)(acc[nq][nd][i] * a.inv_nmax);
+        os[orow * ST + nd * 16 + lr] = __builtin_bit_cast(u16, v);
+      }
     }
-  }
   __syncthreads();
   u16 *dQ = (u16 *)a.dQ;
   for (int c = tid; c < BM * CH; c += NT) {
@@ -934,7 +952,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a) {
     return hipGetLastError();                                                                   \
   }
 
-HSTU_BWD_BF16_LAUNCH(bwd_dq_kernel, 512)
+HSTU_BWD_BF16_LAUNCH(bwd_dq_kernel, 256)
 HSTU_BWD_BF16_LAUNCH(bwd_dkdv_kernel, 256)
 
 hipError_t launch_attn_bwd_dq_bf16(const BwdArgs &a, hipStream_t s) {

@@ -113,7 +113,6 @@ struct NormBwdArgs {
   int tokens_per_wave;            // contiguous tokens handled by one wave
   void *dU;                       // [T, D]
   void *dX;                       // [T, D] gradient w.r.t. the pre-norm output
-  float *dX32;                    // [T, D] the same in fp32, or NULL
   float *dgamma, *dbeta;          // [G, D] accumulated with atomics (zeroed by the caller), or NULL
 };
 hipError_t launch_norm_bwd(const NormBwdArgs &a, bool bf16, hipStream_t s);
@@ -122,7 +121,6 @@ hipError_t launch_norm_bwd(const NormBwdArgs &a, bool bf16, hipStream_t s);
 // (computed by the norm backward into the workspace).
 struct BwdArgs {
   const void *Q, *K, *V, *dO;
-  const float *dO32;               // fp32 dO (bf16 path: split into two bf16 terms for dP)
   void *dQ, *dK, *dV;
   const int64_t *ts;               // timestamps or NULL
   const float *rab_p, *rab_t;      // tables or NULL

@@ -58,12 +58,6 @@ struct Vec<false> {
   __device__ static void store(void *p, long long off, const float *x) {
     *(float4 *)((float *)p + off) = float4{x[0], x[1], x[2], x[3]};
   }
-  // n consecutive fp32 values (n a multiple of 4)
-  template <int n>
-  __device__ static void store4n(float *p, long long off, const float *x) {
-#pragma unroll
-    for (int e = 0; e < n; e += 4) *(float4 *)(p + off + e) = float4{x[e], x[e + 1], x[e + 2], x[e + 3]};
-  }
 };
 
 template <bool BF16, int MAXCH>
@@ -218,7 +212,6 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
           }
           V::store(a.dU, row + ch * N, du);
           V::store(a.dX, row + ch * N, dx);
-          if (a.dX32) Vec<false>::store4n<N>(a.dX32, row + ch * N, dx);
         }
       }
       continue;
@@ -270,7 +263,6 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
 #pragma unroll
         for (int e = 0; e < N; ++e) dx[e] = rstd * (gh[k][e] - m1 - xh[k][e] * m2);
         V::store(a.dX, row + ch * N, dx);
-        if (a.dX32) Vec<false>::store4n<N>(a.dX32, row + ch * N, dx);
       }
     }
   }
