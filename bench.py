@@ -60,10 +60,21 @@ def visible_pairs(lengths, prefix=None, cand=None):
     return tot
 
 
-def kernel_source_hash():
+# Sources each timed kernel is built from (a traffic figure is valid only
+# while these are unchanged).
+KERNEL_SOURCES = {
+    "attn_fwd": ["attn_fwd.hip", "device_common.h", "hstu_internal.h"],
+    "attn_bwd_dq": ["attn_bwd.hip", "device_common.h", "hstu_internal.h"],
+    "attn_bwd_dkdv": ["attn_bwd.hip", "device_common.h", "hstu_internal.h"],
+    "norm_fwd": ["norm.hip", "hstu_internal.h"],
+    "norm_bwd": ["norm.hip", "hstu_internal.h"],
+}
+
+
+def kernel_source_hash(kernel):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "hstu_jagged_pointwise_attn_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -78,7 +89,7 @@ def traffic_from_profiles(workload, kernel):
     with open(path) as f:
         data = json.load(f)
     ent = data.get(workload, {}).get(kernel)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if not ent or kernel not in KERNEL_SOURCES or ent.get("source_hash") != kernel_source_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 

@@ -215,6 +215,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     qmin = __builtin_amdgcn_readfirstlane(wave_min_u32(min(tq_r[0], tq_r[1])));
     qmax = __builtin_amdgcn_readfirstlane(wave_max_u32(max(tq_r[0], tq_r[1])));
   }
+  // Keys [0, wave_hi) are the ones this wave's rows see: a key tile at or
+  // beyond it (the upper half of a diagonal block, or a wave past the last
+  // row) is skipped by this wave; its pairs are all masked.
+  const int wave_hi = __builtin_amdgcn_readfirstlane(
+      (int)wave_max_u32((unsigned)max(hi_r[0], hi_r[1])));
 
   // Global -> register prefetch of one key tile, and register -> LDS store.
   TilePrefetch<NCH> pf;
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     fwd_store_tile<D, BN, USE_P, USE_T>(pf, tid, Ks, Vs, rabw, tkey, tkst, t_ref, bad_t);
     if (nk > 1) fwd_load_tile<D, BN, USE_P, USE_T>(pf, cx, 1);
     __syncthreads();
-    qk(0);
+    if (wave_hi > 0) qk(0);
   }
   for (int kt = 0; kt < nk; ++kt) {
     const int b = kt & 1;
@@ -314,21 +319,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     }
 
     const unsigned *tkb = tkey + b * (USE_T ? BN : 0);
-    if (USE_T && !tconst) {
-      if (full) fwd_epilogue<true, USE_T, false>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
-      else fwd_epilogue<false, USE_T, false>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
-    } else {
-      if (full) fwd_epilogue<true, USE_T, true>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
-      else fwd_epilogue<false, USE_T, true>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
+    if (wave_hi > c0) {
+      if (USE_T && !tconst) {
+        if (full) fwd_epilogue<true, USE_T, false>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
+        else fwd_epilogue<false, USE_T, false>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
+      } else {
+        if (full) fwd_epilogue<true, USE_T, true>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
+        else fwd_epilogue<false, USE_T, true>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
+      }
+      pv(b);
     }
-    pv(b);
     if (kt + 1 < nk) {
       fwd_store_tile<D, BN, USE_P, USE_T>(pf, tid, Ks + (b ^ 1) * BN * KST, Vs + (b ^ 1) * BN * VST,
                                           rabw + (b ^ 1) * (USE_P ? WIN : 0), tkey + (b ^ 1) * (USE_T ? BN : 0),
                                           tkst + (b ^ 1) * 2, t_ref, bad_t);
       if (kt + 2 < nk) fwd_load_tile<D, BN, USE_P, USE_T>(pf, cx, kt + 2);
       __syncthreads();
-      qk(b ^ 1);
+      if (wave_hi > c0 + BN) qk(b ^ 1);
     }
   }
 
