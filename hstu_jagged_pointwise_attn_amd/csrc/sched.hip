@@ -150,25 +150,59 @@ __device__ int block_exclusive_scan(int v, int *s_wsum, int *total) {
   return excl;
 }
 
-__global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
-  __shared__ int s_qoff[kMaxSeqs + 1];
-  __shared__ unsigned s_keys[kSortCap];
-  __shared__ int s_wsum[kSchedThreads / 64];
+// Bitonic sort of n2 (a power of two, at most kSchedThreads) keys, one per
+// thread: stages with partners in the same wave exchange through lane
+// shuffles, the others through LDS. Every thread of the block calls it.
+__device__ void sort_small(unsigned *keys, int n2) {
   const int tid = threadIdx.x;
-
-  if (tid == 0) {
-    int bits = 0;
-    if (a.mode != kSchedMFalcon) {
-      if (a.offsets[0] != 0 || (long long)a.offsets[a.B] != a.Tq) bits |= HSTU_DEV_BAD_OFFSETS;
-    } else {
-      if (a.cand_offsets[0] != 0 || (long long)a.cand_offsets[a.B] != a.Tq ||
-          a.hist_offsets[0] != 0 || (long long)a.hist_offsets[a.B] != a.Tkv)
-        bits |= HSTU_DEV_BAD_OFFSETS;
+  unsigned x = tid < n2 ? keys[tid] : 0xffffffffu;
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      unsigned y;
+      if (j >= 64) {
+        __syncthreads();
+        if (tid < n2) keys[tid] = x;
+        __syncthreads();
+        y = tid < n2 ? keys[tid ^ j] : 0xffffffffu;
+      } else {
+        y = (unsigned)__shfl_xor((int)x, j, 64);
+      }
+      const bool up = (tid & k) == 0, lower = (tid & j) == 0;
+      x = (lower == up) ? min(x, y) : max(x, y);
     }
-    a.hdr[kHdrStatus] = bits;
-    a.hdr[kHdrFirstBad] = bits ? -1 : 0x7fffffff;
   }
   __syncthreads();
+  if (tid < n2) keys[tid] = x;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
+  constexpr int kRecCache = kSchedThreads;  // records kept in LDS for short lists
+  __shared__ int s_qoff[kMaxSeqs + 1];
+  __shared__ unsigned s_keys[kSortCap];
+  __shared__ QTile s_rec[kRecCache];
+  __shared__ int s_wsum[kSchedThreads / 64];
+  __shared__ int s_bits, s_first;
+  const int tid = threadIdx.x;
+
+  // Status: accumulated in LDS, written once at the end.
+  if (tid == 0) {
+    s_bits = 0;
+    s_first = 0x7fffffff;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    bool bad;
+    if (a.mode != kSchedMFalcon)
+      bad = a.offsets[0] != 0 || (long long)a.offsets[a.B] != a.Tq;
+    else
+      bad = a.cand_offsets[0] != 0 || (long long)a.cand_offsets[a.B] != a.Tq ||
+            a.hist_offsets[0] != 0 || (long long)a.hist_offsets[a.B] != a.Tkv;
+    if (bad) {
+      atomicOr(&s_bits, HSTU_DEV_BAD_OFFSETS);
+      atomicMin(&s_first, -1);
+    }
+  }
 
   // Per-sequence validation, descriptors and query-tile counts; scan.
   int carry = 0;
@@ -178,14 +212,14 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
       int bits;
       SeqDesc s = seq_info(a, b, &bits);
       if (bits) {
-        atomicOr(&a.hdr[kHdrStatus], bits);
-        atomicMin(&a.hdr[kHdrFirstBad], b);
+        atomicOr(&s_bits, bits);
+        atomicMin(&s_first, b);
       }
       a.desc[b] = s;
       nq = qtile_count(a, s);
     }
     int total;
-    int excl = block_exclusive_scan(nq, s_wsum, &total);
+    int excl = block_exclusive_scan(nq, s_wsum, &total);  // contains barriers
     if (b < a.B) s_qoff[b] = carry + excl;
     carry += total;
   }
@@ -194,14 +228,10 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
   // Sequences that overlap (possible only with inconsistent offsets) could
   // exceed the capacity sized from the token count: then nothing runs.
   const int NQ = carry <= a.max_tiles ? carry : 0;
-  if (tid == 0 && carry > a.max_tiles) {
-    atomicOr(&a.hdr[kHdrStatus], HSTU_DEV_BAD_OFFSETS);
-    atomicMin(&a.hdr[kHdrFirstBad], -1);
-  }
   for (int b = tid; b <= a.B; b += kSchedThreads) a.qoff[b] = s_qoff[b];
-  if (tid == 0) a.hdr[kHdrNQ] = NQ;
 
   const bool sorted = NQ <= kSortCap;
+  const bool cached = NQ <= kRecCache;
   int n2 = 1;
   while (n2 < NQ) n2 <<= 1;
 
@@ -219,31 +249,50 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
     int bits;
     SeqDesc s = seq_info(a, lo, &bits);
     QTile r = make_tile(a, s, lo, g - s_qoff[lo]);
+    if (cached) s_rec[g] = r;
     if (sorted) s_keys[g] = ((unsigned)(kMaxKeyTiles - r.nk) << 18) | (unsigned)g;
     else a.tiles[g] = r;
   }
-  if (!sorted) return;
   __syncthreads();
+  if (tid == 0) {
+    int bits = s_bits, first = s_first;
+    if (carry > a.max_tiles) {
+      bits |= HSTU_DEV_BAD_OFFSETS;
+      first = -1;
+    }
+    a.hdr[kHdrStatus] = bits;
+    a.hdr[kHdrFirstBad] = first;
+    a.hdr[kHdrNQ] = NQ;
+  }
+  if (!sorted) return;
 
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < n2; i += kSchedThreads) {
-        int ixj = i ^ j;
-        if (ixj > i) {
-          unsigned x = s_keys[i], y = s_keys[ixj];
-          bool up = (i & k) == 0;
-          if ((x > y) == up) {
-            s_keys[i] = y;
-            s_keys[ixj] = x;
+  if (n2 <= kSchedThreads) {
+    sort_small(s_keys, n2);
+  } else {
+    for (int k = 2; k <= n2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < n2; i += kSchedThreads) {
+          int ixj = i ^ j;
+          if (ixj > i) {
+            unsigned x = s_keys[i], y = s_keys[ixj];
+            bool up = (i & k) == 0;
+            if ((x > y) == up) {
+              s_keys[i] = y;
+              s_keys[ixj] = x;
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
 
   for (int r = tid; r < NQ; r += kSchedThreads) {
     int g = (int)(s_keys[r] & 0x3ffffu);
+    if (cached) {
+      a.tiles[r] = s_rec[g];
+      continue;
+    }
     int lo = 0, hi = a.B;
     while (hi - lo > 1) {
       int mid = (lo + hi) >> 1;
