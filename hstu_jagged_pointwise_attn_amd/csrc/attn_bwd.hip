@@ -62,7 +62,7 @@ template <int D, bool USE_P, bool USE_T>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BM = kFwdBM, BN = 32, NWV = 4;
   constexpr int KS = D / 32, ND = D / 16;
-  constexpr int ST = D + 8;            // LDS row stride of K, V and the staged dQ
+  constexpr int ST = D + 16;           // LDS row stride of K, V and the staged dQ
   constexpr int CH = D / 8;
   constexpr int NT = NWV * 64;
   constexpr int NCHUNK = BN * CH;
@@ -509,7 +509,7 @@ template <int D, bool USE_P, bool USE_T>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BN = kBwdKBN, BM = kBwdKBM;
   constexpr int KS = D / 32, ND = D / 16;
-  constexpr int ST = D + 8;            // LDS row stride of the Q and dO tiles
+  constexpr int ST = D + 16;           // LDS row stride of the Q and dO tiles
   constexpr int CH = D / 8;
   constexpr int NCH = BM * CH / 256;
   constexpr int WIN = BM + BN;

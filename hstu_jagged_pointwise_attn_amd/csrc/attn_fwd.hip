@@ -67,7 +67,7 @@ template <int D, int BN, bool USE_P, bool USE_T, int NCH>
 __device__ __forceinline__ void fwd_store_tile(const TilePrefetch<NCH> &pf, int tid, u16 *Kb, u16 *Vb,
                                                float *rw, unsigned *tk, unsigned *tst, long long t_ref,
                                                bool &bad_t) {
-  constexpr int CH = D / 8, WIN = kFwdBM + BN, KST = D + 8, VST = D + 16;
+  constexpr int CH = D / 8, WIN = kFwdBM + BN, KST = D + 16, VST = D + 16;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int chunk = tid + c * 256;
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int KS = D / 32;          // k-steps of the K Q^T contraction
   constexpr int ND = D / 16;          // 16-column blocks of O
-  constexpr int KST = D + 8;          // LDS row stride of K (elements)
+  constexpr int KST = D + 16;         // LDS row stride of K (elements)
   constexpr int VST = D + 16;         // LDS row stride of V (elements)
   constexpr int OST = D + 8;          // LDS row stride of the staged output
   constexpr int CH = D / 8;           // 16-byte chunks per row
