@@ -56,6 +56,7 @@ class Problem:
     gamma: Optional[np.ndarray] = None        # float32 [n_groups, D]
     beta: Optional[np.ndarray] = None
     dY: Optional[torch.Tensor] = None         # [T, H*d]
+    time_filter: bool = False                 # candidates see causal keys only if strictly earlier
     extra: dict = field(default_factory=dict)
 
     @property
@@ -104,6 +105,7 @@ class MFalconProblem:
     beta: Optional[np.ndarray] = None
     Q_hist: Optional[torch.Tensor] = None   # history queries, used only for a full-pass check
     U_hist: Optional[torch.Tensor] = None
+    time_filter: bool = False               # candidates see history keys only if strictly earlier
 
     @property
     def B(self) -> int:
@@ -210,6 +212,28 @@ def custom(name, lengths, *, H, d, dtype=torch.bfloat16, wid=99, std=0.02, n_max
         ts=ts, rab_p=rab_p, rab_t=rab_t,
         group=None if group is None else np.asarray(group, np.uint8), n_groups=n_groups,
         gamma=gamma, beta=beta, dY=dY)
+
+
+def interleave_candidate_times(p: Problem, seed: int) -> Problem:
+    """Give each candidate a timestamp drawn among the times of its sequence's
+    causal segment (half of them exactly equal to one, the rest one second
+    after one), so that under the timestamp filter candidates see different
+    prefixes of the real-time tokens. Sequences without a causal segment keep
+    their times. Creates timestamps if the problem has none."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ts = p.ts.copy() if p.ts is not None else _timestamps(seed % 1000, p.lengths)
+    for b in range(p.B):
+        s, e = int(p.offsets[b]), int(p.offsets[b + 1])
+        P = int(p.prefix_len[b]) if p.prefix_len is not None else 0
+        C = int(p.cand_len[b]) if p.cand_len is not None else 0
+        E = e - s - C
+        if C == 0 or E <= P:
+            continue
+        src = ts[s + P:s + E]
+        pick = src[rng.integers(0, len(src), size=C)] + rng.integers(0, 2, size=C)
+        ts[s + E:e] = pick
+    p.ts = ts
+    return p
 
 
 # ---------------------------------------------------------------- workloads

@@ -53,6 +53,8 @@ def _load():
         _lib.oracle_visible.argtypes = [ctypes.c_int] * 5
         _lib.oracle_classify_tiles.restype = ctypes.c_int
         _lib.oracle_classify_tiles.argtypes = [ctypes.c_int] * 7 + [ctypes.c_void_p]
+        _lib.oracle_classify_tiles_tf.restype = ctypes.c_int
+        _lib.oracle_classify_tiles_tf.argtypes = [ctypes.c_int] * 8 + [ctypes.c_void_p]
         for name in ("oracle_fwd", "oracle_bwd", "oracle_mfalcon"):
             getattr(_lib, name).restype = ctypes.c_int
     return _lib
@@ -93,9 +95,11 @@ def visible(i: int, j: int, L: int, P: int, C: int) -> bool:
 
 def fwd(offsets, Q, K, V, U, *, H, d, prefix_len=None, cand_len=None, ts=None, rab_p=None,
         rab_t=None, n_max=1.0, norm=NORM_LN, eps=1e-5, group=None, n_groups=1, gamma=None,
-        beta=None, row_sel=None, nthreads=0):
+        beta=None, row_sel=None, time_filter=False, nthreads=0):
     """Forward pass. Q/K/V/U: [T, H, d] (any float dtype). Returns dict with
-    Y, O ([T, H*d] float64), mean, rstd ([T] float64)."""
+    Y, O ([T, H*d] float64), mean, rstd ([T] float64). time_filter: MTGR's
+    timestamp filter (a candidate sees a causal-segment key only if the key
+    is strictly earlier)."""
     lib = _load()
     offsets = _i32(offsets)
     B = len(offsets) - 1
@@ -113,7 +117,8 @@ def fwd(offsets, Q, K, V, U, *, H, d, prefix_len=None, cand_len=None, ts=None, r
         _p(rt), ctypes.c_int(0 if rt is None else len(rt)),
         ctypes.c_double(n_max), ctypes.c_int(norm), ctypes.c_double(eps),
         _p(grp), ctypes.c_int(n_groups), _p(gm), _p(bt), _p(sel),
-        _p(Y), _p(O), _p(mean), _p(rstd), ctypes.c_int(_threads(nthreads)))
+        _p(Y), _p(O), _p(mean), _p(rstd), ctypes.c_int(int(bool(time_filter))),
+        ctypes.c_int(_threads(nthreads)))
     if rc != 0:
         raise ValueError(f"oracle_fwd rejected its input (code {rc})")
     return {"Y": Y, "O": O, "mean": mean, "rstd": rstd}
@@ -121,7 +126,7 @@ def fwd(offsets, Q, K, V, U, *, H, d, prefix_len=None, cand_len=None, ts=None, r
 
 def bwd(offsets, Q, K, V, U, dY, *, H, d, prefix_len=None, cand_len=None, ts=None, rab_p=None,
         rab_t=None, n_max=1.0, norm=NORM_LN, eps=1e-5, group=None, n_groups=1, gamma=None,
-        beta=None, nthreads=0):
+        beta=None, time_filter=False, nthreads=0):
     """Backward pass (recomputes the forward). Returns dict with dQ, dK, dV,
     dU ([T, H*d]), drab_p, drab_t, dgamma, dbeta (None when not applicable),
     and drab_p_abs / drab_t_abs: the sums of |dS| that enter each rab entry."""
@@ -150,7 +155,7 @@ def bwd(offsets, Q, K, V, U, dY, *, H, d, prefix_len=None, cand_len=None, ts=Non
         ctypes.c_double(n_max), ctypes.c_int(norm), ctypes.c_double(eps),
         _p(grp), ctypes.c_int(n_groups), _p(gm), _p(bt), _p(dY),
         _p(dQ), _p(dK), _p(dV), _p(dU), _p(drp), _p(drt), _p(dgm), _p(dbt), _p(drpa), _p(drta),
-        ctypes.c_int(_threads(nthreads)))
+        ctypes.c_int(int(bool(time_filter))), ctypes.c_int(_threads(nthreads)))
     if rc != 0:
         raise ValueError(f"oracle_bwd rejected its input (code {rc})")
     return {"dQ": dQ, "dK": dK, "dV": dV, "dU": dU, "drab_p": drp, "drab_t": drt,
@@ -159,7 +164,7 @@ def bwd(offsets, Q, K, V, U, dY, *, H, d, prefix_len=None, cand_len=None, ts=Non
 
 def mfalcon(hist_offsets, cand_offsets, K_cache, V_cache, Qc, Kc, Vc, Uc, *, H, d, hist_ts=None,
             cand_ts=None, rab_p=None, rab_t=None, n_max=1.0, norm=NORM_LN, eps=1e-5,
-            cand_group=None, n_groups=1, gamma=None, beta=None, nthreads=0):
+            cand_group=None, n_groups=1, gamma=None, beta=None, time_filter=False, nthreads=0):
     """M-FALCON scoring of candidates against cached history K/V. Returns dict
     with Y, O ([Tc, H*d]), mean, rstd ([Tc])."""
     lib = _load()
@@ -180,28 +185,30 @@ def mfalcon(hist_offsets, cand_offsets, K_cache, V_cache, Qc, Kc, Vc, Uc, *, H, 
         _p(rt), ctypes.c_int(0 if rt is None else len(rt)),
         ctypes.c_double(n_max), ctypes.c_int(norm), ctypes.c_double(eps),
         _p(grp), ctypes.c_int(n_groups), _p(gm), _p(bt),
-        _p(Y), _p(O), _p(mean), _p(rstd), ctypes.c_int(_threads(nthreads)))
+        _p(Y), _p(O), _p(mean), _p(rstd), ctypes.c_int(int(bool(time_filter))),
+        ctypes.c_int(_threads(nthreads)))
     if rc != 0:
         raise ValueError(f"oracle_mfalcon rejected its input (code {rc})")
     return {"Y": Y, "O": O, "mean": mean, "rstd": rstd}
 
 
-def classify_tiles(L, P, C, r0, nrows, BN, nkt):
+def classify_tiles(L, P, C, r0, nrows, BN, nkt, time_filter=False):
     """Brute-force kinds (0 absent, 1 partial, 2 full) of key tiles [0, nkt)
-    for query rows [r0, r0+nrows) of a frame (L, P, C)."""
+    for query rows [r0, r0+nrows) of a frame (L, P, C). With time_filter, a
+    (candidate row, causal key) pair makes its tile present but not full."""
     kind = np.zeros(max(nkt, 1), dtype=np.int8)
-    _load().oracle_classify_tiles(int(L), int(P), int(C), int(r0), int(nrows), int(BN), int(nkt),
-                                  ctypes.c_void_p(kind.ctypes.data))
+    _load().oracle_classify_tiles_tf(int(L), int(P), int(C), int(r0), int(nrows), int(BN), int(nkt),
+                                     int(bool(time_filter)), ctypes.c_void_p(kind.ctypes.data))
     return kind[:nkt]
 
 
-def _qtile_entry(b, frame_L, P, C, frame_r0, nrows, BN, local_row0):
+def _qtile_entry(b, frame_L, P, C, frame_r0, nrows, BN, local_row0, time_filter=False):
     nkt = -(-frame_L // BN)
-    kinds = classify_tiles(frame_L, P, C, frame_r0, nrows, BN, nkt)
+    kinds = classify_tiles(frame_L, P, C, frame_r0, nrows, BN, nkt, time_filter)
     return {"b": b, "row0": local_row0, "nrows": nrows, "kinds": kinds}
 
 
-def schedule(offsets, BM, BN, prefix_len=None, cand_len=None):
+def schedule(offsets, BM, BN, prefix_len=None, cand_len=None, time_filter=False):
     """Query-tile schedule of the attention forward: one entry per query tile
     (sequence b, first row row0, row count nrows, kinds of its key tiles),
     canonical order (b, row0) ascending."""
@@ -212,11 +219,11 @@ def schedule(offsets, BM, BN, prefix_len=None, cand_len=None):
         P = int(prefix_len[b]) if prefix_len is not None else 0
         C = int(cand_len[b]) if cand_len is not None else 0
         for r0 in range(0, L, BM):
-            out.append(_qtile_entry(b, L, P, C, r0, min(BM, L - r0), BN, r0))
+            out.append(_qtile_entry(b, L, P, C, r0, min(BM, L - r0), BN, r0, time_filter))
     return out
 
 
-def schedule_mfalcon(hist_offsets, cand_offsets, BM, BN, microbatch):
+def schedule_mfalcon(hist_offsets, cand_offsets, BM, BN, microbatch, time_filter=False):
     """Query-tile schedule of M-FALCON scoring: the candidates of user b are
     cut into microbatches of `microbatch` candidates (0 = one microbatch), and
     each microbatch into query tiles of at most BM rows. Row indices are local
@@ -233,7 +240,7 @@ def schedule_mfalcon(hist_offsets, cand_offsets, BM, BN, microbatch):
             e = min(m, s + mb)
             for r0 in range(s, e, BM):
                 nrows = min(BM, e - r0)
-                out.append(_qtile_entry(b, n + m, 0, m, n + r0, nrows, BN, r0))
+                out.append(_qtile_entry(b, n + m, 0, m, n + r0, nrows, BN, r0, time_filter))
     return out
 
 

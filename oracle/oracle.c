@@ -69,6 +69,9 @@ int oracle_time_bucket(int64_t dt, int n_tb) {
   return b < n_tb - 1 ? b : n_tb - 1;
 }
 
+int oracle_classify_tiles_tf(int L, int P, int C, int r0, int nrows, int BN, int nkt,
+                             int time_filter, int8_t *kind);
+
 /* Visibility of key j from row i inside one sequence of length L with a
  * bidirectional prefix of P tokens and a candidate tail of C tokens. */
 int oracle_visible(int i, int j, int L, int P, int C) {
@@ -77,6 +80,17 @@ int oracle_visible(int i, int j, int L, int P, int C) {
   if (i < P) return j < P;
   if (i < E) return j <= i;
   return j < E || j == i;
+}
+
+/* The same with MTGR's timestamp filter for candidates (MTGR deep read,
+ * section 2: exposure samples are filtered by timestamp to stay causal): when
+ * time_filter is set, a candidate row i (i >= E) sees a key j of the causal
+ * segment [P, E) only if t_j < t_i; everything else is as above. */
+static int visible_t(int i, int j, int L, int P, int C, const int64_t *ts, int time_filter) {
+  int v = oracle_visible(i, j, L, P, C);
+  int E = L - C;
+  if (v && time_filter && i >= E && j >= P && j < E) return ts[j] < ts[i];
+  return v;
 }
 
 static int position_of(int i, int E) { return i < E ? i : E; }
@@ -93,6 +107,7 @@ typedef struct {
   const double *rab_p; int n_pos;
   const double *rab_t; int n_tb;
   double inv_nmax;
+  int time_filter;                 /* candidates see causal keys only if earlier (needs ts) */
 } frame_t;
 
 static double logit(const frame_t *f, int i, int j, int *pidx, int *tidx) {
@@ -122,7 +137,7 @@ static double logit(const frame_t *f, int i, int j, int *pidx, int *tidx) {
 static void attend_row(const frame_t *f, int i, double *out) {
   for (int c = 0; c < f->d; c++) out[c] = 0.0;
   for (int j = 0; j < f->L; j++) {
-    if (!oracle_visible(i, j, f->L, f->P, f->C)) continue;
+    if (!visible_t(i, j, f->L, f->P, f->C, f->ts, f->time_filter)) continue;
     int pi, ti;
     double a = silu(logit(f, i, j, &pi, &ti)) * f->inv_nmax;
     const double *vj = f->v + (long)j * f->v_stride;
@@ -183,10 +198,11 @@ int oracle_fwd(int B, int H, int d, const int32_t *offsets, const int32_t *prefi
                const double *rab_t, int n_tb, double n_max, int norm, double eps,
                const uint8_t *group, int n_groups, const double *gamma, const double *beta,
                const uint8_t *row_sel, double *Y, double *O, double *mean, double *rstd,
-               int nthreads) {
+               int time_filter, int nthreads) {
   int err = check_common(B, H, d, offsets, prefix_len, cand_len);
   if (err) return err;
   if (n_max <= 0) return 5;
+  if (time_filter && !ts) return 9;
   if (norm == NORM_GLN && (!group || n_groups <= 0)) return 6;
   const int D = H * d;
   const long T = offsets[B];
@@ -214,6 +230,7 @@ int oracle_fwd(int B, int H, int d, const int32_t *offsets, const int32_t *prefi
     f.rab_p = rab_p; f.n_pos = n_pos;
     f.rab_t = rab_t; f.n_tb = n_tb;
     f.inv_nmax = 1.0 / n_max;
+    f.time_filter = time_filter;
     for (int i = 0; i < f.L; i++) {
       if (row_sel && !row_sel[base + i]) continue;
       attend_row(&f, i, O + (base + i) * D + (long)h * d);
@@ -245,9 +262,10 @@ int oracle_bwd(int B, int H, int d, const int32_t *offsets, const int32_t *prefi
                const uint8_t *group, int n_groups, const double *gamma, const double *beta,
                const double *dY, double *dQ, double *dK, double *dV, double *dU,
                double *drab_p, double *drab_t, double *dgamma, double *dbeta,
-               double *drab_p_abs, double *drab_t_abs, int nthreads) {
+               double *drab_p_abs, double *drab_t_abs, int time_filter, int nthreads) {
   int err = check_common(B, H, d, offsets, prefix_len, cand_len);
   if (err) return err;
+  if (time_filter && !ts) return 9;
   const int D = H * d;
   const long T = offsets[B];
   const int G = (norm == NORM_GLN) ? n_groups : 1;
@@ -262,7 +280,7 @@ int oracle_bwd(int B, int H, int d, const int32_t *offsets, const int32_t *prefi
   }
   err = oracle_fwd(B, H, d, offsets, prefix_len, cand_len, Q, K, V, U, ts, rab_p, n_pos, rab_t,
                    n_tb, n_max, norm, eps, group, n_groups, gamma, beta, NULL, Yt, O, mean, rstd,
-                   nthreads);
+                   time_filter, nthreads);
   if (err) {
     free(O); free(Yt); free(mean); free(rstd); free(dO);
     return err;
@@ -356,12 +374,13 @@ int oracle_bwd(int B, int H, int d, const int32_t *offsets, const int32_t *prefi
       f.rab_p = rab_p; f.n_pos = n_pos;
       f.rab_t = rab_t; f.n_tb = n_tb;
       f.inv_nmax = 1.0 / n_max;
+      f.time_filter = time_filter;
       for (int i = 0; i < f.L; i++) {
         const double *doi = dO + (base + i) * D + (long)h * d;
         const double *qi = f.q + (long)i * D;
         double *dqi = dQ + (base + i) * D + (long)h * d;
         for (int j = 0; j < f.L; j++) {
-          if (!oracle_visible(i, j, f.L, f.P, f.C)) continue;
+          if (!visible_t(i, j, f.L, f.P, f.C, f.ts, f.time_filter)) continue;
           int pidx, tidx;
           double s = logit(&f, i, j, &pidx, &tidx);
           double sig = 1.0 / (1.0 + exp(-s));
@@ -451,7 +470,7 @@ int oracle_mfalcon(int B, int H, int d, const int32_t *hist_offsets,
                    const double *rab_t, int n_tb, double n_max, int norm, double eps,
                    const uint8_t *cand_group, int n_groups, const double *gamma,
                    const double *beta, double *Yc, double *Oc, double *mean, double *rstd,
-                   int nthreads) {
+                   int time_filter, int nthreads) {
   if (B < 0 || H <= 0 || d <= 0 || !hist_offsets || !cand_offsets) return 1;
   if (hist_offsets[0] != 0 || cand_offsets[0] != 0) return 2;
   for (int b = 0; b < B; b++)
@@ -464,6 +483,7 @@ int oracle_mfalcon(int B, int H, int d, const int32_t *hist_offsets,
     for (long t = 0; t < Tc; t++)
       if (cand_group[t] >= n_groups) return 8;
   const int use_ts = hist_ts && cand_ts;
+  if (time_filter && !use_ts) return 9;
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
@@ -501,6 +521,7 @@ int oracle_mfalcon(int B, int H, int d, const int32_t *hist_offsets,
     f.rab_p = rab_p; f.n_pos = n_pos;
     f.rab_t = rab_t; f.n_tb = n_tb;
     f.inv_nmax = 1.0 / n_max;
+    f.time_filter = time_filter;
     for (int c = 0; c < m; c++) attend_row(&f, n + c, Oc + (cb + c) * D + (long)h * d);
     free(fq); free(fk); free(fv); free(ft);
   }
@@ -524,17 +545,27 @@ int oracle_mfalcon(int B, int H, int d, const int32_t *hist_offsets,
  * for kt in [0, nkt) and returns the number of present tiles.
  */
 int oracle_classify_tiles(int L, int P, int C, int r0, int nrows, int BN, int nkt, int8_t *kind) {
+  return oracle_classify_tiles_tf(L, P, C, r0, nrows, BN, nkt, 0, kind);
+}
+
+/* The same when MTGR's timestamp filter is on. The schedule is built from
+ * the segment structure alone, so a (candidate row, causal key) pair counts
+ * as possibly visible: it makes its tile present, and never full. */
+int oracle_classify_tiles_tf(int L, int P, int C, int r0, int nrows, int BN, int nkt,
+                             int time_filter, int8_t *kind) {
   int E = L - C, present = 0;
   for (int kt = 0; kt < nkt; kt++) {
-    long carried = 0, total = 0;
+    long carried = 0, sure = 0, total = 0;
     for (int i = r0; i < r0 + nrows; i++) {
       for (int j = kt * BN; j < kt * BN + BN; j++) {
         total++;
         int cand_self = (i >= E && j == i);
-        if (oracle_visible(i, j, L, P, C) && !cand_self) carried++;
+        if (!oracle_visible(i, j, L, P, C) || cand_self) continue;
+        carried++;
+        if (!(time_filter && i >= E && j >= P && j < E)) sure++;
       }
     }
-    kind[kt] = carried == 0 ? 0 : (carried == total ? 2 : 1);
+    kind[kt] = carried == 0 ? 0 : (sure == total ? 2 : 1);
     if (carried) present++;
   }
   return present;

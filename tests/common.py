@@ -12,7 +12,7 @@ def f64(t):
 def oracle_opts(p):
     return dict(H=p.H, d=p.d, prefix_len=p.prefix_len, cand_len=p.cand_len, ts=p.ts, rab_p=p.rab_p,
                 rab_t=p.rab_t, n_max=p.n_max, norm=p.norm, eps=p.eps, group=p.group,
-                n_groups=p.n_groups, gamma=p.gamma, beta=p.beta)
+                n_groups=p.n_groups, gamma=p.gamma, beta=p.beta, time_filter=p.time_filter)
 
 
 def oracle_fwd(p, row_sel=None, Q=None, K=None, V=None, U=None):
@@ -30,7 +30,7 @@ def oracle_mfalcon(mf):
                           f64(mf.Kc), f64(mf.Vc), f64(mf.Uc), H=mf.H, d=mf.d, hist_ts=mf.hist_ts,
                           cand_ts=mf.cand_ts, rab_p=mf.rab_p, rab_t=mf.rab_t, n_max=mf.n_max, norm=mf.norm,
                           eps=mf.eps, cand_group=mf.cand_group, n_groups=mf.n_groups, gamma=mf.gamma,
-                          beta=mf.beta)
+                          beta=mf.beta, time_filter=mf.time_filter)
 
 
 def rel_l2(got, ref):

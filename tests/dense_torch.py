@@ -38,9 +38,12 @@ def bucket(dt, n_tb):
 
 
 def forward(offsets, Q, K, V, U, *, H, d, prefix_len=None, cand_len=None, ts=None, rab_p=None,
-            rab_t=None, n_max=1.0, norm=1, eps=1e-5, group=None, gamma=None, beta=None):
+            rab_t=None, n_max=1.0, norm=1, eps=1e-5, group=None, gamma=None, beta=None,
+            time_filter=False):
     """Q, K, V, U: float64 tensors [T, H, d] (may require grad); rab tables,
-    gamma, beta: float64 tensors or None. Returns Y [T, H*d] and O [T, H*d]."""
+    gamma, beta: float64 tensors or None. Returns Y [T, H*d] and O [T, H*d].
+    time_filter: the candidate block's view of the causal block is cut down to
+    the keys with an earlier timestamp."""
     T = Q.shape[0]
     D = H * d
     outs = []
@@ -52,6 +55,10 @@ def forward(offsets, Q, K, V, U, *, H, d, prefix_len=None, cand_len=None, ts=Non
         if L == 0:
             continue
         mask = block_mask(L, P, C)
+        if time_filter:
+            E = L - C
+            t = torch.as_tensor(ts[s:e], dtype=torch.int64)
+            mask[E:, P:E] &= t[None, P:E] < t[E:, None]
         bias = torch.zeros(L, L, dtype=torch.float64)
         if rab_p is not None:
             pos = positions(L, C)

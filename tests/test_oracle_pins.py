@@ -128,13 +128,14 @@ def _dense_opts(p):
                 rab_t=None if p.rab_t is None else torch.tensor(p.rab_t, dtype=torch.float64),
                 n_max=float(p.n_max), norm=p.norm, eps=p.eps, group=p.group,
                 gamma=None if p.gamma is None else torch.tensor(p.gamma, dtype=torch.float64),
-                beta=None if p.beta is None else torch.tensor(p.beta, dtype=torch.float64))
+                beta=None if p.beta is None else torch.tensor(p.beta, dtype=torch.float64),
+                time_filter=p.time_filter)
 
 
 def _oracle_opts(p):
     return dict(H=p.H, d=p.d, prefix_len=p.prefix_len, cand_len=p.cand_len, ts=p.ts, rab_p=p.rab_p,
                 rab_t=p.rab_t, n_max=p.n_max, norm=p.norm, eps=p.eps, group=p.group,
-                n_groups=p.n_groups, gamma=p.gamma, beta=p.beta)
+                n_groups=p.n_groups, gamma=p.gamma, beta=p.beta, time_filter=p.time_filter)
 
 
 def _small_problems():
@@ -222,13 +223,22 @@ def _mf_oracle(oracle_mod, mf, cand_rows=None, cand_offsets=None):
     return oracle_mod.mfalcon(mf.hist_offsets, mf.cand_offsets if cand_offsets is None else cand_offsets,
                               f(mf.K_cache), f(mf.V_cache), f(mf.Qc)[sel], f(mf.Kc)[sel], f(mf.Vc)[sel],
                               f(mf.Uc)[sel], H=mf.H, d=mf.d, hist_ts=mf.hist_ts, cand_ts=cts,
-                              rab_p=mf.rab_p, rab_t=mf.rab_t, n_max=mf.n_max, norm=mf.norm, eps=mf.eps)
+                              rab_p=mf.rab_p, rab_t=mf.rab_t, n_max=mf.n_max, norm=mf.norm, eps=mf.eps,
+                              time_filter=mf.time_filter)
 
 
-def test_mfalcon_cached_equals_full_pass(oracle_mod):
+@pytest.mark.parametrize("time_filter", [False, True])
+def test_mfalcon_cached_equals_full_pass(oracle_mod, time_filter):
     """Scoring against cached history K/V equals the candidate rows of one
     full pass over [history | candidates] with the candidate mask."""
     mf = _mf_small()
+    if time_filter:
+        # candidate times among the history times, so the filter bites
+        rng = np.random.default_rng(5)
+        for b in range(mf.B):
+            hs, he, cs, ce = mf.hist_offsets[b], mf.hist_offsets[b + 1], mf.cand_offsets[b], mf.cand_offsets[b + 1]
+            mf.cand_ts[cs:ce] = mf.hist_ts[rng.integers(hs, he, size=ce - cs)] + rng.integers(0, 2, size=ce - cs)
+        mf.time_filter = True
     got = _mf_oracle(oracle_mod, mf)
     ho, co = mf.hist_offsets, mf.cand_offsets
     f = lambda t: t.double().numpy()
@@ -245,7 +255,8 @@ def test_mfalcon_cached_equals_full_pass(oracle_mod):
     off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     full = oracle_mod.fwd(off, np.concatenate(Qs), np.concatenate(Ks), np.concatenate(Vs),
                           np.concatenate(Us), H=mf.H, d=mf.d, cand_len=cand, ts=np.concatenate(ts),
-                          rab_p=mf.rab_p, rab_t=mf.rab_t, n_max=mf.n_max, norm=mf.norm, eps=mf.eps)
+                          rab_p=mf.rab_p, rab_t=mf.rab_t, n_max=mf.n_max, norm=mf.norm, eps=mf.eps,
+                          time_filter=time_filter)
     rows = np.concatenate([np.arange(off[b + 1] - cand[b], off[b + 1]) for b in range(mf.B)])
     np.testing.assert_array_equal(got["Y"], full["Y"][rows])
     np.testing.assert_array_equal(got["O"], full["O"][rows])
@@ -472,3 +483,122 @@ def test_rab_gradient_absolute_mass(oracle_mod, p):
     z = oracle_mod.bwd(p.offsets, p.Q.numpy(), p.K.numpy(), p.V.numpy(), p.U.numpy(),
                        np.zeros_like(p.dY.numpy()), **_oracle_opts(p))
     assert np.all(z["drab_p_abs"] == 0) and np.all(z["drab_t_abs"] == 0)
+
+
+# ------------------------------------------------- MTGR timestamp filter
+
+def _filter_problems():
+    """Hybrid-mask problems whose candidates carry times interleaved with the
+    real-time tokens' times, with the timestamp filter on."""
+    L = np.array([14, 20, 9, 12])
+    P = np.array([3, 5, 0, 4]); C = np.array([5, 6, 4, 0])
+    a = synth.custom("tf_ln", L, H=2, d=4, dtype=torch.float32, wid=61, std=0.7, n_max=2,
+                     norm=synth.NORM_LN, prefix_len=P, cand_len=C, n_pos=8, n_tb=6, rab_std=0.4,
+                     gamma_std=0.3, beta_std=0.3, with_dy=True)
+    b = synth.custom("tf_norab", L, H=1, d=8, dtype=torch.float32, wid=62, std=0.7, n_max=1,
+                     norm=synth.NORM_NONE, prefix_len=P, cand_len=C, with_dy=True)
+    out = []
+    for p, seed in ((a, 71), (b, 72)):
+        synth.interleave_candidate_times(p, seed)
+        p.time_filter = True
+        out.append(p)
+    return out
+
+
+def test_interleaved_times_exercise_the_filter():
+    """The fixtures have candidates that see some real-time tokens and not
+    others, including equal timestamps."""
+    for p in _filter_problems():
+        seen = hidden = equal = 0
+        for b in range(p.B):
+            s = int(p.offsets[b]); L = int(p.lengths[b])
+            P, C = int(p.prefix_len[b]), int(p.cand_len[b])
+            E = L - C
+            for i in range(E, L):
+                for j in range(P, E):
+                    if p.ts[s + j] < p.ts[s + i]:
+                        seen += 1
+                    else:
+                        hidden += 1
+                    equal += int(p.ts[s + j] == p.ts[s + i])
+        assert seen > 0 and hidden > 0 and equal > 0
+
+
+@pytest.mark.parametrize("p", _filter_problems(), ids=lambda p: p.name)
+def test_time_filter_forward_matches_torch_dense(oracle_mod, p):
+    Q, K, V, U = _torch_inputs(p)
+    Yd, Od = dense_torch.forward(p.offsets, Q, K, V, U, **_dense_opts(p))
+    r = oracle_mod.fwd(p.offsets, p.Q.double().numpy(), p.K.double().numpy(), p.V.double().numpy(),
+                       p.U.double().numpy(), **_oracle_opts(p))
+    np.testing.assert_allclose(r["O"], Od.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(r["Y"], Yd.numpy(), rtol=1e-10, atol=1e-12)
+    # and the filter changes the candidate rows
+    q = dict(_oracle_opts(p), time_filter=False)
+    r0 = oracle_mod.fwd(p.offsets, p.Q.double().numpy(), p.K.double().numpy(), p.V.double().numpy(),
+                        p.U.double().numpy(), **q)
+    assert not np.array_equal(r0["O"], r["O"])
+
+
+@pytest.mark.parametrize("p", _filter_problems(), ids=lambda p: p.name)
+def test_time_filter_backward_matches_torch_autograd(oracle_mod, p):
+    Q, K, V, U = (t.requires_grad_(True) for t in _torch_inputs(p))
+    opts = _dense_opts(p)
+    params = [opts[k] for k in ("rab_p", "rab_t", "gamma", "beta") if opts[k] is not None]
+    for t in params:
+        t.requires_grad_(True)
+    Y, _ = dense_torch.forward(p.offsets, Q, K, V, U, **opts)
+    (Y * p.dY.double()).sum().backward()
+    r = oracle_mod.bwd(p.offsets, p.Q.numpy(), p.K.numpy(), p.V.numpy(), p.U.numpy(), p.dY.numpy(),
+                       **_oracle_opts(p))
+    T, D = p.T, p.H * p.d
+    for name, t in (("dQ", Q), ("dK", K), ("dV", V), ("dU", U)):
+        np.testing.assert_allclose(r[name], t.grad.reshape(T, D).numpy(), rtol=1e-9, atol=1e-12, err_msg=name)
+    for name, key in (("drab_p", "rab_p"), ("drab_t", "rab_t"), ("dgamma", "gamma"), ("dbeta", "beta")):
+        if opts[key] is not None:
+            np.testing.assert_allclose(r[name], opts[key].grad.numpy(), rtol=1e-9, atol=1e-12, err_msg=name)
+
+
+def test_time_filter_hides_exactly_the_later_keys(oracle_mod):
+    """Perturbing a real-time key leaves a candidate row bit-identical exactly
+    when the key is not strictly earlier than the candidate (equal times hide
+    the key), and changes it otherwise."""
+    p = _filter_problems()[1]
+    base = oracle_mod.fwd(p.offsets, p.Q.numpy(), p.K.numpy(), p.V.numpy(), p.U.numpy(), **_oracle_opts(p))
+    for b in range(p.B):
+        s = int(p.offsets[b]); L = int(p.lengths[b])
+        P, C = int(p.prefix_len[b]), int(p.cand_len[b])
+        E = L - C
+        for j in range(P, E):
+            V2 = p.V.numpy().copy()
+            V2[s + j] += 5.0
+            r = oracle_mod.fwd(p.offsets, p.Q.numpy(), p.K.numpy(), V2, p.U.numpy(), **_oracle_opts(p))
+            for i in range(E, L):
+                same = np.array_equal(r["O"][s + i], base["O"][s + i])
+                assert same == (not p.ts[s + j] < p.ts[s + i]), (b, i, j)
+
+
+def test_time_filter_is_inert_when_real_time_is_earlier(oracle_mod):
+    """Timestamps increasing along each sequence (candidates last): every
+    real-time token is earlier than every candidate unless their times tie,
+    so with strictly increasing times the filter changes nothing."""
+    L = np.array([11, 15]); P = np.array([2, 3]); C = np.array([3, 4])
+    p = synth.custom("tf_inert", L, H=2, d=4, dtype=torch.float32, wid=63, std=0.7, n_max=2,
+                     norm=synth.NORM_LN, prefix_len=P, cand_len=C, n_pos=8, n_tb=6)
+    p.ts = np.concatenate([1_000_000 + 10 * np.arange(l) for l in L]).astype(np.int64)
+    a = oracle_mod.fwd(p.offsets, p.Q.numpy(), p.K.numpy(), p.V.numpy(), p.U.numpy(), **_oracle_opts(p))
+    p.time_filter = True
+    b = oracle_mod.fwd(p.offsets, p.Q.numpy(), p.K.numpy(), p.V.numpy(), p.U.numpy(), **_oracle_opts(p))
+    np.testing.assert_array_equal(a["Y"], b["Y"])
+
+
+def test_time_filter_schedule_marks_candidate_causal_tiles_partial(oracle_mod):
+    """With the filter a tile holding (candidate row, causal key) pairs is
+    present and never full; without it such a tile can be full."""
+    L, P, C, BN = 40, 8, 16, 8
+    E = L - C
+    plain = oracle_mod.classify_tiles(L, P, C, E, C, BN, L // BN)
+    filt = oracle_mod.classify_tiles(L, P, C, E, C, BN, L // BN, time_filter=True)
+    # keys [0, 8) prefix: full either way; [8, 24) causal: full -> partial; the
+    # candidate tail carries only self pairs, which are added outside the tiles
+    assert list(plain) == [2, 2, 2, 0, 0]
+    assert list(filt) == [2, 1, 1, 0, 0]
