@@ -15,6 +15,7 @@ HSTU_OK, HSTU_ERR_INVALID_ARG, HSTU_ERR_UNSUPPORTED, HSTU_ERR_WORKSPACE, HSTU_ER
 HSTU_BF16, HSTU_F32 = 0, 1
 HSTU_NORM_NONE, HSTU_NORM_LN, HSTU_NORM_GLN = 0, 1, 2
 HSTU_OP_FWD, HSTU_OP_BWD, HSTU_OP_MFALCON = 0, 1, 2
+HSTU_MASK_CAND_TIME_FILTER = 1
 (HSTU_KERNEL_SCHED, HSTU_KERNEL_ATTN_FWD, HSTU_KERNEL_NORM_FWD, HSTU_KERNEL_NORM_BWD, HSTU_KERNEL_ATTN_BWD_DQ,
  HSTU_KERNEL_AUX, HSTU_KERNEL_ATTN_BWD_DKDV) = range(7)
 HSTU_DEV_BAD_OFFSETS, HSTU_DEV_BAD_SEGMENTS, HSTU_DEV_BAD_GROUP, HSTU_DEV_TOO_LONG = 1, 2, 4, 8
@@ -37,7 +38,7 @@ class Problem(ctypes.Structure):
         ("n_pos", ctypes.c_int32), ("n_tb", ctypes.c_int32),
         ("norm", ctypes.c_int32), ("eps", ctypes.c_float),
         ("token_group", _vp),
-        ("n_groups", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("n_groups", ctypes.c_int32), ("mask_flags", ctypes.c_int32),
         ("gamma", _vp), ("beta", _vp),
     ]
 

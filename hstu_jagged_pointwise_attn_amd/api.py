@@ -57,8 +57,9 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 def problem(offsets: torch.Tensor, *, H: int, d: int, dtype: torch.dtype, total_tokens: int,
             max_len: int, n_max: int, prefix_len=None, cand_len=None, timestamps=None, rab_p=None,
             rab_t=None, norm=HSTU_NORM_LN, eps=1e-5, token_group=None, n_groups=1, gamma=None,
-            beta=None):
-    """Build the hstu_problem_t of a jagged batch (device tensors; host scalars)."""
+            beta=None, time_filter=False):
+    """Build the hstu_problem_t of a jagged batch (device tensors; host scalars).
+    time_filter sets HSTU_MASK_CAND_TIME_FILTER."""
     dev = offsets.device
     B = offsets.numel() - 1
     _need(offsets, "offsets", torch.int32, dev)
@@ -84,6 +85,7 @@ def problem(offsets: torch.Tensor, *, H: int, d: int, dtype: torch.dtype, total_
     p.norm, p.eps = int(norm), float(eps)
     p.token_group, p.n_groups = _ptr(token_group), int(n_groups)
     p.gamma, p.beta = _ptr(gamma), _ptr(beta)
+    p.mask_flags = L.HSTU_MASK_CAND_TIME_FILTER if time_filter else 0
     # keep the tensors alive as long as the struct
     p._keep = (offsets, prefix_len, cand_len, timestamps, rab_p, rab_t, token_group, gamma, beta)
     return p

@@ -160,6 +160,10 @@ hstu_status_t check_problem(const hstu_problem_t *p, int op) {
     if (p->n_groups < 1 || p->n_groups > 255)
       return fail(HSTU_ERR_INVALID_ARG, "n_groups = %d not in [1, 255]", p->n_groups);
   }
+  if (p->mask_flags & ~HSTU_MASK_CAND_TIME_FILTER)
+    return fail(HSTU_ERR_INVALID_ARG, "mask_flags = %d has unknown bits", p->mask_flags);
+  if ((p->mask_flags & HSTU_MASK_CAND_TIME_FILTER) && !p->timestamps)
+    return fail(HSTU_ERR_INVALID_ARG, "the candidate timestamp filter needs timestamps");
   const long long D = (long long)p->H * p->d;
   const long long dmax = p->dtype == HSTU_BF16 ? 4096 : 2048;
   if (D > dmax) return fail(HSTU_ERR_UNSUPPORTED, "H*d = %lld > %lld", D, dmax);
@@ -199,6 +203,7 @@ void fill_sched(SchedArgs &s, const hstu_problem_t *p, int op, const Layout &L, 
   s.BM = t.BM;
   s.BN = t.BN;
   s.microbatch = microbatch;
+  s.time_filter = (p->mask_flags & HSTU_MASK_CAND_TIME_FILTER) ? 1 : 0;
   s.max_tiles = (int)L.max_tiles;
   s.hdr = at<int>(ws, L.hdr);
   s.desc = at<SeqDesc>(ws, L.desc);
@@ -233,11 +238,14 @@ hstu_status_t run_forward(const hstu_problem_t *p, int op, const Layout &L, void
   FwdArgs f;
   std::memset(&f, 0, sizeof f);
   f.Q = Q; f.K = K; f.V = V; f.Kself = Kself; f.Vself = Vself; f.O = O;
-  const bool use_t = p->rab_t && ts_q && ts_kv;
+  // Timestamps reach the kernel when rab_t or the candidate filter uses them.
+  const bool tf = (p->mask_flags & HSTU_MASK_CAND_TIME_FILTER) != 0;
+  const bool use_t = (p->rab_t || tf) && ts_q && ts_kv;
   f.ts_q = use_t ? ts_q : nullptr;
   f.ts_kv = use_t ? ts_kv : nullptr;
   f.rab_p = p->rab_p;
-  f.rab_t = use_t ? p->rab_t : nullptr;
+  f.rab_t = (use_t && p->rab_t) ? p->rab_t : nullptr;
+  f.tfilt = (tf && use_t) ? 1 : 0;
   f.n_pos = p->n_pos;
   f.n_tb = p->n_tb;
   f.inv_nmax = 1.0f / (float)p->n_max;
@@ -374,9 +382,11 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
     return fail(HSTU_ERR_INVALID_ARG, "Q/K/V/U/O/dY/dQ/dK/dV/dU must not be NULL");
   if (p->norm != HSTU_NORM_NONE && T > 0 && (!mean || !rstd))
     return fail(HSTU_ERR_INVALID_ARG, "mean/rstd must not be NULL with a norm");
-  const bool use_t = p->rab_t && p->timestamps;
+  const bool tf = (p->mask_flags & HSTU_MASK_CAND_TIME_FILTER) != 0;
+  const bool use_rt = p->rab_t && p->timestamps;            // the rab_t term is on
+  const bool use_t = (p->rab_t || tf) && p->timestamps;     // kernels need timestamps
   if (p->rab_p && !d_rab_p) return fail(HSTU_ERR_INVALID_ARG, "d_rab_p must not be NULL when rab_p is given");
-  if (use_t && !d_rab_t) return fail(HSTU_ERR_INVALID_ARG, "d_rab_t must not be NULL when rab_t is used");
+  if (use_rt && !d_rab_t) return fail(HSTU_ERR_INVALID_ARG, "d_rab_t must not be NULL when rab_t is used");
   Layout L = layout(p, HSTU_OP_BWD, 0, 0);
   s = check_ws(ws, ws_bytes, L.total);
   if (s) return s;
@@ -407,8 +417,7 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
   {
     Timed t_(HSTU_KERNEL_AUX, st);
     if (p->rab_p) HIP_TRY(launch_fill_f32(d_rab_p, p->n_pos, 0.f, st), "fill");
-    if (use_t) HIP_TRY(launch_fill_f32(d_rab_t, p->n_tb, 0.f, st), "fill");
-    else if (p->rab_t && d_rab_t) HIP_TRY(launch_fill_f32(d_rab_t, p->n_tb, 0.f, st), "fill");
+    if (p->rab_t && d_rab_t) HIP_TRY(launch_fill_f32(d_rab_t, p->n_tb, 0.f, st), "fill");
     if (dg) HIP_TRY(launch_fill_f32(dg, (long long)G * D, 0.f, st), "fill");
     if (db) HIP_TRY(launch_fill_f32(db, (long long)G * D, 0.f, st), "fill");
   }
@@ -435,7 +444,8 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
   b.dQ = dQ; b.dK = dK; b.dV = dV;
   b.ts = use_t ? p->timestamps : nullptr;
   b.rab_p = p->rab_p;
-  b.rab_t = use_t ? p->rab_t : nullptr;
+  b.rab_t = use_rt ? p->rab_t : nullptr;
+  b.tfilt = (tf && use_t) ? 1 : 0;
   b.drab_p = d_rab_p;
   b.drab_t = d_rab_t;
   b.n_pos = p->n_pos;

@@ -58,8 +58,9 @@ struct PairPrefetch {
 // tiles. Diagonals that no later key tile can touch are flushed to global
 // memory after every tile.
 // ---------------------------------------------------------------------------
-template <int D, bool USE_P, bool USE_T>
+template <int D, bool USE_P, bool USE_T, bool TF>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  static_assert(!TF || USE_T, "the timestamp filter needs the timestamps");
   constexpr int BM = kFwdBM, BN = 32, NWV = 4;
   constexpr int KS = D / 32, ND = D / 16;
   constexpr int ST = D + 16;           // LDS row stride of K, V and the staged dQ
@@ -100,7 +101,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int fil = fi0 + nrows - 1;
   const int kv_limit = frame_hi(fil, sd.P, sd.E);
   const int nk = (kv_limit + BN - 1) / BN;       // key tiles of 32
-  const int nf = frame_hi(fi0, sd.P, sd.E) / BN;  // the first nf are fully visible
+  // the first nf are fully visible (a candidate under the timestamp filter is
+  // sure to see only the prefix)
+  const int nf = (TF && fil >= sd.E) ? min(frame_hi(fi0, sd.P, sd.E), sd.P) / BN
+                                     : frame_hi(fi0, sd.P, sd.E) / BN;
   const int pos_max = fil < sd.E ? fil : sd.E;
   const long long t_ref = USE_T ? a.ts[sd.q_base + row0] : 0;
 
@@ -108,10 +112,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     s_bad = 0;
     self_acc = 0.f;
   }
+  const bool has_rt = a.rab_t != nullptr;  // USE_T without a table: times for the filter only
   if (USE_T && tid < 33) {
     const int c = tid - 1;
     const int bkt = c < 0 ? 0 : 31 - c;
-    t2tab[tid] = a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1];
+    t2tab[tid] = has_rt ? a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1] : 0.f;
     hts[tid] = 0.f;
     if (tid < 32) htb[tid] = 0.f;
   }
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int wrow0 = min(w * 32, nrows - 1);
   const int pos_w0 = min(fi0 + wrow0, sd.E);
   int hi_r[2], vb_r[2], sh_r[2];
-  bool ok_r[2];
+  bool ok_r[2], tfr[2];
   unsigned tq[2] = {0u, 0u};
   bool bad_t = false;
   bf16x8 qf[2][KS], dof[2][KS];
@@ -140,6 +145,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     hi_r[nq] = ok_r[nq] ? frame_hi(fi, sd.P, sd.E) : 0;
     vb_r[nq] = pos_max - pos_r + lg * 4;
     sh_r[nq] = pos_r - pos_w0;  // 0..31 for the rows of this wave
+    tfr[nq] = TF && ok_r[nq] && fi >= sd.E;
     if (USE_T) {
       const long long dq = a.ts[sd.q_base + row0 + crow] - t_ref;
       bad_t |= dq < -2147483648LL || dq > 2147483647LL;
@@ -162,6 +168,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     qmin = __builtin_amdgcn_readfirstlane(wave_min_u32(min(tq[0], tq[1])));
     qmax = __builtin_amdgcn_readfirstlane(wave_max_u32(max(tq[0], tq[1])));
   }
+  // Whether some row of this wave is a candidate under the timestamp filter.
+  const bool wave_tf = TF && __builtin_amdgcn_readfirstlane(
+      (int)wave_max_u32((tfr[0] || tfr[1]) ? 1u : 0u)) != 0;
 
   PairPrefetch<NCH> pf;
   pf.r = 0.f;
@@ -281,7 +290,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       }
       const int blo = bucket_u32(dlo, a.n_tb), bhi = bucket_u32(dhi, a.n_tb);
       tconst = __builtin_amdgcn_readfirstlane(blo == bhi ? 1 : 0) != 0;
-      tcv = a.rab_t[blo];
+      tcv = has_rt ? a.rab_t[blo] : 0.f;
       tcidx = blo;
     }
 
@@ -290,8 +299,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     // visible; TC: one rab_t bucket for the whole block. On the per-element
     // rab_t path a lane's keys ascend along (mk, i) for each row, so equal
     // buckets come in runs that are merged before they go to the histogram.
-    auto epilogue = [&](auto fullc, auto tconstc) __attribute__((always_inline)) {
+    // TFV: a candidate row under the timestamp filter also needs its key in
+    // the prefix or strictly earlier in time (partial, gathered tiles only).
+    auto epilogue = [&](auto fullc, auto tconstc, auto tfc) __attribute__((always_inline)) {
       constexpr bool FULL = decltype(fullc)::value, TC = decltype(tconstc)::value;
+      constexpr bool TFV = decltype(tfc)::value;
+      static_assert(!TFV || (USE_T && !FULL && !TC), "the filter runs on partial gathered tiles");
+      const int prel = sd.P - (c0 + lg * 4);
       float tsum = 0.f, run_s = 0.f;
       int run_b = -1;
 #pragma unroll
@@ -316,7 +330,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
             }
             const float sg = sigmoid_fast(x);
             float ds = dpt[mk][nq][i] * sg * (1.0f + x * (1.0f - sg));
-            if (!FULL) ds = hirel[nq] > mk * 16 + i ? ds : 0.f;
+            bool vis = hirel[nq] > mk * 16 + i;
+            if (TFV) vis = vis && (!tfr[nq] || prel > mk * 16 + i || tk4[i] < tq[nq]);
+            if (!FULL) ds = vis ? ds : 0.f;
             dsv[i] = ds;
             if (USE_P) skw[(nq * 16 + lr) * SKW + mk * 16 + lg * 4 + i + 31 - sh_r[nq]] = ds;
             if (USE_T) {
@@ -345,12 +361,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       }
       if (USE_T && !TC && run_b >= 0) atomicAdd(&hts[run_b], run_s);
     };
-    if (USE_T && !tconst) {
-      if (full) epilogue(bc<true>(), bc<false>());
-      else epilogue(bc<false>(), bc<false>());
-    } else {
-      if (full) epilogue(bc<true>(), bc<true>());
-      else epilogue(bc<false>(), bc<true>());
+    bool done = false;
+    if constexpr (TF) {
+      if (wave_tf && !full) {
+        epilogue(bc<false>(), bc<false>(), bc<true>());
+        done = true;
+      }
+    }
+    if (!done) {
+      if (USE_T && !tconst) {
+        if (full) epilogue(bc<true>(), bc<false>(), bc<false>());
+        else epilogue(bc<false>(), bc<false>(), bc<false>());
+      } else {
+        if (full) epilogue(bc<true>(), bc<true>(), bc<false>());
+        else epilogue(bc<false>(), bc<true>(), bc<false>());
+      }
     }
     if (USE_P) {
       // column sums of the skewed block = this wave's diagonal sums
@@ -405,7 +430,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   // A candidate's pair with itself (|pos| and |dt| are 0).
   const bool any_cand = fil >= sd.E;
   if (any_cand) {
-    const float bias0 = (USE_P ? a.rab_p[0] : 0.f) + (USE_T ? a.rab_t[0] : 0.f);
+    const float bias0 = (USE_P ? a.rab_p[0] : 0.f) + (USE_T && has_rt ? a.rab_t[0] : 0.f);
     u16 *dK = (u16 *)a.dK, *dV = (u16 *)a.dV;
 #pragma unroll
     for (int nq = 0; nq < 2; ++nq) {
@@ -467,9 +492,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   __syncthreads();
   if (tid == 0 && any_cand) {
     if (USE_P) atomicAdd(a.drab_p, self_acc * a.inv_nmax);
-    if (USE_T) atomicAdd(a.drab_t, self_acc * a.inv_nmax);
+    if (USE_T && has_rt) atomicAdd(a.drab_t, self_acc * a.inv_nmax);
   }
-  if (USE_T && tid < 33) {
+  if (USE_T && has_rt && tid < 33) {
     const float v = hts[tid];
     if (v != 0.f) {
       const int c = tid - 1;
@@ -505,8 +530,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK/dV kernel (key-major): 4 waves x 16 keys, query steps of 64 rows.
 // ---------------------------------------------------------------------------
-template <int D, bool USE_P, bool USE_T>
+template <int D, bool USE_P, bool USE_T, bool TF>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  static_assert(!TF || USE_T, "the timestamp filter needs the timestamps");
   constexpr int BN = kBwdKBN, BM = kBwdKBM;
   constexpr int KS = D / 32, ND = D / 16;
   constexpr int ST = D + 16;           // LDS row stride of the Q and dO tiles
@@ -535,10 +561,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const u16 *Q = (const u16 *)a.Q, *K = (const u16 *)a.K, *V = (const u16 *)a.V;
   const u16 *dO = (const u16 *)a.dO;
 
+  const bool has_rt = a.rab_t != nullptr;  // USE_T without a table: times for the filter only
   if (USE_T && tid < 33) {
     const int c = tid - 1;
     const int bkt = c < 0 ? 0 : 31 - c;
-    t2tab[tid] = a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1];
+    t2tab[tid] = has_rt ? a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1] : 0.f;
   }
 
   // This lane's key (B-operand and C-column layout): k0 + w*16 + lr.
@@ -666,9 +693,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       }
       const int blo = bucket_u32(dlo, a.n_tb), bhi = bucket_u32(dhi, a.n_tb);
       tconst = blo == bhi;
-      tcv = a.rab_t[blo];
+      tcv = has_rt ? a.rab_t[blo] : 0.f;
     }
-    const bool full = fr0 >= rmin_tile;
+    // Under the timestamp filter, candidate rows of this step see the tile's
+    // causal keys by time: such a step is partial and takes the gathered path.
+    const bool tf_step = TF && fr0 + BM > sd.E && k0 + nkeys > sd.P;
+    if (tf_step) tconst = false;
+    const bool full = fr0 >= rmin_tile && !tf_step;
     const int rrel = rmin - (fr0 + lg * 4);  // element (mr, i) visible iff 16 mr + i >= rrel
     bf16x8 pa[2], da[2];
 #pragma unroll
@@ -687,7 +718,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
           const float sg = sigmoid_fast(x);
           float p = x * sg;
           float d = dp[mr][i] * sg * (1.0f + x * (1.0f - sg));
-          if (!full && !(mr * 16 + i >= rrel)) {
+          bool vis = mr * 16 + i >= rrel;
+          if (TF && tf_step) {
+            const int row = fr0 + lg * 4 + mr * 16 + i;
+            vis = vis && (row < sd.E || key < sd.P || tk < tr4[i]);
+          }
+          if (!full && !vis) {
             p = 0.f;
             d = 0.f;
           }
@@ -765,12 +801,13 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lrow = tid >> 2, part = tid & 3;
   const float *Q = (const float *)a.Q, *K = (const float *)a.K, *V = (const float *)a.V;
   const float *dO = (const float *)a.dO;
-  const bool use_p = a.rab_p != nullptr, use_t = a.rab_t != nullptr;
+  const bool use_p = a.rab_p != nullptr, use_t = a.ts != nullptr, has_rt = a.rab_t != nullptr;
   const bool ok = lrow < nrows;
   const int fi = sd.q_frame0 + row0 + lrow;
   const int hi = ok ? frame_hi(fi, sd.P, sd.E) : 0;
   const int pos = fi < sd.E ? fi : sd.E;
   const long long tq = (use_t && ok) ? a.ts[sd.q_base + row0 + lrow] : 0;
+  const bool tfr = use_t && a.tfilt && ok && fi >= sd.E;  // candidate under the timestamp filter
   const long long roff = (long long)(sd.q_base + row0 + lrow) * ld + h * D + part * DP;
   float q[DP], g[DP], dq[DP];
 #pragma unroll
@@ -810,18 +847,18 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a) {
         pidx = pos_bucket(pos - j, a.n_pos);
         s += a.rab_p[pidx];
       }
-      if (use_t) {
+      if (use_t && has_rt) {
         tidx = time_bucket(tq - tsk[jl], a.n_tb);
         s += a.rab_t[tidx];
       }
-      if (j < hi) {
+      if (j < hi && (!tfr || j < sd.P || tsk[jl] < tq)) {
         const float sg = 1.0f / (1.0f + expf(-s));
         const float ds = da * sg * (1.0f + s * (1.0f - sg));
 #pragma unroll
         for (int c = 0; c < DP; ++c) dq[c] = fmaf(ds, Ks[jl][part * DP + c], dq[c]);
         if (part == 0) {
           if (use_p) atomicAdd(a.drab_p + pidx, ds * a.inv_nmax);
-          if (use_t) atomicAdd(a.drab_t + tidx, ds * a.inv_nmax);
+          if (use_t && has_rt) atomicAdd(a.drab_t + tidx, ds * a.inv_nmax);
         }
       }
     }
@@ -838,7 +875,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a) {
     s += __shfl_xor(s, 2, 64);
     da += __shfl_xor(da, 1, 64);
     da += __shfl_xor(da, 2, 64);
-    s += (use_p ? a.rab_p[0] : 0.f) + (use_t ? a.rab_t[0] : 0.f);
+    s += (use_p ? a.rab_p[0] : 0.f) + (use_t && has_rt ? a.rab_t[0] : 0.f);
     const float sg = 1.0f / (1.0f + expf(-s));
     const float ds = da * sg * (1.0f + s * (1.0f - sg));
     float *dK = (float *)a.dK, *dV = (float *)a.dV;
@@ -850,7 +887,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a) {
     }
     if (part == 0) {
       if (use_p) atomicAdd(a.drab_p, ds * a.inv_nmax);
-      if (use_t) atomicAdd(a.drab_t, ds * a.inv_nmax);
+      if (use_t && has_rt) atomicAdd(a.drab_t, ds * a.inv_nmax);
     }
   }
   if (ok) {
@@ -877,7 +914,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lkey = tid >> 2, part = tid & 3;
   const float *Q = (const float *)a.Q, *K = (const float *)a.K, *V = (const float *)a.V;
   const float *dO = (const float *)a.dO;
-  const bool use_p = a.rab_p != nullptr, use_t = a.rab_t != nullptr;
+  const bool use_p = a.rab_p != nullptr, use_t = a.ts != nullptr, has_rt = a.rab_t != nullptr;
   const bool kok = lkey < nkeys;
   const int key = k0 + (kok ? lkey : 0);
   const int rmin = kok ? (key < sd.P ? 0 : key) : 0x7fffffff;
@@ -916,8 +953,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a) {
       da += __shfl_xor(da, 1, 64);
       da += __shfl_xor(da, 2, 64);
       if (use_p) s += a.rab_p[pos_bucket((i < sd.E ? i : sd.E) - key, a.n_pos)];
-      if (use_t) s += a.rab_t[time_bucket(tsr[rl] - tk, a.n_tb)];
-      if (i >= rmin) {
+      if (use_t && has_rt) s += a.rab_t[time_bucket(tsr[rl] - tk, a.n_tb)];
+      // under the timestamp filter a candidate row sees a causal key only if later
+      const bool tf_ok = !(use_t && a.tfilt && i >= sd.E && key >= sd.P) || tk < tsr[rl];
+      if (i >= rmin && tf_ok) {
         const float sg = 1.0f / (1.0f + expf(-s));
         const float p = s * sg;
         const float ds = da * sg * (1.0f + s * (1.0f - sg));
@@ -944,11 +983,20 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a) {
 #define HSTU_BWD_BF16_LAUNCH(KERNEL, NTHR)                                                      \
   template <int D>                                                                              \
   hipError_t launch_##KERNEL##_d(const BwdArgs &a, hipStream_t s) {                             \
-    const bool p = a.rab_p != nullptr, t = a.rab_t != nullptr;                                  \
-    if (p && t) hipLaunchKernelGGL((KERNEL<D, true, true>), dim3(a.units), dim3(NTHR), 0, s, a); \
-    else if (p) hipLaunchKernelGGL((KERNEL<D, true, false>), dim3(a.units), dim3(NTHR), 0, s, a); \
-    else if (t) hipLaunchKernelGGL((KERNEL<D, false, true>), dim3(a.units), dim3(NTHR), 0, s, a); \
-    else hipLaunchKernelGGL((KERNEL<D, false, false>), dim3(a.units), dim3(NTHR), 0, s, a);     \
+    const bool p = a.rab_p != nullptr, t = a.ts != nullptr;                                     \
+    const dim3 g(a.units), b(NTHR);                                                             \
+    if (a.tfilt) {                                                                              \
+      if (p) hipLaunchKernelGGL((KERNEL<D, true, true, true>), g, b, 0, s, a);                  \
+      else hipLaunchKernelGGL((KERNEL<D, false, true, true>), g, b, 0, s, a);                   \
+    } else if (p && t) {                                                                        \
+      hipLaunchKernelGGL((KERNEL<D, true, true, false>), g, b, 0, s, a);                        \
+    } else if (p) {                                                                             \
+      hipLaunchKernelGGL((KERNEL<D, true, false, false>), g, b, 0, s, a);                       \
+    } else if (t) {                                                                             \
+      hipLaunchKernelGGL((KERNEL<D, false, true, false>), g, b, 0, s, a);                       \
+    } else {                                                                                    \
+      hipLaunchKernelGGL((KERNEL<D, false, false, false>), g, b, 0, s, a);                      \
+    }                                                                                           \
     return hipGetLastError();                                                                   \
   }
 

@@ -93,11 +93,16 @@ __device__ __forceinline__ void fwd_store_tile(const TilePrefetch<NCH> &pf, int 
 // P V: pa[nq][kk] holds keys kk*32 + {lg*4 + 0..3, 16 + lg*4 + 0..3}.
 // FULL: every pair of the tile is visible. TCONST: rab_t is the scalar tcv
 // for the whole block, else it is gathered per element.
-template <bool FULL, bool USE_T, bool TCONST>
+// TF (timestamp filter, partial tiles with the gathered rab_t path only): a
+// row flagged in tfr also needs its key inside the prefix (prel = P - first
+// key of this lane's group) or strictly earlier in time.
+template <bool FULL, bool USE_T, bool TCONST, bool TF = false>
 __device__ __forceinline__ void fwd_epilogue(const f32x4 (&st)[4][2], bf16x8 (&pa)[2][2],
                                              const int (&hirel)[2], const unsigned (&tq)[2],
                                              const unsigned *tkb, const float *t2tab, float tcv,
-                                             int lg) {
+                                             int lg, const bool (&tfr)[2] = {false, false},
+                                             int prel = 0) {
+  static_assert(!TF || (USE_T && !FULL && !TCONST), "the filter runs on partial gathered tiles");
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     u32x4 w[2];
@@ -114,7 +119,9 @@ __device__ __forceinline__ void fwd_epilogue(const f32x4 (&st)[4][2], bf16x8 (&p
           float x = st[mk][nq][i];
           if (USE_T) x += TCONST ? tcv : t2tab[ffbh_u32(absdiff_u32(tq[nq], tk4[i])) + 1];
           p[i] = silu_fast(x);
-          if (!FULL) p[i] = hirel[nq] > mk * 16 + i ? p[i] : 0.f;
+          bool vis = hirel[nq] > mk * 16 + i;
+          if (TF) vis = vis && (!tfr[nq] || prel > mk * 16 + i || tk4[i] < tq[nq]);
+          if (!FULL) p[i] = vis ? p[i] : 0.f;
         }
         w[nq][h2 * 2] = pack_bf16x2(p[0], p[1]);
         w[nq][h2 * 2 + 1] = pack_bf16x2(p[2], p[3]);
@@ -136,8 +143,9 @@ __device__ __forceinline__ void fwd_epilogue(const f32x4 (&st)[4][2], bf16x8 (&p
 // of a distant key tile rarely changes); then rab_t is one scalar for the
 // whole block, else it is gathered per element from a 33-entry LDS table
 // indexed by ffbh(|dt|) + 1.
-template <int D, bool USE_P, bool USE_T>
+template <int D, bool USE_P, bool USE_T, bool TF>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
+  static_assert(!TF || USE_T, "the timestamp filter needs the timestamps");
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int KS = D / 32;          // k-steps of the K Q^T contraction
   constexpr int ND = D / 16;          // 16-column blocks of O
@@ -175,18 +183,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int pos_max = fil < sd.E ? fil : sd.E;
   const long long t_ref = USE_T ? a.ts_q[sd.q_base + row0] : 0;
 
+  // With USE_T the kernel has timestamps; the rab_t table may still be
+  // absent when they serve only the timestamp filter (then it adds zero).
+  const bool has_rt = a.rab_t != nullptr;
   if (tid == 0) s_bad = 0;
   if (USE_T && tid < 33) {
     const int c = tid - 1;
     const int bkt = c < 0 ? 0 : 31 - c;
-    t2tab[tid] = a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1];
+    t2tab[tid] = has_rt ? a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1] : 0.f;
   }
   __syncthreads();
 
   // This lane's query rows in the S^T layout: local rows w*32 + nq*16 + lr.
   int hi_r[2], vb_r[2];
   unsigned tq_r[2] = {0u, 0u};
-  bool ok_r[2];
+  bool ok_r[2], tfr[2];
   bf16x8 qf[2][KS];
   bool bad_t = false;
 #pragma unroll
@@ -197,6 +208,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     const int fi = fi0 + crow;
     hi_r[nq] = ok_r[nq] ? frame_hi(fi, sd.P, sd.E) : 0;
     vb_r[nq] = pos_max - (fi < sd.E ? fi : sd.E) + lg * 4;
+    tfr[nq] = TF && ok_r[nq] && fi >= sd.E;
     if (USE_T) {
       const long long dq = a.ts_q[sd.q_base + row0 + crow] - t_ref;
       bad_t |= dq < -2147483648LL || dq > 2147483647LL;
@@ -220,6 +232,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   // row) is skipped by this wave; its pairs are all masked.
   const int wave_hi = __builtin_amdgcn_readfirstlane(
       (int)wave_max_u32((unsigned)max(hi_r[0], hi_r[1])));
+  // Whether some row of this wave is a candidate under the timestamp filter.
+  const bool wave_tf = TF && __builtin_amdgcn_readfirstlane(
+      (int)wave_max_u32((tfr[0] || tfr[1]) ? 1u : 0u)) != 0;
 
   // Global -> register prefetch of one key tile, and register -> LDS store.
   TilePrefetch<NCH> pf;
@@ -315,11 +330,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       }
       const int blo = bucket_u32(dlo, a.n_tb), bhi = bucket_u32(dhi, a.n_tb);
       tconst = blo == bhi;
-      tcv = a.rab_t[blo];
+      tcv = has_rt ? a.rab_t[blo] : 0.f;
     }
 
     const unsigned *tkb = tkey + b * (USE_T ? BN : 0);
     if (wave_hi > c0) {
+      if constexpr (TF) {
+        if (wave_tf && !full) {
+          fwd_epilogue<false, USE_T, false, true>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg, tfr,
+                                                  sd.P - (c0 + lg * 4));
+          pv(b);
+          goto tile_done;
+        }
+      }
       if (USE_T && !tconst) {
         if (full) fwd_epilogue<true, USE_T, false>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
         else fwd_epilogue<false, USE_T, false>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
@@ -329,6 +352,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       }
       pv(b);
     }
+  tile_done:
     if (kt + 1 < nk) {
       fwd_store_tile<D, BN, USE_P, USE_T>(pf, tid, Ks + (b ^ 1) * BN * KST, Vs + (b ^ 1) * BN * VST,
                                           rabw + (b ^ 1) * (USE_P ? WIN : 0), tkey + (b ^ 1) * (USE_T ? BN : 0),
@@ -343,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const bool any_cand = fil >= sd.E;
   if (any_cand) {
     const u16 *Ksf = (const u16 *)a.Kself, *Vsf = (const u16 *)a.Vself;
-    const float bias0 = (USE_P ? a.rab_p[0] : 0.f) + (USE_T ? a.rab_t[0] : 0.f);
+    const float bias0 = (USE_P ? a.rab_p[0] : 0.f) + (USE_T && has_rt ? a.rab_t[0] : 0.f);
     float as[2];
 #pragma unroll
     for (int nq = 0; nq < 2; ++nq) {
@@ -427,13 +451,14 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   const long long ld = (long long)H * D;
   const int tid = threadIdx.x, lrow = tid >> 2, part = tid & 3;
   const float *Q = (const float *)a.Q, *K = (const float *)a.K, *V = (const float *)a.V;
-  const bool use_p = a.rab_p != nullptr, use_t = a.rab_t != nullptr;
+  const bool use_p = a.rab_p != nullptr, use_t = a.ts_q != nullptr, has_rt = a.rab_t != nullptr;
 
   const bool ok = lrow < nrows;
   const int fi = sd.q_frame0 + row0 + lrow;
   const int hi = ok ? frame_hi(fi, sd.P, sd.E) : 0;
   const int pos = fi < sd.E ? fi : sd.E;
   const long long tq = (use_t && ok) ? a.ts_q[sd.q_base + row0 + lrow] : 0;
+  const bool tfr = use_t && a.tfilt && ok && fi >= sd.E;  // candidate under the timestamp filter
   float q[DP], o[DP];
 #pragma unroll
   for (int c = 0; c < DP; ++c) {
@@ -463,8 +488,9 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
       s += __shfl_xor(s, 1, 64);
       s += __shfl_xor(s, 2, 64);
       if (use_p) s += a.rab_p[pos_bucket(pos - j, a.n_pos)];
-      if (use_t) s += a.rab_t[time_bucket(tq - tsk[jl], a.n_tb)];
-      const float p = j < hi ? s / (1.0f + expf(-s)) : 0.f;
+      if (use_t && has_rt) s += a.rab_t[time_bucket(tq - tsk[jl], a.n_tb)];
+      const bool vis = j < hi && (!tfr || j < sd.P || tsk[jl] < tq);
+      const float p = vis ? s / (1.0f + expf(-s)) : 0.f;
 #pragma unroll
       for (int c = 0; c < DP; ++c) o[c] = fmaf(p, Vs[jl][part * DP + c], o[c]);
     }
@@ -478,7 +504,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
     for (int c = 0; c < DP; ++c) s = fmaf(q[c], Ksf[srow + c], s);
     s += __shfl_xor(s, 1, 64);
     s += __shfl_xor(s, 2, 64);
-    s += (use_p ? a.rab_p[0] : 0.f) + (use_t ? a.rab_t[0] : 0.f);
+    s += (use_p ? a.rab_p[0] : 0.f) + (use_t && has_rt ? a.rab_t[0] : 0.f);
     const float p = s / (1.0f + expf(-s));
 #pragma unroll
     for (int c = 0; c < DP; ++c) o[c] = fmaf(p, Vsf[srow + c], o[c]);
@@ -497,11 +523,20 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
 
 template <int D>
 hipError_t launch_bf16_d(const FwdArgs &a, hipStream_t s) {
-  const bool p = a.rab_p != nullptr, t = a.rab_t != nullptr;
-  if (p && t) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true>), dim3(a.units), dim3(256), 0, s, a);
-  else if (p) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false>), dim3(a.units), dim3(256), 0, s, a);
-  else if (t) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, true>), dim3(a.units), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false>), dim3(a.units), dim3(256), 0, s, a);
+  const bool p = a.rab_p != nullptr, t = a.ts_q != nullptr;
+  const dim3 g(a.units), b(256);
+  if (a.tfilt) {
+    if (p) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, true, true>), g, b, 0, s, a);
+  } else if (p && t) {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true, false>), g, b, 0, s, a);
+  } else if (p) {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false, false>), g, b, 0, s, a);
+  } else if (t) {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, true, false>), g, b, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, false>), g, b, 0, s, a);
+  }
   return hipGetLastError();
 }
 

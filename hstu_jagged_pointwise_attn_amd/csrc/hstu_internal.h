@@ -52,6 +52,7 @@ struct SchedArgs {
   long long Tq, Tkv;
   int max_len, hist_max_len;
   int BM, BN, microbatch;
+  int time_filter; // candidates see causal keys by timestamp: their causal tiles are never full
   int max_tiles;   // capacity of `tiles`; a larger count marks the offsets bad and runs nothing
   int *hdr;
   SeqDesc *desc;
@@ -66,11 +67,12 @@ struct FwdArgs {
   const void *Q, *K, *V;          // query rows / key rows
   const void *Kself, *Vself;      // rows used by a candidate's pair with itself
   void *O;                        // [Tq, H*d] output, scaled by 1/N_max
-  const int64_t *ts_q, *ts_kv;    // timestamps of query / key rows, or NULL
+  const int64_t *ts_q, *ts_kv;    // timestamps of query / key rows (rab_t or the filter), or NULL
   const float *rab_p, *rab_t;
   int n_pos, n_tb;
   float inv_nmax;
   int H, d;
+  int tfilt;                      // candidates see causal-segment keys only if strictly earlier
   int *hdr;                       // header words (tile count in, status bits out)
   const SeqDesc *desc;
   const QTile *tiles;
@@ -122,12 +124,13 @@ hipError_t launch_norm_bwd(const NormBwdArgs &a, bool bf16, hipStream_t s);
 struct BwdArgs {
   const void *Q, *K, *V, *dO;
   void *dQ, *dK, *dV;
-  const int64_t *ts;               // timestamps or NULL
+  const int64_t *ts;               // timestamps (rab_t or the filter) or NULL
   const float *rab_p, *rab_t;      // tables or NULL
   float *drab_p, *drab_t;          // fp32 accumulators (zeroed by the caller)
   int n_pos, n_tb;
   float inv_nmax;
   int H, d;
+  int tfilt;                       // candidates see causal-segment keys only if strictly earlier
   int *hdr;                        // header of the schedule this kernel runs
   const SeqDesc *desc;
   const QTile *tiles;

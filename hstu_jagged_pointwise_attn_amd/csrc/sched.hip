@@ -10,7 +10,11 @@
 //   hi(i) = P for i < P,  i + 1 for P <= i < E,  E for i >= E,
 // and hi is non-decreasing in i. So the key tiles a query tile [i0, i1]
 // touches are [0, ceil(hi(i1)/BN)), the first floor(hi(i0)/BN) of them fully
-// visible. Tiles with no visible pair are never listed.
+// visible. Tiles with no visible pair are never listed. Under MTGR's
+// timestamp filter a candidate sees a causal key only if the key is earlier;
+// the schedule does not read timestamps, so for a query tile with candidate
+// rows only the prefix tiles count as fully visible and the kernels test the
+// remaining pairs one by one.
 //
 // Steps: per-sequence validation and query-tile counts -> exclusive scan ->
 // one record per query tile -> longest-first order (bitonic sort in LDS on
@@ -114,6 +118,8 @@ __device__ QTile make_tile(const SchedArgs &a, const SeqDesc &s, int b, int t) {
   int i0 = s.q_frame0 + row0, i1 = i0 + nrows - 1;
   int nk = div_up(frame_hi(i1, s.P, s.E), a.BN);
   int nf = frame_hi(i0, s.P, s.E) / a.BN;
+  // Under the timestamp filter a candidate row is sure to see only the prefix.
+  if (a.time_filter && i1 >= s.E) nf = min(nf, s.P / a.BN);
   QTile r;
   r.b = b;
   r.row0 = row0;

@@ -34,7 +34,7 @@ def upload(p, device="cuda", with_grad_inputs=False):
         offsets, H=p.H, d=p.d, dtype=p.dtype, total_tokens=p.T, max_len=p.max_len, n_max=p.n_max,
         prefix_len=ns.prefix_len, cand_len=ns.cand_len, timestamps=ns.ts, rab_p=ns.rab_p,
         rab_t=ns.rab_t, norm=p.norm, eps=p.eps, token_group=ns.group, n_groups=p.n_groups,
-        gamma=ns.gamma, beta=ns.beta)
+        gamma=ns.gamma, beta=ns.beta, time_filter=p.time_filter)
     return ns
 
 
@@ -60,7 +60,7 @@ def upload_mfalcon(mf, device="cuda"):
         ns.cand_offsets, H=mf.H, d=mf.d, dtype=mf.dtype, total_tokens=int(mf.cand_offsets[-1]),
         max_len=cand_max, n_max=mf.n_max, timestamps=ns.cand_ts, rab_p=ns.rab_p, rab_t=ns.rab_t,
         norm=mf.norm, eps=mf.eps, token_group=ns.group, n_groups=mf.n_groups, gamma=ns.gamma,
-        beta=ns.beta)
+        beta=ns.beta, time_filter=mf.time_filter)
     return ns
 
 

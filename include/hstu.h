@@ -102,7 +102,17 @@ enum {
  *   token_group  uint8 [T] group id per token (GLN only), n_groups in [1, 255]
  *   gamma, beta  fp32 [n_groups, H*d] affine of the norm, or NULL (identity);
  *                for LN only row 0 is used
+ *   mask_flags   0, or HSTU_MASK_CAND_TIME_FILTER: MTGR's timestamp filter for
+ *                candidates (MTGR deep read, section 2: exposure samples are
+ *                filtered by timestamp to stay causal). A candidate row then
+ *                sees a key of the causal segment [P, E) only if the key's
+ *                timestamp is strictly earlier than the candidate's; prefix
+ *                keys and the candidate's own pair are unaffected. Requires
+ *                timestamps (the rab_t table may be NULL). For M-FALCON the
+ *                whole history is the causal segment.
  */
+enum { HSTU_MASK_CAND_TIME_FILTER = 1 };
+
 typedef struct hstu_problem {
   int32_t B, H, d, dtype;
   int64_t total_tokens;
@@ -119,7 +129,7 @@ typedef struct hstu_problem {
   float eps;
   const uint8_t *token_group;
   int32_t n_groups;
-  int32_t reserved;
+  int32_t mask_flags;
   const float *gamma;
   const float *beta;
 } hstu_problem_t;

@@ -70,6 +70,9 @@ def _ws(L, p, op=0):
     ({"max_len": 2_000_000}, 2),
     ({"B": 100000}, 2),
     ({"H": 64, "d": 128}, 2),        # D = 8192 wider than the norm kernel supports
+    ({"mask_flags": 2}, 1),          # unknown mask bit
+    ({"mask_flags": 1}, 1),          # timestamp filter without timestamps
+    ({"mask_flags": 1, "timestamps": ctypes.c_void_p(0x2000)}, 0),
 ])
 def test_workspace_size_validation(L, kw, status):
     st, n = _ws(L, _problem(L, **kw))
