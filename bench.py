@@ -41,6 +41,9 @@ WORKLOAD_TEXT = {
     "long": "Long-sequence fwd+bwd bf16: 32 sequences, lognormal lengths (median 2048) in [256, 8192], "
             "8 heads, d=128, causal, rab_p 8192 + rab_t 128, LN, N_max 8192",
     "tiny_fp32": "Tiny fp32 causal fwd: 4 sequences U{8..64}, 2 heads, d=32, rab_p 64 + rab_t 16, LN, N_max 64",
+    "batchprep": "Batch preparation of the training shape: 128 sequences (truncated Pareto(1.2), mean 776, max "
+                 "4096) cut to the Stochastic Length budget 776 on the device, Q/K/V/U (4 heads, d=128, bf16) and "
+                 "timestamps gathered, then 8 work-balanced bins by attention cost",
 }
 
 
@@ -157,6 +160,76 @@ def cpu_baseline(p, flops_per_pair, kind, budget_s):
                       f"{t1:.1f} s of fp64 oracle time with OpenMP on {cores} threads"}
 
 
+def bench_batchprep(args):
+    """One step = hstu_stochastic_length + hstu_gather_rows of Q, K, V, U and
+    the timestamps + hstu_balance_bins. value = input tokens per second; the
+    roofline is the gather's HBM traffic against 8 TB/s."""
+    import numpy as np
+    import torch
+
+    from hstu_jagged_pointwise_attn_amd import _lib, api, synth
+
+    p = synth.train_bf16(False)
+    cap = synth.stochastic_length_cap(4096, 1.6)
+    T, D = p.T, p.H * p.d
+    keys = np.random.default_rng(2024).integers(0, 2 ** 32, size=T, dtype=np.uint64).astype(np.uint32)
+    dev = torch.device("cuda")
+    off = torch.from_numpy(p.offsets).to(dev)
+    dkeys = torch.from_numpy(keys.view(np.int32)).to(dev)
+    Q, K, V, U = (x.contiguous().to(dev) for x in (p.Q, p.K, p.V, p.U))
+    ts = torch.from_numpy(p.ts).to(dev)
+    new_off, idx, status = api.stochastic_length(off, dkeys, cap, p.max_len)
+    n = int(new_off[-1].item())
+
+    def step():
+        api.stochastic_length(off, dkeys, cap, p.max_len)
+        for x in (Q, K, V, U, ts):
+            api.gather_rows(x, idx, n)
+        api.balance_bins(new_off, 8, _lib.HSTU_COST_ATTENTION)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    api.kernel_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    per = {}
+    for kid, name in ((_lib.HSTU_KERNEL_STOCHASTIC_LENGTH, "stochastic_length"),
+                      (_lib.HSTU_KERNEL_GATHER, "gather_rows"), (_lib.HSTU_KERNEL_BALANCE, "balance_bins")):
+        tms, k = api.kernel_timing_read(kid)
+        if k:
+            per[name] = tms / k
+    api.kernel_timing(False)
+    # gather launches: 4 of n rows x D bf16 and one of n int64; bytes read + written + indices
+    row_bytes = [D * 2] * 4 + [8]
+    gather_bytes = sum(n * rb * 2 + 4 * n for rb in row_bytes)
+    gather_ms = per["gather_rows"] * len(row_bytes)
+    achieved = gather_bytes / (gather_ms * 1e-3) / 1e9
+    log(f"[bench] {ms:.4f} ms/step; per-launch ms: " + ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
+    rec = {
+        "metric": "batch preparation input tokens/s (Stochastic Length + gathers + balanced bins, 1 MI355X)",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded generators; no dataset)",
+        "config": {"workload": WORKLOAD_TEXT["batchprep"], "name": "batchprep", "tokens_in": T, "tokens_kept": n,
+                   "cap": cap, "batch": p.B, "heads": p.H, "d": p.d},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "gather_rows (5 launches)",
+                     "kernel_ms": gather_ms, "per_kernel_ms": per},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +257,8 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     wl = args.workload
+    if wl == "batchprep":
+        return bench_batchprep(args)
     log(f"[bench] generating workload {wl}")
     if wl == "mfalcon":
         src = synth.mfalcon_bf16()

@@ -16,8 +16,10 @@ HSTU_BF16, HSTU_F32 = 0, 1
 HSTU_NORM_NONE, HSTU_NORM_LN, HSTU_NORM_GLN = 0, 1, 2
 HSTU_OP_FWD, HSTU_OP_BWD, HSTU_OP_MFALCON = 0, 1, 2
 HSTU_MASK_CAND_TIME_FILTER = 1
+HSTU_COST_TOKENS, HSTU_COST_ATTENTION = 0, 1
 (HSTU_KERNEL_SCHED, HSTU_KERNEL_ATTN_FWD, HSTU_KERNEL_NORM_FWD, HSTU_KERNEL_NORM_BWD, HSTU_KERNEL_ATTN_BWD_DQ,
- HSTU_KERNEL_AUX, HSTU_KERNEL_ATTN_BWD_DKDV) = range(7)
+ HSTU_KERNEL_AUX, HSTU_KERNEL_ATTN_BWD_DKDV, HSTU_KERNEL_STOCHASTIC_LENGTH, HSTU_KERNEL_GATHER,
+ HSTU_KERNEL_BALANCE) = range(10)
 HSTU_DEV_BAD_OFFSETS, HSTU_DEV_BAD_SEGMENTS, HSTU_DEV_BAD_GROUP, HSTU_DEV_TOO_LONG = 1, 2, 4, 8
 HSTU_DEV_BAD_TIMESTAMPS = 16
 
@@ -70,6 +72,10 @@ SIGNATURES = {
     "hstu_kernel_timing": ([ctypes.c_int32], ctypes.c_int),
     "hstu_kernel_timing_read": ([ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
                                  ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
+    "hstu_stochastic_length": ([_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp, _vp,
+                                _vp, _vp, _vp], ctypes.c_int),
+    "hstu_gather_rows": ([_vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp], ctypes.c_int),
+    "hstu_balance_bins": ([_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp], ctypes.c_int),
 }
 
 

@@ -223,3 +223,47 @@ def kernel_timing_read(kernel: int):
     ms, n = ctypes.c_double(0), ctypes.c_int64(0)
     L.check(L.lib().hstu_kernel_timing_read(int(kernel), ctypes.byref(ms), ctypes.byref(n)))
     return float(ms.value), int(n.value)
+
+
+# ------------------------------------------------------------ batch preparation
+
+def stochastic_length(offsets: torch.Tensor, keys: torch.Tensor, cap: int, max_len: int, stream=None):
+    """hstu_stochastic_length. offsets int32 [B+1], keys int32/uint32 bits
+    [T] on the device. Returns (new_offsets int32 [B+1], gather_idx int32 [T],
+    status int32 [1]); the first new_offsets[B] entries of gather_idx are
+    valid."""
+    dev = offsets.device
+    B = offsets.numel() - 1
+    T = keys.numel()
+    _need(offsets, "offsets", torch.int32, dev)
+    if keys.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("keys must be 32-bit")
+    new_off = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    idx = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    L.check(L.lib().hstu_stochastic_length(_ptr(offsets), B, T, int(max_len), int(cap), _ptr(keys), _ptr(new_off),
+                                           _ptr(idx), _ptr(status), _stream(stream)))
+    return new_off, idx, status
+
+
+def gather_rows(src: torch.Tensor, idx: torch.Tensor, n: int, stream=None):
+    """hstu_gather_rows: rows src[idx[r]] for r < n of a dense [rows, ...] tensor."""
+    dev = src.device
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    row_bytes = src[0].numel() * src.element_size() if src.shape[0] else src.element_size()
+    dst = torch.empty((int(n),) + tuple(src.shape[1:]), dtype=src.dtype, device=dev)
+    L.check(L.lib().hstu_gather_rows(_ptr(src), _ptr(idx), int(n), int(row_bytes), _ptr(dst), _stream(stream)))
+    return dst
+
+
+def balance_bins(offsets: torch.Tensor, n_bins: int, cost_kind=L.HSTU_COST_TOKENS, stream=None):
+    """hstu_balance_bins. Returns (bin int32 [B], bin_cost int64 [n_bins])."""
+    dev = offsets.device
+    B = offsets.numel() - 1
+    _need(offsets, "offsets", torch.int32, dev)
+    b = torch.empty(max(B, 1), dtype=torch.int32, device=dev)
+    cost = torch.empty(n_bins, dtype=torch.int64, device=dev)
+    L.check(L.lib().hstu_balance_bins(_ptr(offsets), B, int(n_bins), int(cost_kind), _ptr(b), _ptr(cost),
+                                      _stream(stream)))
+    return b[:B], cost

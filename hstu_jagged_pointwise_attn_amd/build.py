@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhstu.so")
-SOURCES = ["sched.hip", "attn_fwd.hip", "attn_bwd.hip", "norm.hip", "api.cpp"]
+SOURCES = ["sched.hip", "attn_fwd.hip", "attn_bwd.hip", "norm.hip", "batching.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -512,6 +512,46 @@ hstu_status_t hstu_schedule_export(const hstu_problem_t *p, int32_t op,
   return HSTU_OK;
 }
 
+hstu_status_t hstu_stochastic_length(const int32_t *offsets, int32_t B, int64_t total_tokens, int32_t max_len,
+                                     int32_t cap, const uint32_t *keys, int32_t *new_offsets,
+                                     int32_t *gather_idx, int32_t *status, void *stream) {
+  if (B < 0) return fail(HSTU_ERR_INVALID_ARG, "B = %d < 0", B);
+  if (total_tokens < 0 || total_tokens >= (1ll << 31))
+    return fail(HSTU_ERR_INVALID_ARG, "total_tokens = %lld out of [0, 2^31)", (long long)total_tokens);
+  if (max_len < 0) return fail(HSTU_ERR_INVALID_ARG, "max_len = %d < 0", max_len);
+  if (cap < 1) return fail(HSTU_ERR_INVALID_ARG, "cap = %d < 1", cap);
+  if (!offsets || !new_offsets || !status) return fail(HSTU_ERR_INVALID_ARG, "offsets/new_offsets/status NULL");
+  if (total_tokens > 0 && (!keys || !gather_idx)) return fail(HSTU_ERR_INVALID_ARG, "keys/gather_idx NULL");
+  Timed t_(HSTU_KERNEL_STOCHASTIC_LENGTH, (hipStream_t)stream);
+  HIP_TRY(launch_stochastic_length(offsets, B, total_tokens, max_len, cap, keys, new_offsets, gather_idx, status,
+                                   (hipStream_t)stream),
+          "stochastic length launch");
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_gather_rows(const void *src, const int32_t *idx, int64_t n, int64_t row_bytes, void *dst,
+                               void *stream) {
+  if (n < 0) return fail(HSTU_ERR_INVALID_ARG, "n = %lld < 0", (long long)n);
+  if (row_bytes <= 0 || row_bytes % 4) return fail(HSTU_ERR_INVALID_ARG, "row_bytes = %lld not a positive multiple of 4", (long long)row_bytes);
+  if (n > 0 && (!src || !idx || !dst)) return fail(HSTU_ERR_INVALID_ARG, "src/idx/dst NULL");
+  Timed t_(HSTU_KERNEL_GATHER, (hipStream_t)stream);
+  HIP_TRY(launch_gather_rows(src, idx, n, row_bytes, dst, (hipStream_t)stream), "gather launch");
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_balance_bins(const int32_t *offsets, int32_t B, int32_t n_bins, int32_t cost_kind,
+                                int32_t *bin, int64_t *bin_cost, void *stream) {
+  if (B < 0 || B > 8192) return fail(HSTU_ERR_INVALID_ARG, "B = %d not in [0, 8192]", B);
+  if (n_bins < 1 || n_bins > 64) return fail(HSTU_ERR_INVALID_ARG, "n_bins = %d not in [1, 64]", n_bins);
+  if (cost_kind != HSTU_COST_TOKENS && cost_kind != HSTU_COST_ATTENTION)
+    return fail(HSTU_ERR_INVALID_ARG, "cost_kind = %d", cost_kind);
+  if (!offsets || !bin_cost || (B > 0 && !bin)) return fail(HSTU_ERR_INVALID_ARG, "offsets/bin/bin_cost NULL");
+  Timed t_(HSTU_KERNEL_BALANCE, (hipStream_t)stream);
+  HIP_TRY(launch_balance(offsets, B, n_bins, cost_kind, bin, (long long *)bin_cost, (hipStream_t)stream),
+          "balance launch");
+  return HSTU_OK;
+}
+
 hstu_status_t hstu_get_device_status(const void *ws, void *stream, int32_t *host_code) {
   if (!ws || !host_code) return fail(HSTU_ERR_INVALID_ARG, "NULL argument");
   hipStream_t st = (hipStream_t)stream;

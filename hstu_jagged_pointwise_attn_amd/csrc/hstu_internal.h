@@ -146,4 +146,13 @@ hipError_t launch_attn_bwd_dkdv_f32(const BwdArgs &a, hipStream_t s);
 
 hipError_t launch_fill_f32(float *p, long long n, float v, hipStream_t s);
 
+// Batch preparation (Stochastic Length, row gather, work-balanced bins).
+hipError_t launch_stochastic_length(const int *offsets, int B, long long T, int max_len, int cap,
+                                    const unsigned *keys, int *new_offsets, int *gather_idx, int *status,
+                                    hipStream_t s);
+hipError_t launch_gather_rows(const void *src, const int *idx, long long n, long long row_bytes, void *dst,
+                              hipStream_t s);
+hipError_t launch_balance(const int *offsets, int B, int n_bins, int cost_kind, int *bin, long long *bin_cost,
+                          hipStream_t s);
+
 }  // namespace hstu

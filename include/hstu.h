@@ -260,10 +260,54 @@ enum {
   HSTU_KERNEL_ATTN_BWD_DQ = 4,    /* attention backward, query-major pass (dQ, d rab) */
   HSTU_KERNEL_AUX = 5,            /* fills */
   HSTU_KERNEL_ATTN_BWD_DKDV = 6,  /* attention backward, key-major pass (dK, dV) */
-  HSTU_KERNEL_COUNT = 7
+  HSTU_KERNEL_STOCHASTIC_LENGTH = 7,  /* hstu_stochastic_length (both of its kernels) */
+  HSTU_KERNEL_GATHER = 8,         /* hstu_gather_rows */
+  HSTU_KERNEL_BALANCE = 9,        /* hstu_balance_bins */
+  HSTU_KERNEL_COUNT = 10
 };
 hstu_status_t hstu_kernel_timing(int32_t enable);
 hstu_status_t hstu_kernel_timing_read(int32_t kernel, double *total_ms, int64_t *launches);
+
+/*
+ * Stochastic Length (HSTU blog, section 3.4: training sequences are sampled
+ * down to a length budget, 4096 -> about 776 at alpha = 1.6). Device side,
+ * no host round trip. For every sequence b of the input batch (offsets [B+1],
+ * device) of length L_b: if L_b <= cap all its tokens are kept, else the cap
+ * tokens with the smallest (keys[t], t) are kept, in their original order (a
+ * uniform random subset when keys are independent uniform random words; the
+ * randomness is the caller's input, so the result is reproducible).
+ *   keys         uint32 [total_tokens] device, one per input token
+ *   new_offsets  int32 [B+1] device out: offsets of the kept batch
+ *   gather_idx   int32 [total_tokens] device out: for r < new_offsets[B], the
+ *                input index of the r-th kept token (gather rows with it)
+ *   status       int32 [1] device out: 0, or HSTU_DEV_BAD_OFFSETS /
+ *                HSTU_DEV_TOO_LONG (then nothing is kept: new_offsets all 0)
+ * Requires cap >= 1 and max_len >= every L_b. Asynchronous on `stream`.
+ */
+hstu_status_t hstu_stochastic_length(const int32_t *offsets, int32_t B, int64_t total_tokens, int32_t max_len,
+                                     int32_t cap, const uint32_t *keys, int32_t *new_offsets,
+                                     int32_t *gather_idx, int32_t *status, void *stream);
+
+/*
+ * dst[r] = src[idx[r]] for n rows of row_bytes bytes (a multiple of 4; all
+ * pointers device, rows dense). Gathers the tensors of a batch through the
+ * indices hstu_stochastic_length returns. Asynchronous on `stream`.
+ */
+hstu_status_t hstu_gather_rows(const void *src, const int32_t *idx, int64_t n, int64_t row_bytes, void *dst,
+                               void *stream);
+
+/*
+ * Work-balanced jagged batching (MTGR deep read, section 2: batch sizes are
+ * adapted so that every GPU holds the same number of tokens). Sequences of a
+ * batch (offsets [B+1], device) are assigned to n_bins bins (1..64), taken in
+ * order of decreasing cost (ties by index), each to the bin with the smallest
+ * cost so far (ties to the lowest bin). Cost: HSTU_COST_TOKENS = L, or
+ * HSTU_COST_ATTENTION = L * L. Outputs (device): bin [B], bin_cost int64
+ * [n_bins]. B <= 8192. Asynchronous on `stream`.
+ */
+enum { HSTU_COST_TOKENS = 0, HSTU_COST_ATTENTION = 1 };
+hstu_status_t hstu_balance_bins(const int32_t *offsets, int32_t B, int32_t n_bins, int32_t cost_kind,
+                                int32_t *bin, int64_t *bin_cost, void *stream);
 
 #ifdef __cplusplus
 }

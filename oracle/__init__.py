@@ -248,3 +248,39 @@ def lpt_order(entries):
     """Longest-processing-time order: by number of present key tiles,
     descending; ties keep the canonical order."""
     return sorted(range(len(entries)), key=lambda g: (-int(np.count_nonzero(entries[g]["kinds"])), g))
+
+
+def stochastic_length(offsets, keys, cap):
+    """Stochastic Length (HSTU blog, section 3.4): a sequence longer than cap
+    keeps the cap tokens with the smallest (key, index), in their order;
+    shorter ones are kept whole. Returns (new_offsets, gather_idx) as int64
+    arrays (gather_idx holds input token indices)."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.uint32)
+    new_off = [0]
+    idx = []
+    for b in range(len(offsets) - 1):
+        s, e = int(offsets[b]), int(offsets[b + 1])
+        toks = list(range(s, e))
+        if len(toks) > cap:
+            ranked = sorted(toks, key=lambda t: (int(keys[t]), t))
+            toks = sorted(ranked[:cap])
+        idx.extend(toks)
+        new_off.append(new_off[-1] + len(toks))
+    return np.array(new_off, dtype=np.int64), np.array(idx, dtype=np.int64)
+
+
+def balance_bins(lengths, n_bins, cost_kind=0):
+    """Work-balanced batching (MTGR deep read, section 2): sequences in order
+    of decreasing cost (ties by index) each go to the bin with the smallest
+    cost so far (ties to the lowest bin). cost_kind 0: L, 1: L * L. Returns
+    (bin per sequence, cost per bin)."""
+    cost = [int(L) if cost_kind == 0 else int(L) * int(L) for L in lengths]
+    order = sorted(range(len(cost)), key=lambda b: (-cost[b], b))
+    load = [0] * n_bins
+    out = [0] * len(cost)
+    for b in order:
+        best = min(range(n_bins), key=lambda k: (load[k], k))
+        out[b] = best
+        load[best] += cost[b]
+    return np.array(out, dtype=np.int64), np.array(load, dtype=np.int64)

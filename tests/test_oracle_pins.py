@@ -602,3 +602,68 @@ def test_time_filter_schedule_marks_candidate_causal_tiles_partial(oracle_mod):
     # candidate tail carries only self pairs, which are added outside the tiles
     assert list(plain) == [2, 2, 2, 0, 0]
     assert list(filt) == [2, 1, 1, 0, 0]
+
+
+# ------------------------------------------- batch preparation (SL, bins)
+
+def test_stochastic_length_special_cases(oracle_mod):
+    off = np.array([0, 5, 5, 17, 20])
+    T = 20
+    # cap at least every length: identity
+    no, idx = oracle_mod.stochastic_length(off, np.zeros(T, np.uint32), 12)
+    np.testing.assert_array_equal(no, off)
+    np.testing.assert_array_equal(idx, np.arange(T))
+    # increasing keys keep the first cap tokens, decreasing keys the last cap
+    no, idx = oracle_mod.stochastic_length(off, np.arange(T, dtype=np.uint32), 4)
+    np.testing.assert_array_equal(no, [0, 4, 4, 8, 11])
+    np.testing.assert_array_equal(idx, [0, 1, 2, 3, 5, 6, 7, 8, 17, 18, 19])
+    no, idx = oracle_mod.stochastic_length(off, (100 - np.arange(T)).astype(np.uint32), 4)
+    np.testing.assert_array_equal(idx, [1, 2, 3, 4, 13, 14, 15, 16, 17, 18, 19])
+    # equal keys: ties go by index, so the first cap are kept
+    no, idx = oracle_mod.stochastic_length(off, np.full(T, 7, np.uint32), 2)
+    np.testing.assert_array_equal(idx, [0, 1, 5, 6, 17, 18])
+
+
+def test_stochastic_length_is_uniform(oracle_mod):
+    """With independent uniform keys every token of a long sequence is kept
+    with probability cap / L (checked to a few standard errors), and the kept
+    tokens keep their order."""
+    L, cap, trials = 40, 10, 3000
+    rng = np.random.default_rng(11)
+    hits = np.zeros(L)
+    for _ in range(trials):
+        keys = rng.integers(0, 2 ** 32, size=L, dtype=np.uint64).astype(np.uint32)
+        no, idx = oracle_mod.stochastic_length([0, L], keys, cap)
+        assert no[-1] == cap and np.all(np.diff(idx) > 0)
+        hits[idx] += 1
+    p = cap / L
+    se = np.sqrt(p * (1 - p) / trials)
+    assert np.all(np.abs(hits / trials - p) < 5 * se)
+
+
+def test_balance_bins_hand_fixture(oracle_mod):
+    # lengths 5, 3, 3, 2 into 2 bins: 5 -> 0, 3 -> 1, 3 -> 1, 2 -> 0
+    b, c = oracle_mod.balance_bins([3, 5, 2, 3], 2)
+    np.testing.assert_array_equal(b, [1, 0, 0, 1])
+    np.testing.assert_array_equal(c, [7, 6])
+    # attention cost: 25 -> 0, 9 -> 1, 9 -> 1, 4 -> 1 (loads 25 | 9, 18, 22)
+    b, c = oracle_mod.balance_bins([3, 5, 2, 3], 2, cost_kind=1)
+    np.testing.assert_array_equal(b, [1, 0, 1, 1])
+    np.testing.assert_array_equal(c, [25, 22])
+
+
+def test_balance_bins_within_graham_bound(oracle_mod):
+    """Longest-first greedy is within (4/3 - 1/(3m)) of the best makespan,
+    found here by brute force on small inputs; costs are conserved."""
+    import itertools
+    rng = np.random.default_rng(12)
+    for _ in range(30):
+        n, m = int(rng.integers(3, 8)), int(rng.integers(2, 4))
+        lengths = rng.integers(1, 50, size=n)
+        b, c = oracle_mod.balance_bins(lengths, m)
+        assert c.sum() == lengths.sum()
+        for k in range(m):
+            assert c[k] == lengths[b == k].sum()
+        best = min(max(sum(int(lengths[i]) for i in range(n) if a[i] == k) for k in range(m))
+                   for a in itertools.product(range(m), repeat=n))
+        assert c.max() <= (4.0 / 3.0 - 1.0 / (3 * m)) * best + 1e-9
