@@ -29,6 +29,7 @@ NORM_NONE, NORM_LN, NORM_GLN = 0, 1, 2
 
 # Tensor ids for seeding.
 _LEN, _TS, _Q, _K, _V, _U, _RP, _RT, _GAMMA, _DY, _KC, _VC, _QC, _UC, _CTS, _SEG = range(16)
+_X, _W1, _B1, _W2, _B2, _DOUT = range(16, 22)
 
 
 @dataclass
@@ -377,3 +378,57 @@ def subbatch(p: Problem, seqs) -> Problem:
         prefix_len=seq_np(p.prefix_len), cand_len=seq_np(p.cand_len), ts=sel_np(p.ts),
         rab_p=p.rab_p, rab_t=p.rab_t, group=sel_np(p.group), n_groups=p.n_groups,
         gamma=p.gamma, beta=p.beta, dY=sel(p.dY))
+
+
+@dataclass
+class LayerProblem:
+    """A full HSTU layer: the attention problem `core` (its masks, rab, norm
+    and sizes; its Q/K/V/U are not used, the layer makes its own from X)
+    plus the layer input X [T, d_model], the projections W1 [d_model, 4D],
+    b1 [4D], W2 [D, d_model], b2 [d_model] and the output gradient dOut."""
+    core: Problem
+    d_model: int
+    X: torch.Tensor
+    W1: torch.Tensor
+    W2: torch.Tensor
+    b1: Optional[np.ndarray]
+    b2: Optional[np.ndarray]
+    dOut: Optional[torch.Tensor]
+
+    @property
+    def name(self) -> str:
+        return self.core.name
+
+    @property
+    def T(self) -> int:
+        return self.core.T
+
+
+def with_layer(p: Problem, d_model: Optional[int] = None, wid: int = 60, x_std=1.0, w_std=0.02,
+               bias_std: Optional[float] = 0.02, with_dout=True) -> LayerProblem:
+    """Layer inputs around problem p: X ~ N(0, x_std) and the weights
+    ~ N(0, w_std) in p's dtype (0.02 is the pages' initialisation scale for
+    the workloads' tensors), fp32 biases ~ N(0, bias_std) (None: no biases),
+    dOut ~ N(0, 1). d_model defaults to D = H * d."""
+    D = p.H * p.d
+    dm = D if d_model is None else int(d_model)
+    T = p.T
+    b1 = b2 = None
+    if bias_std is not None:
+        b1 = _rng(wid, _B1).standard_normal(4 * D, dtype=np.float32) * np.float32(bias_std)
+        b2 = _rng(wid, _B2).standard_normal(dm, dtype=np.float32) * np.float32(bias_std)
+    return LayerProblem(
+        core=p, d_model=dm, X=_normal(wid, _X, (T, dm), x_std, p.dtype),
+        W1=_normal(wid, _W1, (dm, 4 * D), w_std, p.dtype), W2=_normal(wid, _W2, (D, dm), w_std, p.dtype),
+        b1=b1, b2=b2, dOut=_normal(wid, _DOUT, (T, dm), 1.0, p.dtype) if with_dout else None)
+
+
+def layer_train_bf16() -> LayerProblem:
+    """The training shape (train_bf16) as one full layer: d_model = D = 512,
+    projection biases on."""
+    return with_layer(train_bf16(False), wid=62)
+
+
+def layer_long_bf16() -> LayerProblem:
+    """The long-sequence shape (long_bf16) as one full layer: d_model = D = 1024."""
+    return with_layer(long_bf16(), wid=65)

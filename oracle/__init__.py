@@ -284,3 +284,52 @@ def balance_bins(lengths, n_bins, cost_kind=0):
         out[b] = best
         load[best] += cost[b]
     return np.array(out, dtype=np.int64), np.array(load, dtype=np.int64)
+
+
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def _silu_grad(z):
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def layer_fwd(offsets, X, W1, W2, *, H, d, b1=None, b2=None, **attn):
+    """One HSTU layer (HSTU blog, section 3, the layer formula): the input
+    projection f1(X) = X W1 + b1 of width 4D, phi1 = SiLU, its column blocks
+    taken as U, V, Q, K in that order, the attention core (``fwd`` above,
+    keyword arguments passed through) and the output projection
+    f2(Y) = Y W2 + b2 of Y = Norm(A V) * U. X: [T, d_model], W1: [d_model, 4D],
+    W2: [D, d_model]. Returns dict with Out, Z (the pre-activation f1(X)), the
+    split U, V, Q, K and the core's Y, O, mean, rstd."""
+    D = H * d
+    X, W1, W2 = _f64(X), _f64(W1), _f64(W2)
+    Z = X @ W1
+    if b1 is not None:
+        Z = Z + _f64(b1)
+    A = _silu(Z)
+    U, V, Q, K = (A[:, i * D:(i + 1) * D] for i in range(4))
+    core = fwd(offsets, Q, K, V, U, H=H, d=d, **attn)
+    Out = core["Y"] @ W2
+    if b2 is not None:
+        Out = Out + _f64(b2)
+    return {"Out": Out, "Z": Z, "U": U, "V": V, "Q": Q, "K": K, **core}
+
+
+def layer_bwd(offsets, X, W1, W2, dOut, *, H, d, b1=None, b2=None, **attn):
+    """Backward of ``layer_fwd`` by the chain rule through its steps: the
+    output projection (dY = dOut W2^T, dW2 = Y^T dOut, db2 = column sums of
+    dOut), the attention core (``bwd`` above), SiLU (dZ = [dU | dV | dQ | dK]
+    * SiLU'(Z)) and the input projection (dW1 = X^T dZ, db1 = column sums of
+    dZ, dX = dZ W1^T). Returns dict with dX, dW1, db1, dW2, db2, dZ and the
+    core's drab_p, drab_t, dgamma, dbeta."""
+    f = layer_fwd(offsets, X, W1, W2, H=H, d=d, b1=b1, b2=b2, **attn)
+    X, W1, W2, dOut = _f64(X), _f64(W1), _f64(W2), _f64(dOut)
+    attn = {k: v for k, v in attn.items() if k not in ("row_sel",)}
+    dY = dOut @ W2.T
+    g = bwd(offsets, f["Q"], f["K"], f["V"], f["U"], dY, H=H, d=d, **attn)
+    dZ = np.concatenate([g["dU"], g["dV"], g["dQ"], g["dK"]], axis=1) * _silu_grad(f["Z"])
+    return {"dX": dZ @ W1.T, "dW1": X.T @ dZ, "db1": dZ.sum(0), "dW2": f["Y"].T @ dOut,
+            "db2": dOut.sum(0), "dZ": dZ, "dY": dY, "drab_p": g["drab_p"], "drab_t": g["drab_t"],
+            "dgamma": g["dgamma"], "dbeta": g["dbeta"]}

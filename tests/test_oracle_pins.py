@@ -667,3 +667,96 @@ def test_balance_bins_within_graham_bound(oracle_mod):
         best = min(max(sum(int(lengths[i]) for i in range(n) if a[i] == k) for k in range(m))
                    for a in itertools.product(range(m), repeat=n))
         assert c.max() <= (4.0 / 3.0 - 1.0 / (3 * m)) * best + 1e-9
+
+
+# ------------------------------------------------------------------ full layer
+
+def _layer_problems():
+    """Small layers with d_model != D (a transposed weight cannot go
+    unnoticed) over the backward pins' attention problems."""
+    out = []
+    for i, p in enumerate(_grad_problems()):
+        out.append(synth.with_layer(p, d_model=[6, 11, 5][i], wid=70 + i, x_std=0.8, w_std=0.4,
+                                    bias_std=None if i == 2 else 0.3))
+    return out
+
+
+def _torch_layer(lp, X, W1, b1, W2, b2, opts):
+    """The layer out of torch library routines: matmul, F.silu, torch.split
+    into U, V, Q, K, the dense attention above, matmul."""
+    p = lp.core
+    D = p.H * p.d
+    Z = X @ W1 + (b1 if b1 is not None else 0.0)
+    U, V, Q, K = (t.reshape(p.T, p.H, p.d) for t in torch.split(torch.nn.functional.silu(Z), D, dim=1))
+    Y, _ = dense_torch.forward(p.offsets, Q, K, V, U, **opts)
+    return Y @ W2 + (b2 if b2 is not None else 0.0)
+
+
+def _layer_np(lp):
+    f = lambda t: None if t is None else np.asarray(t.double().numpy() if torch.is_tensor(t) else t, np.float64)
+    return f(lp.X), f(lp.W1), f(lp.b1), f(lp.W2), f(lp.b2), f(lp.dOut)
+
+
+@pytest.mark.parametrize("lp", _layer_problems(), ids=lambda lp: lp.name)
+def test_layer_matches_torch_autograd(oracle_mod, lp):
+    p = lp.core
+    X, W1, b1, W2, b2, dOut = _layer_np(lp)
+    leaves = {k: (None if v is None else torch.tensor(v, requires_grad=True))
+              for k, v in dict(X=X, W1=W1, b1=b1, W2=W2, b2=b2).items()}
+    opts = _dense_opts(p)
+    params = {k: opts[k] for k in ("rab_p", "rab_t", "gamma", "beta") if opts[k] is not None}
+    for t in params.values():
+        t.requires_grad_(True)
+    Out = _torch_layer(lp, leaves["X"], leaves["W1"], leaves["b1"], leaves["W2"], leaves["b2"], opts)
+    (Out * torch.tensor(dOut)).sum().backward()
+    f = oracle_mod.layer_fwd(p.offsets, X, W1, W2, b1=b1, b2=b2, **_oracle_opts(p))
+    np.testing.assert_allclose(f["Out"], Out.detach().numpy(), rtol=1e-10, atol=1e-12)
+    g = oracle_mod.layer_bwd(p.offsets, X, W1, W2, dOut, b1=b1, b2=b2, **_oracle_opts(p))
+    for name, key in (("dX", "X"), ("dW1", "W1"), ("db1", "b1"), ("dW2", "W2"), ("db2", "b2")):
+        if leaves[key] is not None:
+            np.testing.assert_allclose(g[name], leaves[key].grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=name)
+    for name, key in (("drab_p", "rab_p"), ("drab_t", "rab_t"), ("dgamma", "gamma"), ("dbeta", "beta")):
+        if key in params:
+            np.testing.assert_allclose(g[name], params[key].grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=name)
+
+
+@pytest.mark.parametrize("lp", _layer_problems()[:2], ids=lambda lp: lp.name)
+def test_layer_backward_matches_central_differences(oracle_mod, lp):
+    """<grad, delta> against central differences of sum(Out * dOut) from
+    layer_fwd itself, for every layer parameter and the input."""
+    p = lp.core
+    X, W1, b1, W2, b2, dOut = _layer_np(lp)
+    vals = {k: v for k, v in dict(X=X, W1=W1, b1=b1, W2=W2, b2=b2).items() if v is not None}
+    opts = _oracle_opts(p)
+
+    def f(v):
+        return float((oracle_mod.layer_fwd(p.offsets, v["X"], v["W1"], v["W2"], b1=v.get("b1"),
+                                           b2=v.get("b2"), **opts)["Out"] * dOut).sum())
+
+    g = oracle_mod.layer_bwd(p.offsets, X, W1, W2, dOut, b1=b1, b2=b2, **opts)
+    rng = np.random.default_rng(5)
+    h = 1e-5
+    for k in vals:
+        delta = rng.normal(size=vals[k].shape)
+        fd = (f({**vals, k: vals[k] + h * delta}) - f({**vals, k: vals[k] - h * delta})) / (2 * h)
+        an = float((g["d" + k] * delta).sum())
+        assert an == pytest.approx(fd, rel=1e-6, abs=1e-9), k
+
+
+def test_layer_with_block_identity_weights_is_the_core(oracle_mod):
+    """W1 = [a_u I | a_v I | a_q I | a_k I] (d_model = D), no biases and
+    W2 = I make the layer the attention core on Q = SiLU(a_q X) and so on:
+    pins the order of the split and where each block goes. The SiLU here is
+    torch's."""
+    p = _grad_problems()[0]
+    D = p.H * p.d
+    lp = synth.with_layer(p, wid=77, x_std=1.0, bias_std=None)
+    X = lp.X.double().numpy()
+    scales = dict(u=0.5, v=-1.25, q=2.0, k=0.75)
+    W1 = np.concatenate([s * np.eye(D) for s in scales.values()], axis=1)
+    f = oracle_mod.layer_fwd(p.offsets, X, W1, np.eye(D), **_oracle_opts(p))
+    act = {k: torch.nn.functional.silu(torch.tensor(s * X)).numpy() for k, s in scales.items()}
+    core = oracle_mod.fwd(p.offsets, act["q"], act["k"], act["v"], act["u"], **_oracle_opts(p))
+    for name, want in (("Q", act["q"]), ("K", act["k"]), ("V", act["v"]), ("U", act["u"])):
+        np.testing.assert_allclose(f[name], want, rtol=1e-14, atol=1e-300, err_msg=name)
+    np.testing.assert_allclose(f["Out"], core["Y"], rtol=1e-12, atol=1e-14)
