@@ -41,6 +41,12 @@ WORKLOAD_TEXT = {
     "long": "Long-sequence fwd+bwd bf16: 32 sequences, lognormal lengths (median 2048) in [256, 8192], "
             "8 heads, d=128, causal, rab_p 8192 + rab_t 128, LN, N_max 8192",
     "tiny_fp32": "Tiny fp32 causal fwd: 4 sequences U{8..64}, 2 heads, d=32, rab_p 64 + rab_t 16, LN, N_max 64",
+    "layer_train": "Full HSTU layer fwd+bwd bf16 on the training shape: X [T, 512] -> f1 (512 x 2048, bias) -> "
+                   "SiLU -> U|V|Q|K -> attention (128 jagged sequences, mean 776, 4 heads, d=128, causal, rab_p/rab_t, "
+                   "LN, N_max 4096) -> f2 (512 x 512, bias)",
+    "layer_long": "Full HSTU layer fwd+bwd bf16 on the long-sequence shape: X [T, 1024] -> f1 (1024 x 4096, bias) -> "
+                  "SiLU -> U|V|Q|K -> attention (32 sequences, median 2048, 8 heads, d=128, causal, rab_p/rab_t, LN, "
+                  "N_max 8192) -> f2 (1024 x 1024, bias)",
     "batchprep": "Batch preparation of the training shape: 128 sequences (truncated Pareto(1.2), mean 776, max "
                  "4096) cut to the Stochastic Length budget 776 on the device, Q/K/V/U (4 heads, d=128, bf16) and "
                  "timestamps gathered, then 8 work-balanced bins by attention cost",
@@ -230,6 +236,139 @@ def bench_batchprep(args):
     print(json.dumps(rec), flush=True)
 
 
+def cpu_baseline_layer(lp, budget_s):
+    """The CPU oracle's layer forward + backward on a bounded sample of the
+    layer workload's sequences (seeded order), sized to about budget_s."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from hstu_jagged_pointwise_attn_amd import synth
+    from tests.common import oracle_layer_bwd
+
+    oracle.build(force=False)
+    cores = os.cpu_count() or 1
+    p = lp.core
+    D, dm = p.H * p.d, lp.d_model
+    order = np.random.default_rng(12345).permutation(p.B).tolist()
+    work = [12.0 * p.d * p.H * visible_pairs([p.lengths[s]]) + 30.0 * int(p.lengths[s]) * D * dm for s in order]
+    off = p.offsets.astype(np.int64)
+
+    def run(seqs):
+        rows = torch.from_numpy(np.concatenate([np.arange(off[s], off[s + 1]) for s in seqs]))
+        sub = synth.LayerProblem(core=synth.subbatch(p, seqs), d_model=dm, X=lp.X.index_select(0, rows), W1=lp.W1,
+                                 W2=lp.W2, b1=lp.b1, b2=lp.b2, dOut=lp.dOut.index_select(0, rows))
+        t0 = time.perf_counter()
+        oracle_layer_bwd(sub)  # runs the layer forward, then the backward
+        return time.perf_counter() - t0
+
+    def take(target):
+        n, acc = 0, 0.0
+        while n < len(order) and (acc < target or n == 0):
+            acc += work[n]
+            n += 1
+        return n, acc
+
+    n0, w0 = take(min(sum(work), 5e10))
+    rate = w0 / max(run(order[:n0]), 1e-6)
+    n1, w1 = take(rate * budget_s)
+    t1 = run(order[:n1])
+    return {"value": w1 / t1 / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n1} of {len(order)} sequences in a seeded order (layer forward + backward, "
+                      f"{w1 / 1e12:.3f} useful TFLOP); {t1:.1f} s of fp64 oracle time with OpenMP on {cores} threads"}
+
+
+def bench_layer(args):
+    """One step = hstu_layer_fwd + hstu_layer_bwd of one batch. Useful FLOPs:
+    12*d per visible pair and head for the attention core, and 2*M*N*K for
+    each of the six projection GEMMs (f1, f2 forward; their input and weight
+    gradients), i.e. 30 * T * D * d_model."""
+    import numpy as np
+    import torch
+
+    from hstu_jagged_pointwise_attn_amd import _lib, api, device, synth
+
+    lp = synth.layer_train_bf16() if args.workload == "layer_train" else synth.layer_long_bf16()
+    p = lp.core
+    D, dm, T = p.H * p.d, lp.d_model, p.T
+    log(f"[bench] layer workload {args.workload}: T={T} D={D} d_model={dm}")
+    ns = device.upload_layer(lp)
+    # the forward keeps U, V, Q, K for the backward (no recomputation from Z)
+    f = device.run_layer_fwd(ns, save_act=True)
+    g = device.run_layer_bwd(ns, f)
+    fws, bws = f.ws, g.ws
+
+    def step():
+        api.layer_fwd(ns.problem, ns.weights, ns.X, Out=f.Out, Z=f.Z, UVQK=f.UVQK, Y=f.Y, O=f.O, mean=f.mean,
+                      rstd=f.rstd, ws=fws)
+        api.layer_bwd(ns.problem, ns.weights, ns.X, f, ns.dOut, dX=g.dX, dW1=g.dW1, db1=g.db1, dW2=g.dW2, db2=g.db2,
+                      d_rab_p=g.d_rab_p, d_rab_t=g.d_rab_t, d_gamma=g.d_gamma, d_beta=g.d_beta, ws=bws)
+
+    pairs = visible_pairs(p.lengths) * p.H
+    attn_flops = 12.0 * p.d * pairs
+    gemm_flops = 30.0 * T * D * dm
+    flops = attn_flops + gemm_flops
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.4f} ms/step, {value:.2f} useful TFLOP/s")
+    api.kernel_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    per_step, per_launch = {}, {}
+    names = ((_lib.HSTU_KERNEL_SCHED, "sched"), (_lib.HSTU_KERNEL_ATTN_FWD, "attn_fwd"),
+             (_lib.HSTU_KERNEL_NORM_FWD, "norm_fwd"), (_lib.HSTU_KERNEL_NORM_BWD, "norm_bwd"),
+             (_lib.HSTU_KERNEL_ATTN_BWD_DQ, "attn_bwd_dq"), (_lib.HSTU_KERNEL_ATTN_BWD_DKDV, "attn_bwd_dkdv"),
+             (_lib.HSTU_KERNEL_AUX, "aux"), (_lib.HSTU_KERNEL_GEMM, "gemm"), (_lib.HSTU_KERNEL_LAYER_EW, "layer_ew"))
+    for kid, kname in names:
+        tms, n = api.kernel_timing_read(kid)
+        if n:
+            per_step[kname] = tms / args.steps
+            per_launch[kname] = tms / n
+    api.kernel_timing(False)
+    log("[bench] per-step ms: " + ", ".join(f"{k}={v:.4f}" for k, v in per_step.items()))
+    # Dominant kernel by time per step: the projection GEMMs (hipBLASLt, six
+    # launches per step, reported together) or one of the attention kernels.
+    kflops = {"attn_fwd": 4.0 * p.d * pairs, "attn_bwd_dq": 4.0 * p.d * pairs, "attn_bwd_dkdv": 4.0 * p.d * pairs,
+              "gemm": gemm_flops}
+    dom = max((k for k in kflops if k in per_step), key=lambda k: per_step[k])
+    achieved = kflops[dom] / (per_step[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": traffic_from_profiles(args.workload, dom) if dom in KERNEL_SOURCES else None,
+                "kernel": dom + (" (6 launches per step)" if dom == "gemm" else ""),
+                "kernel_ms": per_step[dom], "per_kernel_ms_per_step": per_step, "per_launch_ms": per_launch}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline_layer(lp, args.cpu_seconds)
+        log(f"[bench] CPU oracle {cpu['value']:.5f} TFLOP/s")
+    rec = {
+        "metric": "HSTU layer fwd+bwd useful TFLOP/s (attention core + projections, 1 MI355X)", "value": value,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded generators; no dataset)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload, "step": "layer_fwdbwd",
+                   "activations": "U, V, Q, K kept from the forward",
+                   "batch": p.B, "tokens": T, "d_model": dm, "heads": p.H, "d": p.d,
+                   "useful_tflop_per_step": flops / 1e12, "attention_tflop": attn_flops / 1e12,
+                   "gemm_tflop": gemm_flops / 1e12, "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -259,6 +398,8 @@ def main():
     wl = args.workload
     if wl == "batchprep":
         return bench_batchprep(args)
+    if wl.startswith("layer_"):
+        return bench_layer(args)
     log(f"[bench] generating workload {wl}")
     if wl == "mfalcon":
         src = synth.mfalcon_bf16()

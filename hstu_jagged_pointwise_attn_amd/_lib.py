@@ -19,7 +19,7 @@ HSTU_MASK_CAND_TIME_FILTER = 1
 HSTU_COST_TOKENS, HSTU_COST_ATTENTION = 0, 1
 (HSTU_KERNEL_SCHED, HSTU_KERNEL_ATTN_FWD, HSTU_KERNEL_NORM_FWD, HSTU_KERNEL_NORM_BWD, HSTU_KERNEL_ATTN_BWD_DQ,
  HSTU_KERNEL_AUX, HSTU_KERNEL_ATTN_BWD_DKDV, HSTU_KERNEL_STOCHASTIC_LENGTH, HSTU_KERNEL_GATHER,
- HSTU_KERNEL_BALANCE) = range(10)
+ HSTU_KERNEL_BALANCE, HSTU_KERNEL_GEMM, HSTU_KERNEL_LAYER_EW) = range(12)
 HSTU_DEV_BAD_OFFSETS, HSTU_DEV_BAD_SEGMENTS, HSTU_DEV_BAD_GROUP, HSTU_DEV_TOO_LONG = 1, 2, 4, 8
 HSTU_DEV_BAD_TIMESTAMPS = 16
 
@@ -43,6 +43,11 @@ class Problem(ctypes.Structure):
         ("n_groups", ctypes.c_int32), ("mask_flags", ctypes.c_int32),
         ("gamma", _vp), ("beta", _vp),
     ]
+
+
+class LayerWeights(ctypes.Structure):
+    """Mirror of hstu_layer_weights_t (include/hstu.h)."""
+    _fields_ = [("d_model", ctypes.c_int32), ("W1", _vp), ("b1", _vp), ("W2", _vp), ("b2", _vp)]
 
 
 class HSTUError(RuntimeError):
@@ -76,6 +81,12 @@ SIGNATURES = {
                                 _vp, _vp, _vp], ctypes.c_int),
     "hstu_gather_rows": ([_vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp], ctypes.c_int),
     "hstu_balance_bins": ([_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp], ctypes.c_int),
+    "hstu_layer_workspace_size": ([ctypes.POINTER(Problem), ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "hstu_layer_fwd": ([ctypes.POINTER(Problem), ctypes.POINTER(LayerWeights)] + [_vp] * 9
+                       + [ctypes.c_size_t, _vp], ctypes.c_int),
+    "hstu_layer_bwd": ([ctypes.POINTER(Problem), ctypes.POINTER(LayerWeights)] + [_vp] * 18
+                       + [ctypes.c_size_t, _vp], ctypes.c_int),
 }
 
 

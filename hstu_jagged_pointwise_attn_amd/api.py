@@ -267,3 +267,97 @@ def balance_bins(offsets: torch.Tensor, n_bins: int, cost_kind=L.HSTU_COST_TOKEN
     L.check(L.lib().hstu_balance_bins(_ptr(offsets), B, int(n_bins), int(cost_kind), _ptr(b), _ptr(cost),
                                       _stream(stream)))
     return b[:B], cost
+
+
+def layer_weights(W1: torch.Tensor, W2: torch.Tensor, b1=None, b2=None):
+    """The hstu_layer_weights_t of W1 [d_model, 4D], W2 [D, d_model] (the
+    problem's dtype) and the optional fp32 biases b1 [4D], b2 [d_model]."""
+    dm = W1.shape[0]
+    dev = W1.device
+    _need(W1, "W1", None, dev)
+    _need(W2, "W2", W1.dtype, dev, W1.shape[1] // 4 * dm)
+    _need(b1, "b1", torch.float32, dev, W1.shape[1])
+    _need(b2, "b2", torch.float32, dev, dm)
+    w = L.LayerWeights()
+    w.d_model = int(dm)
+    w.W1, w.W2, w.b1, w.b2 = _ptr(W1), _ptr(W2), _ptr(b1), _ptr(b2)
+    w._keep = (W1, W2, b1, b2)
+    return w
+
+
+def layer_workspace_size(p, d_model: int, op) -> int:
+    n = ctypes.c_size_t(0)
+    L.check(L.lib().hstu_layer_workspace_size(ctypes.byref(p), int(d_model), op, ctypes.byref(n)))
+    return int(n.value)
+
+
+def layer_fwd(p, w, X, *, Out=None, Z=None, UVQK=None, save_act=False, Y=None, O=None, mean=None, rstd=None,
+              ws=None, stream=None):
+    """hstu_layer_fwd. X: [T, d_model]. Returns a namespace with Out
+    [T, d_model] and the saved Z [T, 4D], Y, O [T, D], mean, rstd, ws, and
+    UVQK [4, T, D] (the activations, kept for the backward) when save_act is
+    set or UVQK is given (else None)."""
+    T, D, dm = p.total_tokens, p.H * p.d, w.d_model
+    dev, dt = X.device, X.dtype
+    if _DTYPES.get(dt) != p.dtype:
+        raise TypeError("tensor dtype differs from the problem's dtype")
+    _need(X, "X", dt, dev, T * dm)
+    Out = torch.empty(T, dm, dtype=dt, device=dev) if Out is None else Out
+    Z = torch.empty(T, 4 * D, dtype=dt, device=dev) if Z is None else Z
+    if UVQK is None and save_act:
+        UVQK = torch.empty(4, T, D, dtype=dt, device=dev)
+    _need(UVQK, "UVQK", dt, dev, 4 * T * D)
+    Y = torch.empty(T, D, dtype=dt, device=dev) if Y is None else Y
+    O = torch.empty(T, D, dtype=dt, device=dev) if O is None else O
+    mean = torch.empty(T, dtype=torch.float32, device=dev) if mean is None else mean
+    rstd = torch.empty(T, dtype=torch.float32, device=dev) if rstd is None else rstd
+    for t, n, k in ((Out, "Out", T * dm), (Z, "Z", T * 4 * D), (Y, "Y", T * D), (O, "O", T * D)):
+        _need(t, n, dt, dev, k)
+    _need(mean, "mean", torch.float32, dev, T)
+    _need(rstd, "rstd", torch.float32, dev, T)
+    if ws is None:
+        ws = workspace(layer_workspace_size(p, dm, HSTU_OP_FWD), dev)
+    L.check(L.lib().hstu_layer_fwd(ctypes.byref(p), ctypes.byref(w), _ptr(X), _ptr(Out), _ptr(Z), _ptr(UVQK), _ptr(Y),
+                                   _ptr(O), _ptr(mean), _ptr(rstd), _ptr(ws), ws.numel(), _stream(stream)))
+    return SimpleNamespace(Out=Out, Z=Z, UVQK=UVQK, Y=Y, O=O, mean=mean, rstd=rstd, ws=ws)
+
+
+def layer_bwd(p, w, X, f, dOut, *, dX=None, dW1=None, db1=None, dW2=None, db2=None, d_rab_p=None, d_rab_t=None,
+              d_gamma=None, d_beta=None, want_bias=True, want_affine=True, ws=None, stream=None):
+    """hstu_layer_bwd. f: the namespace layer_fwd returned (Z, UVQK, Y, O,
+    mean, rstd; UVQK may be None). Returns a namespace with dX and the fp32 dW1, db1, dW2, db2,
+    d_rab_p, d_rab_t, d_gamma, d_beta (None when not applicable)."""
+    T, D, dm = p.total_tokens, p.H * p.d, w.d_model
+    dev, dt = X.device, X.dtype
+    _need(X, "X", dt, dev, T * dm)
+    _need(dOut, "dOut", dt, dev, T * dm)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dX = torch.empty(T, dm, dtype=dt, device=dev) if dX is None else dX
+    dW1 = torch.empty(dm, 4 * D, **f32) if dW1 is None else dW1
+    dW2 = torch.empty(D, dm, **f32) if dW2 is None else dW2
+    if want_bias:
+        db1 = torch.empty(4 * D, **f32) if db1 is None else db1
+        db2 = torch.empty(dm, **f32) if db2 is None else db2
+    _need(dX, "dX", dt, dev, T * dm)
+    _need(dW1, "dW1", torch.float32, dev, dm * 4 * D)
+    _need(dW2, "dW2", torch.float32, dev, D * dm)
+    _need(db1, "db1", torch.float32, dev, 4 * D)
+    _need(db2, "db2", torch.float32, dev, dm)
+    if p.rab_p and d_rab_p is None:
+        d_rab_p = torch.empty(p.n_pos, **f32)
+    if p.rab_t and d_rab_t is None:
+        d_rab_t = torch.empty(p.n_tb, **f32)
+    G = p.n_groups if p.norm == HSTU_NORM_GLN else 1
+    if want_affine and p.gamma and d_gamma is None:
+        d_gamma = torch.empty(G, D, **f32)
+    if want_affine and p.beta and d_beta is None:
+        d_beta = torch.empty(G, D, **f32)
+    if ws is None:
+        ws = workspace(layer_workspace_size(p, dm, HSTU_OP_BWD), dev)
+    L.check(L.lib().hstu_layer_bwd(
+        ctypes.byref(p), ctypes.byref(w), _ptr(X), _ptr(f.Z), _ptr(getattr(f, "UVQK", None)), _ptr(f.Y), _ptr(f.O),
+        _ptr(f.mean), _ptr(f.rstd),
+        _ptr(dOut), _ptr(dX), _ptr(dW1), _ptr(db1), _ptr(dW2), _ptr(db2), _ptr(d_rab_p), _ptr(d_rab_t),
+        _ptr(d_gamma), _ptr(d_beta), _ptr(ws), ws.numel(), _stream(stream)))
+    return SimpleNamespace(dX=dX, dW1=dW1, db1=db1, dW2=dW2, db2=db2, d_rab_p=d_rab_p, d_rab_t=d_rab_t,
+                           d_gamma=d_gamma, d_beta=d_beta, ws=ws)

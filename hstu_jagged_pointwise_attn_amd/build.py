@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhstu.so")
-SOURCES = ["sched.hip", "attn_fwd.hip", "attn_bwd.hip", "norm.hip", "batching.hip", "api.cpp"]
+SOURCES = ["sched.hip", "attn_fwd.hip", "attn_bwd.hip", "norm.hip", "batching.hip", "layer.hip", "gemm.cpp",
+           "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
@@ -51,7 +52,8 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError("hipcc failed for " + ", ".join(failed))
     tmp = LIB + ".tmp"
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], check=True)
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-L/opt/rocm/lib",
+                    "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"], check=True)
     os.replace(tmp, LIB)
     return LIB
 

@@ -2,6 +2,7 @@
 // sequence of every entry point declared in include/hstu.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -284,6 +285,111 @@ hstu_status_t run_forward(const hstu_problem_t *p, int op, const Layout &L, void
   return HSTU_OK;
 }
 
+
+// ---------------------------------------------------------------- full layer
+
+constexpr size_t kGemmWsBytes = size_t(64) << 20;
+
+// Layer workspace: the core's workspace first (so its status header is the
+// layer's), then the split activations U|V|Q|K (reused for dZ in the
+// backward), and for the backward dY and the core's gradients dU|dV|dQ|dK;
+// last the GEMM workspace.
+struct LayerLayout {
+  size_t core_bytes, act, dy, grads, sums, wpart, gemm, total;
+};
+
+// Weight gradients W[M, N] = A^T B over T rows: split T into S equal chunks
+// (a strided batch of S GEMMs into fp32 slices, then the slices summed) so
+// that the few output tiles still fill the chip.
+constexpr int kMaxSplits = 16;
+int splits_for(long long M, long long N, long long T) {
+  const long long tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  int S = 1;
+  while (S < kMaxSplits && tiles * S * 2 <= 512 && T / (S * 2) >= 512) S *= 2;
+  return S;
+}
+
+LayerLayout layer_layout(const hstu_problem_t *p, int op, int d_model) {
+  LayerLayout y{};
+  y.core_bytes = layout(p, op, 0, 0).total;
+  const size_t esz = p->dtype == HSTU_BF16 ? 2 : 4;
+  const size_t td = (size_t)p->total_tokens * p->H * p->d * esz;
+  size_t off = align256(y.core_bytes);
+  y.act = off;   off += align256(4 * td);
+  if (op == HSTU_OP_BWD) {
+    y.dy = off;    off += align256(td);
+    y.grads = off; off += align256(4 * td);
+    const size_t cols = std::max<size_t>((size_t)4 * p->H * p->d, (size_t)d_model);
+    y.sums = off;  off += align256(sizeof(float) * kColsumGroups * cols);
+    const size_t wmax = std::max<size_t>((size_t)4 * p->H * p->d * d_model, (size_t)p->H * p->d * d_model);
+    y.wpart = off; off += align256(sizeof(float) * (kMaxSplits + 1) * wmax);
+  }
+  y.gemm = off;  off += kGemmWsBytes;
+  y.total = off;
+  return y;
+}
+
+bool aligned16(const void *q) { return ((uintptr_t)q & 15) == 0; }
+
+hstu_status_t check_layer(const hstu_problem_t *p, const hstu_layer_weights_t *w) {
+  if (!w) return fail(HSTU_ERR_INVALID_ARG, "layer weights are NULL");
+  if (w->d_model < 1 || w->d_model > 65536)
+    return fail(HSTU_ERR_INVALID_ARG, "d_model = %d not in [1, 65536]", w->d_model);
+  if (!w->W1 || !w->W2) return fail(HSTU_ERR_INVALID_ARG, "W1/W2 must not be NULL");
+  if (!aligned16(w->W1) || !aligned16(w->W2)) return fail(HSTU_ERR_INVALID_ARG, "W1/W2 must be 16-byte aligned");
+  (void)p;
+  return HSTU_OK;
+}
+
+hstu_status_t gemm_fail(int st, const char *what) {
+  return fail(gemm_unsupported(st) ? HSTU_ERR_UNSUPPORTED : HSTU_ERR_HIP, "%s: %s (status %d)", what,
+              gemm_status_text(st), st);
+}
+
+#define GEMM_RUN(g, what)                                            \
+  do {                                                               \
+    Timed t_(HSTU_KERNEL_GEMM, st);                                  \
+    const int gs_ = gemm_rm((g), at<char>(ws, y.gemm), kGemmWsBytes, st); \
+    if (gs_ != 0) return gemm_fail(gs_, what);                       \
+  } while (0)
+
+GemmRM gemm(bool ta, bool tb, long long M, long long N, long long K, const void *A, long long lda, const void *B,
+            long long ldb, void *C, long long ldc, GemmType ab, GemmType c, const float *bias) {
+  GemmRM g;
+  std::memset(&g, 0, sizeof g);
+  g.ta = ta; g.tb = tb; g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
+  g.ab = ab; g.c = c; g.bias = bias; g.accumulate = false;
+  return g;
+}
+
+// W (fp32 [M, N]) = A^T B for A [T, M], B [T, N] (row-major, dense, element
+// type et), split over T as splits_for() says; `part` holds the slices.
+hstu_status_t weight_grad(const void *A, long long M, const void *B, long long N, long long T, GemmType et, float *W,
+                          float *part, void *ws, const LayerLayout &y, hipStream_t st, const char *what) {
+  const size_t esz = et == kGemmBF16 ? 2 : 4;
+  const int S = splits_for(M, N, T);
+  if (S == 1) {
+    GEMM_RUN(gemm(true, false, M, N, T, A, M, B, N, W, N, et, kGemmF32, nullptr), what);
+    return HSTU_OK;
+  }
+  const long long Tc = T / S, rem = T - Tc * S;
+  GemmRM g = gemm(true, false, M, N, Tc, A, M, B, N, part, N, et, kGemmF32, nullptr);
+  g.batch = S;
+  g.sA = Tc * M;
+  g.sB = Tc * N;
+  g.sC = M * N;
+  GEMM_RUN(g, what);
+  if (rem > 0) {
+    const char *a = static_cast<const char *>(A) + (size_t)(Tc * S) * M * esz;
+    const char *b = static_cast<const char *>(B) + (size_t)(Tc * S) * N * esz;
+    GEMM_RUN(gemm(true, false, M, N, rem, a, M, b, N, part + (size_t)S * M * N, N, et, kGemmF32, nullptr), what);
+  }
+  Timed t_(HSTU_KERNEL_LAYER_EW, st);
+  HIP_TRY(launch_sum_slices(part, S + (rem > 0 ? 1 : 0), M * N, W, st), "slice-sum launch");
+  return HSTU_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -549,6 +655,116 @@ hstu_status_t hstu_balance_bins(const int32_t *offsets, int32_t B, int32_t n_bin
   Timed t_(HSTU_KERNEL_BALANCE, (hipStream_t)stream);
   HIP_TRY(launch_balance(offsets, B, n_bins, cost_kind, bin, (long long *)bin_cost, (hipStream_t)stream),
           "balance launch");
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_layer_workspace_size(const hstu_problem_t *p, int32_t d_model, int32_t op, size_t *bytes) {
+  if (!bytes) return fail(HSTU_ERR_INVALID_ARG, "bytes is NULL");
+  if (op != HSTU_OP_FWD && op != HSTU_OP_BWD) return fail(HSTU_ERR_INVALID_ARG, "op = %d", op);
+  hstu_status_t s = check_problem(p, op);
+  if (s) return s;
+  if (d_model < 1 || d_model > 65536) return fail(HSTU_ERR_INVALID_ARG, "d_model = %d not in [1, 65536]", d_model);
+  *bytes = layer_layout(p, op, d_model).total;
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_layer_fwd(const hstu_problem_t *p, const hstu_layer_weights_t *w, const void *X, void *Out,
+                             void *Z, void *UVQK, void *Y, void *O, float *mean, float *rstd, void *ws,
+                             size_t ws_bytes, void *stream) {
+  hstu_status_t s = check_problem(p, HSTU_OP_FWD);
+  if (s) return s;
+  s = check_layer(p, w);
+  if (s) return s;
+  const long long T = p->total_tokens;
+  if (T > 0 && (!X || !Out || !Z || !Y || !O)) return fail(HSTU_ERR_INVALID_ARG, "X/Out/Z/Y/O must not be NULL");
+  if (!aligned16(X) || !aligned16(Out) || !aligned16(Z) || !aligned16(UVQK) || !aligned16(Y) || !aligned16(O))
+    return fail(HSTU_ERR_INVALID_ARG, "X/Out/Z/UVQK/Y/O must be 16-byte aligned");
+  const LayerLayout y = layer_layout(p, HSTU_OP_FWD, w->d_model);
+  s = check_ws(ws, ws_bytes, y.total);
+  if (s) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf16 = p->dtype == HSTU_BF16;
+  const GemmType et = bf16 ? kGemmBF16 : kGemmF32;
+  const long long D = (long long)p->H * p->d, dm = w->d_model;
+  const size_t td = (size_t)T * D * (bf16 ? 2 : 4);
+  char *act = UVQK ? static_cast<char *>(UVQK) : at<char>(ws, y.act);
+  void *U = act, *V = act + td, *Q = act + 2 * td, *K = act + 3 * td;
+  if (T > 0) GEMM_RUN(gemm(false, false, T, 4 * D, dm, X, dm, w->W1, 4 * D, Z, 4 * D, et, et, w->b1), "f1 GEMM");
+  {
+    Timed t_(HSTU_KERNEL_LAYER_EW, st);
+    HIP_TRY(launch_silu_split(Z, T, (int)D, bf16, U, V, Q, K, st), "SiLU split launch");
+  }
+  s = hstu_attn_fwd(p, Q, K, V, U, Y, O, mean, rstd, ws, y.core_bytes, stream);
+  if (s) return s;
+  if (T > 0) GEMM_RUN(gemm(false, false, T, dm, D, Y, D, w->W2, dm, Out, dm, et, et, w->b2), "f2 GEMM");
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_layer_bwd(const hstu_problem_t *p, const hstu_layer_weights_t *w, const void *X,
+                             const void *Z, const void *UVQK, const void *Y, const void *O, const float *mean,
+                             const float *rstd,
+                             const void *dOut, void *dX, float *dW1, float *db1, float *dW2, float *db2,
+                             float *d_rab_p, float *d_rab_t, float *d_gamma, float *d_beta, void *ws,
+                             size_t ws_bytes, void *stream) {
+  hstu_status_t s = check_problem(p, HSTU_OP_BWD);
+  if (s) return s;
+  s = check_layer(p, w);
+  if (s) return s;
+  const long long T = p->total_tokens;
+  if (!dW1 || !dW2) return fail(HSTU_ERR_INVALID_ARG, "dW1/dW2 must not be NULL");
+  if (T > 0 && (!X || !Z || !Y || !O || !dOut || !dX))
+    return fail(HSTU_ERR_INVALID_ARG, "X/Z/Y/O/dOut/dX must not be NULL");
+  if (!aligned16(X) || !aligned16(Z) || !aligned16(UVQK) || !aligned16(Y) || !aligned16(O) || !aligned16(dOut) ||
+      !aligned16(dX) || !aligned16(dW1) || !aligned16(dW2))
+    return fail(HSTU_ERR_INVALID_ARG, "X/Z/UVQK/Y/O/dOut/dX/dW1/dW2 must be 16-byte aligned");
+  const LayerLayout y = layer_layout(p, HSTU_OP_BWD, w->d_model);
+  s = check_ws(ws, ws_bytes, y.total);
+  if (s) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf16 = p->dtype == HSTU_BF16;
+  const GemmType et = bf16 ? kGemmBF16 : kGemmF32;
+  const long long D = (long long)p->H * p->d, dm = w->d_model;
+  const size_t td = (size_t)T * D * (bf16 ? 2 : 4);
+  char *act = at<char>(ws, y.act), *gr = at<char>(ws, y.grads);
+  void *dY = at<char>(ws, y.dy);
+  float *partial = at<float>(ws, y.sums);
+  float *wpart = at<float>(ws, y.wpart);
+  // U, V, Q, K: the forward's saved activations, or recomputed from Z into ws
+  const char *sv = UVQK ? static_cast<const char *>(UVQK) : act;
+  const void *U = sv, *V = sv + td, *Q = sv + 2 * td, *K = sv + 3 * td;
+  void *dU = gr, *dV = gr + td, *dQ = gr + 2 * td, *dK = gr + 3 * td;
+
+  // f2: dY = dOut W2^T, dW2 = Y^T dOut, db2 = column sums of dOut
+  if (T > 0) {
+    GEMM_RUN(gemm(false, true, T, D, dm, dOut, dm, w->W2, dm, dY, D, et, et, nullptr), "f2 input-gradient GEMM");
+    s = weight_grad(Y, D, dOut, dm, T, et, dW2, wpart, ws, y, st, "f2 weight-gradient GEMM");
+    if (s) return s;
+  }
+  {
+    Timed t_(HSTU_KERNEL_LAYER_EW, st);
+    if (T == 0) HIP_TRY(launch_fill_f32(dW2, D * dm, 0.f, st), "fill");
+    if (db2) HIP_TRY(launch_colsum(dOut, T, (int)dm, bf16, partial, db2, st), "bias-gradient launch");
+    if (!UVQK)
+      HIP_TRY(launch_silu_split(Z, T, (int)D, bf16, act, act + td, act + 2 * td, act + 3 * td, st),
+              "SiLU split launch");
+  }
+  // the attention core
+  s = hstu_attn_bwd(p, Q, K, V, U, O, mean, rstd, dY, dQ, dK, dV, dU, d_rab_p, d_rab_t, d_gamma, d_beta, ws,
+                    y.core_bytes, stream);
+  if (s) return s;
+  // phi1 and f1: dZ = [dU|dV|dQ|dK] * SiLU'(Z) into the activation buffer
+  void *dZ = act;
+  {
+    Timed t_(HSTU_KERNEL_LAYER_EW, st);
+    HIP_TRY(launch_dsilu(Z, dU, dV, dQ, dK, T, (int)D, bf16, dZ, partial, db1, st), "SiLU backward launch");
+    if (T == 0) HIP_TRY(launch_fill_f32(dW1, dm * 4 * D, 0.f, st), "fill");
+  }
+  if (T > 0) {
+    s = weight_grad(X, dm, dZ, 4 * D, T, et, dW1, wpart, ws, y, st, "f1 weight-gradient GEMM");
+    if (s) return s;
+    GEMM_RUN(gemm(false, true, T, dm, 4 * D, dZ, 4 * D, w->W1, 4 * D, dX, dm, et, et, nullptr),
+             "f1 input-gradient GEMM");
+  }
   return HSTU_OK;
 }
 

@@ -155,4 +155,40 @@ hipError_t launch_gather_rows(const void *src, const int *idx, long long n, long
 hipError_t launch_balance(const int *offsets, int B, int n_bins, int cost_kind, int *bin, long long *bin_cost,
                           hipStream_t s);
 
+// Full layer (projections around the core). Row-major GEMM on hipBLASLt:
+// C[M, N] = op(A) op(B) (+ bias over N) (+ C when accumulating); returns a
+// hipblasStatus_t (0 = success).
+enum GemmType { kGemmBF16 = 0, kGemmF32 = 1 };
+struct GemmRM {
+  bool ta, tb;              // op(A) = A^T, op(B) = B^T
+  long long M, N, K;
+  const void *A;            // stored [M, K] (ta false) or [K, M] (ta true), row stride lda
+  long long lda;
+  const void *B;            // stored [K, N] (tb false) or [N, K] (tb true), row stride ldb
+  long long ldb;
+  void *C;                  // [M, N], row stride ldc
+  long long ldc;
+  GemmType ab, c;           // element type of A and B, and of C
+  const float *bias;        // fp32 [N] or NULL
+  bool accumulate;
+  int batch;                // > 1: a strided batch of GEMMs of these sizes
+  long long sA, sB, sC;     // element offsets between consecutive batch entries
+};
+int gemm_rm(const GemmRM &g, void *ws, size_t ws_bytes, hipStream_t s);
+const char *gemm_status_text(int st);
+bool gemm_unsupported(int st);  // no algorithm for the problem
+
+hipError_t launch_silu_split(const void *Z, long long T, int D, bool bf16, void *U, void *V, void *Q, void *K,
+                             hipStream_t s);
+// Column sums run in two passes through a scratch `partial` of
+// kColsumGroups * n floats (n = columns).
+constexpr int kColsumGroups = 1024;
+// db (fp32 [4D], overwritten with the column sums of dZ) may be NULL
+hipError_t launch_dsilu(const void *Z, const void *dU, const void *dV, const void *dQ, const void *dK, long long T,
+                        int D, bool bf16, void *dZ, float *partial, float *db, hipStream_t s);
+// out[i] = sum over s < nslices of slices[s * n + i] (fp32, n elements)
+hipError_t launch_sum_slices(const float *slices, int nslices, long long n, float *out, hipStream_t s);
+// out (fp32 [n]) = column sums of M [T, n]
+hipError_t launch_colsum(const void *M, long long T, int n, bool bf16, float *partial, float *out, hipStream_t s);
+
 }  // namespace hstu

@@ -72,3 +72,27 @@ def run_mfalcon(ns, microbatch=None, **kw):
     mb = ns.src.microbatch if microbatch is None else microbatch
     return api.mfalcon_score(ns.problem, ns.hist_offsets, ns.hist_tokens, ns.hist_max_len, ns.K_cache,
                              ns.V_cache, ns.Qc, ns.Kc, ns.Vc, ns.Uc, hist_ts=ns.hist_ts, microbatch=mb, **kw)
+
+
+def upload_layer(lp, device="cuda"):
+    """Device tensors of a synth.LayerProblem: the core problem (upload), X,
+    the weights and dOut, and the hstu_layer_weights_t."""
+    ns = upload(lp.core, device)
+    dev = ns.device
+    ns.layer = lp
+    ns.X = lp.X.contiguous().to(dev)
+    ns.W1 = lp.W1.contiguous().to(dev)
+    ns.W2 = lp.W2.contiguous().to(dev)
+    ns.b1 = _t(lp.b1, torch.float32, dev)
+    ns.b2 = _t(lp.b2, torch.float32, dev)
+    ns.dOut = None if lp.dOut is None else lp.dOut.contiguous().to(dev)
+    ns.weights = api.layer_weights(ns.W1, ns.W2, ns.b1, ns.b2)
+    return ns
+
+
+def run_layer_fwd(ns, **kw):
+    return api.layer_fwd(ns.problem, ns.weights, ns.X, **kw)
+
+
+def run_layer_bwd(ns, f, **kw):
+    return api.layer_bwd(ns.problem, ns.weights, ns.X, f, ns.dOut, **kw)

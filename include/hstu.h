@@ -34,7 +34,8 @@
  *   - The caller owns every buffer. The library never allocates device
  *     memory: scratch comes from the workspace `ws` of at least
  *     hstu_workspace_size() bytes (256-byte aligned). Concurrent calls need
- *     distinct workspaces.
+ *     distinct workspaces. (The one exception is the hipBLASLt handle that
+ *     the full-layer entry points create per device on first use.)
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = default stream)
  *     and nothing synchronises the host, except where stated. Outputs are
  *     valid once the stream has reached the end of the call.
@@ -263,7 +264,9 @@ enum {
   HSTU_KERNEL_STOCHASTIC_LENGTH = 7,  /* hstu_stochastic_length (both of its kernels) */
   HSTU_KERNEL_GATHER = 8,         /* hstu_gather_rows */
   HSTU_KERNEL_BALANCE = 9,        /* hstu_balance_bins */
-  HSTU_KERNEL_COUNT = 10
+  HSTU_KERNEL_GEMM = 10,          /* the layer's projection GEMMs (hipBLASLt) */
+  HSTU_KERNEL_LAYER_EW = 11,      /* the layer's SiLU / SiLU' / bias-gradient passes */
+  HSTU_KERNEL_COUNT = 12
 };
 hstu_status_t hstu_kernel_timing(int32_t enable);
 hstu_status_t hstu_kernel_timing_read(int32_t kernel, double *total_ms, int64_t *launches);
@@ -308,6 +311,81 @@ hstu_status_t hstu_gather_rows(const void *src, const int32_t *idx, int64_t n, i
 enum { HSTU_COST_TOKENS = 0, HSTU_COST_ATTENTION = 1 };
 hstu_status_t hstu_balance_bins(const int32_t *offsets, int32_t B, int32_t n_bins, int32_t cost_kind,
                                 int32_t *bin, int64_t *bin_cost, void *stream);
+
+/*
+ * Full HSTU layer around the attention core (HSTU blog, section 3, the layer
+ * formula: Q(X) = phi1(f1(X)), the pointwise attention, and
+ * O(X) = f2(Norm(A V) * U)). With D = H*d and X [T, d_model]:
+ *   Z          = X W1 + b1                    [T, 4D]   f1
+ *   U|V|Q|K    = SiLU(Z)                      phi1 = SiLU; the four column
+ *                                             blocks of width D, in this order
+ *   Y, O       = hstu_attn_fwd(p, Q, K, V, U) [T, D]    the attention core
+ *   Out        = Y W2 + b2                    [T, d_model]  f2
+ * The pages name phi1 and the split only for Q; taking SiLU and one 4D-wide
+ * projection for all four is the plainest reading. f1 and f2 run on hipBLASLt
+ * (fp32 accumulation), the SiLU passes and everything else in this library's
+ * kernels.
+ *
+ * Weights (device pointers, row-major, dense):
+ *   d_model  width of X and Out, 1 <= d_model <= 65536
+ *   W1       [d_model, 4D] in the problem's dtype;  b1 fp32 [4D] or NULL
+ *   W2       [D, d_model] in the problem's dtype;   b2 fp32 [d_model] or NULL
+ * X, Out, Z, Y, O, dOut and dX are in the problem's dtype and must be 16-byte
+ * aligned, like W1 and W2.
+ */
+typedef struct hstu_layer_weights {
+  int32_t d_model;
+  const void *W1;
+  const float *b1;
+  const void *W2;
+  const float *b2;
+} hstu_layer_weights_t;
+
+/*
+ * Workspace bytes of hstu_layer_fwd (op = HSTU_OP_FWD) or hstu_layer_bwd
+ * (op = HSTU_OP_BWD) for problem p and width d_model (host only). It holds
+ * the attention core's workspace, the split activations (and their
+ * gradients) and 64 MiB for the GEMMs.
+ */
+hstu_status_t hstu_layer_workspace_size(const hstu_problem_t *p, int32_t d_model, int32_t op, size_t *bytes);
+
+/*
+ * Layer forward. Writes Out [T, d_model] and, for the backward, Z [T, 4D],
+ * Y and O [T, D] and mean, rstd fp32 [T] (NULL allowed when norm == NONE).
+ * UVQK is optional: NULL keeps the activations U, V, Q, K in ws; else they
+ * are written to UVQK [4, T, D] (U, then V, Q, K, each [T, D]) so that the
+ * backward can reuse them instead of recomputing them from Z (4*T*D more
+ * elements of memory for one pass less).
+ * p describes the jagged batch, its masks, rab tables and norm exactly as for
+ * hstu_attn_fwd. The first call on a device creates that device's hipBLASLt
+ * handle, which loads hipBLASLt's kernels; apart from that handle nothing is
+ * allocated (everything else lives in ws). The first call for a new GEMM
+ * size class (token counts are rounded to four classes per octave) times
+ * hipBLASLt's candidate algorithms on `stream` and waits for them; later
+ * calls of the class do not synchronise. Under stream capture the untimed
+ * first candidate is used.
+ */
+hstu_status_t hstu_layer_fwd(const hstu_problem_t *p, const hstu_layer_weights_t *w, const void *X, void *Out,
+                             void *Z, void *UVQK, void *Y, void *O, float *mean, float *rstd, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/*
+ * Layer backward given dOut [T, d_model] and the forward's saved Z, UVQK
+ * (or NULL: recomputed from Z), Y, O, mean, rstd for the same X and weights.
+ * Writes (overwriting):
+ *   dX        [T, d_model] in the problem's dtype
+ *   dW1, dW2  fp32, shaped like W1 and W2 (16-byte aligned)
+ *   db1, db2  fp32 [4D] and [d_model] (NULL skips each)
+ *   d_rab_p, d_rab_t, d_gamma, d_beta  as in hstu_attn_bwd
+ * Sums over tokens run in fp32 (the GEMMs in hipBLASLt's order, the weight
+ * gradients split over token chunks whose partial sums are then added in a
+ * fixed order). The GEMM algorithm choice is made as in hstu_layer_fwd.
+ */
+hstu_status_t hstu_layer_bwd(const hstu_problem_t *p, const hstu_layer_weights_t *w, const void *X,
+                             const void *Z, const void *UVQK, const void *Y, const void *O, const float *mean,
+                             const float *rstd, const void *dOut, void *dX, float *dW1, float *db1, float *dW2,
+                             float *db2, float *d_rab_p, float *d_rab_t, float *d_gamma, float *d_beta, void *ws,
+                             size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -51,3 +51,15 @@ TOL_F32 = 1e-5
 
 def tol(p):
     return TOL_F32 if p.dtype == torch.float32 else TOL_BF16
+
+
+def oracle_layer_fwd(lp):
+    p = lp.core
+    return oracle.layer_fwd(p.offsets, f64(lp.X), f64(lp.W1), f64(lp.W2), b1=f64(lp.b1), b2=f64(lp.b2),
+                            **oracle_opts(p))
+
+
+def oracle_layer_bwd(lp):
+    p = lp.core
+    return oracle.layer_bwd(p.offsets, f64(lp.X), f64(lp.W1), f64(lp.W2), f64(lp.dOut), b1=f64(lp.b1),
+                            b2=f64(lp.b2), **oracle_opts(p))

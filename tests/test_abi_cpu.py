@@ -110,3 +110,50 @@ def test_mfalcon_rejects_prefix_and_cand_len(L):
                                 -1, *([dummy] * 5), 1 << 20, None)
     assert st == L.HSTU_ERR_INVALID_ARG
     del n
+
+
+def _weights(L, dm=16, **kw):
+    w = L.LayerWeights()
+    w.d_model, w.W1, w.W2 = dm, ctypes.c_void_p(0x4000), ctypes.c_void_p(0x8000)
+    for k, v in kw.items():
+        setattr(w, k, v)
+    return w
+
+
+def test_layer_workspace_size(L):
+    p = _problem(L)
+    lib = L.lib()
+    n = ctypes.c_size_t(0)
+    assert lib.hstu_layer_workspace_size(ctypes.byref(p), 16, L.HSTU_OP_FWD, ctypes.byref(n)) == 0
+    _, core = _ws(L, p, L.HSTU_OP_FWD)
+    T, D = p.total_tokens, p.H * p.d
+    assert n.value >= core + 4 * T * D * 2 + (64 << 20) and n.value % 256 == 0
+    nb = ctypes.c_size_t(0)
+    assert lib.hstu_layer_workspace_size(ctypes.byref(p), 16, L.HSTU_OP_BWD, ctypes.byref(nb)) == 0
+    assert nb.value > n.value
+    for dm, op in ((0, L.HSTU_OP_FWD), (70000, L.HSTU_OP_FWD), (16, L.HSTU_OP_MFALCON)):
+        assert lib.hstu_layer_workspace_size(ctypes.byref(p), dm, op, ctypes.byref(n)) == L.HSTU_ERR_INVALID_ARG
+
+
+def test_layer_entry_points_reject_bad_arguments(L):
+    p = _problem(L)
+    lib = L.lib()
+    dummy = ctypes.c_void_p(0x2000)
+    big = ctypes.c_void_p(0x100000)
+    fwd = lambda w, X=dummy, ws=big, n=1 << 40: lib.hstu_layer_fwd(
+        ctypes.byref(p), None if w is None else ctypes.byref(w), X, dummy, dummy, None, dummy, dummy, dummy, dummy,
+        ws, n, None)
+    assert fwd(None) == L.HSTU_ERR_INVALID_ARG
+    assert fwd(_weights(L, dm=0)) == L.HSTU_ERR_INVALID_ARG
+    assert fwd(_weights(L, W1=None)) == L.HSTU_ERR_INVALID_ARG
+    assert fwd(_weights(L, W2=ctypes.c_void_p(0x8004))) == L.HSTU_ERR_INVALID_ARG  # misaligned weight
+    assert fwd(_weights(L), X=ctypes.c_void_p(0x2002)) == L.HSTU_ERR_INVALID_ARG   # misaligned X
+    assert fwd(_weights(L), X=None) == L.HSTU_ERR_INVALID_ARG
+    assert fwd(_weights(L), n=1024) == L.HSTU_ERR_WORKSPACE
+    w = _weights(L)
+    bwd = lambda dW1, n=1 << 40: lib.hstu_layer_bwd(
+        ctypes.byref(p), ctypes.byref(w), dummy, dummy, None, *([dummy] * 5), dummy, dW1, None, dummy, None, None,
+        None, None, None, big, n, None)
+    assert bwd(None) == L.HSTU_ERR_INVALID_ARG
+    assert bwd(ctypes.c_void_p(0x2004)) == L.HSTU_ERR_INVALID_ARG  # misaligned dW1
+    assert bwd(dummy, n=1024) == L.HSTU_ERR_WORKSPACE
