@@ -432,3 +432,96 @@ def layer_train_bf16() -> LayerProblem:
 def layer_long_bf16() -> LayerProblem:
     """The long-sequence shape (long_bf16) as one full layer: d_model = D = 1024."""
     return with_layer(long_bf16(), wid=65)
+
+
+@dataclass
+class StackProblem:
+    """Candidates of B users scored through a stack of HSTU layers against the
+    users' histories (M-FALCON over several layers). X_hist [Th, d_model] and
+    X_cand [Tc, d_model] are the first layer's inputs; `layers` holds one dict
+    per layer with W1 [d_model, 4D], W2 [D, d_model] (the problem's dtype),
+    fp32 b1, b2, and optional fp32 rab_p, rab_t, gamma, beta."""
+    name: str
+    dtype: torch.dtype
+    H: int
+    d: int
+    d_model: int
+    hist_offsets: np.ndarray
+    cand_offsets: np.ndarray
+    X_hist: torch.Tensor
+    X_cand: torch.Tensor
+    layers: list
+    n_max: int
+    microbatch: int
+    norm: int = NORM_LN
+    eps: float = 1e-5
+    hist_ts: Optional[np.ndarray] = None
+    cand_ts: Optional[np.ndarray] = None
+    hist_group: Optional[np.ndarray] = None
+    cand_group: Optional[np.ndarray] = None
+    n_groups: int = 1
+    time_filter: bool = False
+
+    @property
+    def B(self) -> int:
+        return len(self.cand_offsets) - 1
+
+
+def stack_custom(name, hist_len, cand_len, *, n_layers, H, d, d_model=None, dtype=torch.bfloat16, wid=120,
+                 microbatch=0, n_max=None, norm=NORM_LN, x_std=1.0, w_std=0.02, bias_std=0.02, n_pos=0, n_tb=0,
+                 rab_std=0.02, gamma_std=None, beta_std=None, n_groups=1, with_ts=None, x_cand_seed=0) -> StackProblem:
+    """A stack problem with the given history and candidate counts per user.
+    Timestamps: per-user history times as for the attention workloads and
+    candidate times = last history time + floor(Exp(3600)) (made when rab_t
+    is on or with_ts is set). GLN groups: history tokens group 0, candidates
+    group 1 (n_groups = 2). x_cand_seed varies the candidates' inputs only
+    (a new request against the same histories)."""
+    hist_len = np.asarray(hist_len, dtype=np.int64)
+    cand_len = np.asarray(cand_len, dtype=np.int64)
+    B = len(hist_len)
+    D = H * d
+    dm = D if d_model is None else int(d_model)
+    ho, co = _offsets(hist_len), _offsets(cand_len)
+    Th, Tc = int(ho[-1]), int(co[-1])
+    hts = cts = None
+    if n_tb or with_ts:
+        hts = _timestamps(wid, hist_len)
+        rng = _rng(wid, _CTS)
+        base = np.array([hts[ho[b + 1] - 1] if hist_len[b] else 1_700_000_000 for b in range(B)], np.int64)
+        cts = (np.concatenate([base[b] + np.floor(rng.exponential(3600.0, size=int(cand_len[b]))).astype(np.int64)
+                               for b in range(B)]) if Tc else np.zeros(0, np.int64))
+    G = 2 if norm == NORM_GLN else 1
+    layers = []
+    for l in range(n_layers):
+        lw = 1000 * wid + 50 * l  # per-layer seeds
+        lay = {"W1": _normal(lw, _W1, (dm, 4 * D), w_std, dtype), "W2": _normal(lw, _W2, (D, dm), w_std, dtype)}
+        if bias_std is not None:
+            lay["b1"] = _rng(lw, _B1).standard_normal(4 * D, dtype=np.float32) * np.float32(bias_std)
+            lay["b2"] = _rng(lw, _B2).standard_normal(dm, dtype=np.float32) * np.float32(bias_std)
+        if n_pos:
+            lay["rab_p"] = _rng(lw, _RP).standard_normal(n_pos, dtype=np.float32) * np.float32(rab_std)
+        if n_tb:
+            lay["rab_t"] = _rng(lw, _RT).standard_normal(n_tb, dtype=np.float32) * np.float32(rab_std)
+        if gamma_std is not None:
+            lay["gamma"] = (1.0 + _rng(lw, _GAMMA).standard_normal((G, D), dtype=np.float32)
+                            * np.float32(gamma_std)).astype(np.float32)
+        if beta_std is not None:
+            lay["beta"] = (_rng(lw, _GAMMA + 100).standard_normal((G, D), dtype=np.float32)
+                           * np.float32(beta_std)).astype(np.float32)
+        layers.append(lay)
+    return StackProblem(
+        name=name, dtype=dtype, H=H, d=d, d_model=dm, hist_offsets=ho, cand_offsets=co,
+        X_hist=_normal(wid, _X, (Th, dm), x_std, dtype),
+        X_cand=_normal(wid + 7919 * x_cand_seed, _DOUT, (Tc, dm), x_std, dtype),
+        layers=layers, n_max=int(n_max if n_max is not None else max(int((hist_len + cand_len).max()) if B else 1, 1)),
+        microbatch=microbatch, norm=norm, hist_ts=hts, cand_ts=cts,
+        hist_group=np.zeros(Th, np.uint8) if norm == NORM_GLN else None,
+        cand_group=np.ones(Tc, np.uint8) if norm == NORM_GLN else None, n_groups=G)
+
+
+def mfalcon_stack_bf16(n_layers=3) -> StackProblem:
+    """The M-FALCON ranking shape (16 users x 2048 history tokens x 1024
+    candidates, microbatch 256, 8 heads, d = 128, LN, no rab, N_max 3072)
+    through a stack of 3 layers (MTGR-Small's depth) with d_model = D = 1024."""
+    return stack_custom("mfalcon_stack", np.full(16, 2048), np.full(16, 1024), n_layers=n_layers, H=8, d=128,
+                        wid=130, microbatch=256, n_max=3072)

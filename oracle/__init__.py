@@ -333,3 +333,53 @@ def layer_bwd(offsets, X, W1, W2, dOut, *, H, d, b1=None, b2=None, **attn):
     return {"dX": dZ @ W1.T, "dW1": X.T @ dZ, "db1": dZ.sum(0), "dW2": f["Y"].T @ dOut,
             "db2": dOut.sum(0), "dZ": dZ, "dY": dY, "drab_p": g["drab_p"], "drab_t": g["drab_t"],
             "dgamma": g["dgamma"], "dbeta": g["dbeta"]}
+
+
+def mfalcon_stack(hist_offsets, cand_offsets, X_hist, X_cand, layers, *, H, d, hist_ts=None, cand_ts=None,
+                  hist_group=None, cand_group=None, n_groups=1, n_max=1.0, norm=NORM_LN, eps=1e-5,
+                  time_filter=False):
+    """Candidate scoring through a stack of HSTU layers (HSTU blog, sections
+    4.2 and 4.3: a user's history and its candidates form one sequence, every
+    candidate sees the whole history and itself, none sees another). Plain
+    definition, without any cache: for each user the sequence [history |
+    candidates] runs through every layer (``layer_fwd`` with P = 0 and
+    C = number of candidates), each layer's output feeding the next.
+    layers: list of dicts with W1, W2 and optionally b1, b2, rab_p, rab_t,
+    gamma, beta. Returns dict with Out (candidate rows of the last layer,
+    [Tc, d_model]) and Out_hist (history rows, [Th, d_model])."""
+    ho = np.asarray(hist_offsets, dtype=np.int64)
+    co = np.asarray(cand_offsets, dtype=np.int64)
+    B = len(co) - 1
+    Xh, Xc = _f64(X_hist), _f64(X_cand)
+    rows_h, rows_c, lens, cands = [], [], [], []
+    pos = 0
+    for b in range(B):
+        n, m = int(ho[b + 1] - ho[b]), int(co[b + 1] - co[b])
+        rows_h.append(np.arange(pos, pos + n))
+        rows_c.append(np.arange(pos + n, pos + n + m))
+        lens.append(n + m)
+        cands.append(m)
+        pos += n + m
+    rh = np.concatenate(rows_h) if rows_h else np.zeros(0, np.int64)
+    rc = np.concatenate(rows_c) if rows_c else np.zeros(0, np.int64)
+    X = np.zeros((pos, Xh.shape[1] if Xh.ndim == 2 else Xc.shape[1]))
+    X[rh] = Xh
+    X[rc] = Xc
+
+    def interleave(a_h, a_c, dtype):
+        if a_h is None:
+            return None
+        out = np.zeros(pos, dtype=dtype)
+        out[rh] = np.asarray(a_h)
+        out[rc] = np.asarray(a_c)
+        return out
+
+    ts = interleave(hist_ts, cand_ts, np.int64)
+    grp = interleave(hist_group, cand_group, np.uint8)
+    offsets = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    for lay in layers:
+        X = layer_fwd(offsets, X, lay["W1"], lay["W2"], H=H, d=d, b1=lay.get("b1"), b2=lay.get("b2"),
+                      cand_len=np.asarray(cands, np.int32), ts=ts, rab_p=lay.get("rab_p"), rab_t=lay.get("rab_t"),
+                      n_max=n_max, norm=norm, eps=eps, group=grp, n_groups=n_groups, gamma=lay.get("gamma"),
+                      beta=lay.get("beta"), time_filter=time_filter)["Out"]
+    return {"Out": X[rc], "Out_hist": X[rh]}

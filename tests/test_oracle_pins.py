@@ -760,3 +760,87 @@ def test_layer_with_block_identity_weights_is_the_core(oracle_mod):
     for name, want in (("Q", act["q"]), ("K", act["k"]), ("V", act["v"]), ("U", act["u"])):
         np.testing.assert_allclose(f[name], want, rtol=1e-14, atol=1e-300, err_msg=name)
     np.testing.assert_allclose(f["Out"], core["Y"], rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------ layer stack, M-FALCON
+
+def _stack_small(**kw):
+    args = dict(n_layers=2, H=2, d=4, d_model=6, dtype=torch.float32, wid=140, x_std=1.0, w_std=0.4,
+                bias_std=0.3, n_pos=16, n_tb=8, rab_std=0.3, gamma_std=0.3, beta_std=0.3)
+    args.update(kw)
+    return synth.stack_custom("stack_small", [7, 0, 12], [3, 2, 5], **args)
+
+
+def _stack_run(oracle_mod, sp, hist_rows=None, cand_rows=None):
+    """oracle.mfalcon_stack on sp, optionally restricted to some history or
+    candidate rows (per-user counts recomputed)."""
+    def sel(offsets, rows):
+        off = np.asarray(offsets, np.int64)
+        if rows is None:
+            return off, np.arange(off[-1])
+        rows = np.asarray(sorted(rows), np.int64)
+        counts = [int(((rows >= off[b]) & (rows < off[b + 1])).sum()) for b in range(len(off) - 1)]
+        return np.concatenate([[0], np.cumsum(counts)]), rows
+    ho, hr = sel(sp.hist_offsets, hist_rows)
+    co, cr = sel(sp.cand_offsets, cand_rows)
+    f = lambda t: t.double().numpy()
+    return oracle_mod.mfalcon_stack(
+        ho, co, f(sp.X_hist)[hr], f(sp.X_cand)[cr], sp.layers, H=sp.H, d=sp.d,
+        hist_ts=None if sp.hist_ts is None else sp.hist_ts[hr], cand_ts=None if sp.cand_ts is None else sp.cand_ts[cr],
+        n_max=sp.n_max, norm=sp.norm, eps=sp.eps, time_filter=sp.time_filter), cr
+
+
+def test_stack_history_rows_ignore_candidates(oracle_mod):
+    sp = _stack_small()
+    full, _ = _stack_run(oracle_mod, sp)
+    none, _ = _stack_run(oracle_mod, sp, cand_rows=[])
+    np.testing.assert_allclose(full["Out_hist"], none["Out_hist"], rtol=1e-12, atol=1e-14)
+
+
+def test_stack_candidates_ignore_each_other(oracle_mod):
+    sp = _stack_small()
+    full, _ = _stack_run(oracle_mod, sp)
+    keep = [r for r in range(int(sp.cand_offsets[-1])) if r not in (1, 5, 6)]
+    part, cr = _stack_run(oracle_mod, sp, cand_rows=keep)
+    np.testing.assert_allclose(part["Out"], full["Out"][cr], rtol=1e-12, atol=1e-14)
+
+
+def test_stack_cached_layers_equal_full_pass(oracle_mod):
+    """Layer by layer with per-layer history K/V caches (layer_fwd over the
+    histories alone) and oracle.mfalcon for the candidates equals the full
+    pass over [history | candidates]: the history K/V of every layer is all a
+    candidate needs."""
+    for tf in (False, True):
+        sp = _stack_small()
+        sp.time_filter = tf
+        ref, _ = _stack_run(oracle_mod, sp)
+        D = sp.H * sp.d
+        Xh, Xc = sp.X_hist.double().numpy(), sp.X_cand.double().numpy()
+        for lay in sp.layers:
+            h = oracle_mod.layer_fwd(sp.hist_offsets, Xh, lay["W1"], lay["W2"], H=sp.H, d=sp.d, b1=lay.get("b1"),
+                                     b2=lay.get("b2"), ts=sp.hist_ts, rab_p=lay.get("rab_p"), rab_t=lay.get("rab_t"),
+                                     n_max=sp.n_max, norm=sp.norm, eps=sp.eps, gamma=lay.get("gamma"),
+                                     beta=lay.get("beta"))
+            Zc = Xc @ np.asarray(lay["W1"].double()) + lay["b1"]
+            A = torch.nn.functional.silu(torch.tensor(Zc)).numpy()
+            Uc, Vc, Qc, Kc = (A[:, i * D:(i + 1) * D] for i in range(4))
+            m = oracle_mod.mfalcon(sp.hist_offsets, sp.cand_offsets, h["K"], h["V"], Qc, Kc, Vc, Uc, H=sp.H, d=sp.d,
+                                   hist_ts=sp.hist_ts, cand_ts=sp.cand_ts, rab_p=lay.get("rab_p"),
+                                   rab_t=lay.get("rab_t"), n_max=sp.n_max, norm=sp.norm, eps=sp.eps,
+                                   gamma=lay.get("gamma"), beta=lay.get("beta"), time_filter=tf)
+            Xc = m["Y"] @ np.asarray(lay["W2"].double()) + lay["b2"]
+            Xh = h["Out"]
+        np.testing.assert_allclose(Xc, ref["Out"], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(Xh, ref["Out_hist"], rtol=1e-10, atol=1e-12)
+
+
+def test_stack_candidate_permutation_permutes_outputs(oracle_mod):
+    sp = _stack_small()
+    ref, _ = _stack_run(oracle_mod, sp)
+    perm = np.arange(int(sp.cand_offsets[-1]))
+    perm[5:10] = perm[5:10][::-1]  # reverse the last user's candidates
+    sp2 = _stack_small()
+    sp2.X_cand = sp.X_cand[torch.from_numpy(perm)]
+    sp2.cand_ts = sp.cand_ts[perm]
+    got, _ = _stack_run(oracle_mod, sp2)
+    np.testing.assert_allclose(got["Out"], ref["Out"][perm], rtol=1e-12, atol=1e-14)
