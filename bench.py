@@ -47,6 +47,9 @@ WORKLOAD_TEXT = {
     "layer_long": "Full HSTU layer fwd+bwd bf16 on the long-sequence shape: X [T, 1024] -> f1 (1024 x 4096, bias) -> "
                   "SiLU -> U|V|Q|K -> attention (32 sequences, median 2048, 8 heads, d=128, causal, rab_p/rab_t, LN, "
                   "N_max 8192) -> f2 (1024 x 1024, bias)",
+    "mfalcon_stack": "M-FALCON serving through 3 HSTU layers bf16: 16 users x 2048 history tokens (per-layer K/V "
+                     "caches built once by a history pass) x 1024 candidates scored in microbatches of 256 per layer, "
+                     "8 heads, d=128, d_model=1024, LN, N_max 3072",
     "batchprep": "Batch preparation of the training shape: 128 sequences (truncated Pareto(1.2), mean 776, max "
                  "4096) cut to the Stochastic Length budget 776 on the device, Q/K/V/U (4 heads, d=128, bf16) and "
                  "timestamps gathered, then 8 work-balanced bins by attention cost",
@@ -369,6 +372,160 @@ def bench_layer(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_stack(args):
+    """One step = hstu_stack_score of all candidates through the 3 layers
+    against caches built once (untimed) by hstu_stack_history. Useful FLOPs
+    per layer: 4*d per (candidate, visible history key or itself) pair and
+    head, and 2*Tc*d_model*4D + 2*Tc*D*d_model for the two projections. Also
+    reports the latency of a small request (one user, 128 candidates) run
+    eagerly and as a replayed HIP graph."""
+    import numpy as np
+    import torch
+
+    from hstu_jagged_pointwise_attn_amd import _lib, api, device, synth
+
+    sp = synth.mfalcon_stack_bf16()
+    ns = device.upload_stack(sp)
+    D, dm, nl = sp.H * sp.d, sp.d_model, len(sp.layers)
+    Tc = int(sp.cand_offsets[-1])
+    log(f"[bench] stack: {sp.B} users, Th={ns.hist_tokens}, Tc={Tc}, {nl} layers")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    device.run_stack_history(ns)
+    torch.cuda.synchronize()
+    hist_ms_first = (time.perf_counter() - t0) * 1e3
+    h = device.run_stack_history(ns)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    device.run_stack_history(ns, Out=h.Out, ws=h.ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    hist_ms = e0.elapsed_time(e1)
+    s0 = device.run_stack_score(ns)
+
+    def step():
+        device.run_stack_score(ns, Out=s0.Out, ws=s0.ws)
+
+    pairs = sum(int(np.diff(sp.cand_offsets)[u]) * (int(np.diff(sp.hist_offsets)[u]) + 1) for u in range(sp.B)) * sp.H
+    attn_flops = nl * 4.0 * sp.d * pairs
+    gemm_flops = nl * 10.0 * Tc * D * dm
+    flops = attn_flops + gemm_flops
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.4f} ms/step, {value:.2f} useful TFLOP/s, {Tc / (ms * 1e-3):.3e} candidates/s")
+    api.kernel_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    per_step = {}
+    for kid, kname in ((_lib.HSTU_KERNEL_SCHED, "sched"), (_lib.HSTU_KERNEL_ATTN_FWD, "attn_fwd"),
+                       (_lib.HSTU_KERNEL_NORM_FWD, "norm_fwd"), (_lib.HSTU_KERNEL_GEMM, "gemm"),
+                       (_lib.HSTU_KERNEL_LAYER_EW, "layer_ew")):
+        tms, n = api.kernel_timing_read(kid)
+        if n:
+            per_step[kname] = tms / args.steps
+    api.kernel_timing(False)
+    log("[bench] per-step ms: " + ", ".join(f"{k}={v:.4f}" for k, v in per_step.items()))
+    kflops = {"attn_fwd": attn_flops, "gemm": gemm_flops}
+    dom = max((k for k in kflops if k in per_step), key=lambda k: per_step[k])
+    achieved = kflops[dom] / (per_step[dom] * 1e-3) / 1e12
+
+    # a small request: one user, 2048 history tokens, 128 candidates; eager vs graph replay
+    small = synth.stack_custom("stack_small_request", [2048], [128], n_layers=nl, H=sp.H, d=sp.d, wid=131,
+                               microbatch=128, n_max=sp.n_max)
+    nsm = device.upload_stack(small)
+    device.run_stack_history(nsm)
+    sm = device.run_stack_score(nsm)
+    torch.cuda.synchronize()
+    graph, gout = api.stack_score_capture(nsm.cand_problem, nsm.layers, nsm.hist_offsets, nsm.hist_tokens,
+                                          nsm.hist_max_len, nsm.X_cand, hist_ts=nsm.hist_ts,
+                                          microbatch=small.microbatch)
+    reps = 50
+
+    def timed(fn, wait_each):
+        """Wall time per request: back to back (throughput), or waiting for
+        each request before issuing the next (latency)."""
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn()
+            if wait_each:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e3 / reps
+
+    run_eager = lambda: device.run_stack_score(nsm, Out=sm.Out, ws=sm.ws)
+    eager_ms, graph_ms = timed(run_eager, False), timed(graph.launch, False)
+    eager_lat, graph_lat = timed(run_eager, True), timed(graph.launch, True)
+    log(f"[bench] small request: back-to-back eager {eager_ms:.3f} ms, graph {graph_ms:.3f} ms; "
+        f"latency eager {eager_lat:.3f} ms, graph {graph_lat:.3f} ms")
+    del graph
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline_stack(sp, args.cpu_seconds, (attn_flops + gemm_flops) / sp.B)
+        log(f"[bench] CPU oracle {cpu['value']:.5f} TFLOP/s")
+    rec = {
+        "metric": "M-FALCON multi-layer candidate scoring useful TFLOP/s (1 MI355X)", "value": value,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded generators; no dataset)",
+        "config": {"workload": WORKLOAD_TEXT["mfalcon_stack"], "name": "mfalcon_stack", "step": "stack_score",
+                   "users": sp.B, "history": int(np.diff(sp.hist_offsets)[0]),
+                   "candidates": int(np.diff(sp.cand_offsets)[0]), "microbatch": sp.microbatch, "layers": nl,
+                   "heads": sp.H, "d": sp.d, "d_model": dm, "candidates_per_s": Tc / (ms * 1e-3),
+                   "history_pass_ms": hist_ms, "history_pass_first_call_ms": hist_ms_first,
+                   "useful_tflop_per_step": flops / 1e12, "attention_tflop": attn_flops / 1e12,
+                   "gemm_tflop": gemm_flops / 1e12,
+                   "small_request": {"users": 1, "history": 2048, "candidates": 128,
+                                     "back_to_back_ms": {"eager": eager_ms, "graph": graph_ms},
+                                     "latency_ms": {"eager": eager_lat, "graph": graph_lat}}},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": dom + (" (2 launches per layer)" if dom == "gemm" else f" ({nl} launches)"),
+                     "kernel_ms": per_step[dom], "per_kernel_ms_per_step": per_step},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_stack(sp, budget_s, flops_per_user):
+    """The oracle's full pass (oracle.mfalcon_stack) on as many users of the
+    stack workload as fit about budget_s (users are the same size)."""
+    import oracle
+    from tests.common import f64_layers
+
+    oracle.build(force=False)
+    cores = os.cpu_count() or 1
+    layers = f64_layers(sp.layers)
+    f = lambda t: t.double().numpy()
+
+    def run(n):
+        he, ce = int(sp.hist_offsets[n]), int(sp.cand_offsets[n])
+        t0 = time.perf_counter()
+        oracle.mfalcon_stack(sp.hist_offsets[:n + 1], sp.cand_offsets[:n + 1], f(sp.X_hist[:he]), f(sp.X_cand[:ce]),
+                             layers, H=sp.H, d=sp.d, n_max=sp.n_max, norm=sp.norm, eps=sp.eps)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    n = max(1, min(sp.B, int(budget_s / max(t1, 1e-3))))
+    t = run(n) if n > 1 else t1
+    return {"value": n * flops_per_user / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of {sp.B} users (full pass over history + candidates, all layers); "
+                      f"{t:.1f} s of fp64 oracle time with OpenMP on {cores} threads"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -400,6 +557,8 @@ def main():
         return bench_batchprep(args)
     if wl.startswith("layer_"):
         return bench_layer(args)
+    if wl == "mfalcon_stack":
+        return bench_stack(args)
     log(f"[bench] generating workload {wl}")
     if wl == "mfalcon":
         src = synth.mfalcon_bf16()

@@ -50,6 +50,12 @@ class LayerWeights(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("W1", _vp), ("b1", _vp), ("W2", _vp), ("b2", _vp)]
 
 
+class StackLayer(ctypes.Structure):
+    """Mirror of hstu_stack_layer_t (include/hstu.h)."""
+    _fields_ = [("w", LayerWeights), ("rab_p", _vp), ("rab_t", _vp), ("gamma", _vp), ("beta", _vp),
+                ("K_cache", _vp), ("V_cache", _vp)]
+
+
 class HSTUError(RuntimeError):
     def __init__(self, status, message):
         super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
@@ -87,6 +93,17 @@ SIGNATURES = {
                        + [ctypes.c_size_t, _vp], ctypes.c_int),
     "hstu_layer_bwd": ([ctypes.POINTER(Problem), ctypes.POINTER(LayerWeights)] + [_vp] * 18
                        + [ctypes.c_size_t, _vp], ctypes.c_int),
+    "hstu_stack_workspace_size": ([ctypes.POINTER(Problem), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "hstu_stack_history": ([ctypes.POINTER(Problem), ctypes.c_int32, ctypes.POINTER(StackLayer), _vp, _vp, _vp,
+                            ctypes.c_size_t, _vp], ctypes.c_int),
+    "hstu_stack_score": ([ctypes.POINTER(Problem), ctypes.c_int32, ctypes.POINTER(StackLayer), _vp, ctypes.c_int64,
+                          ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    "hstu_stack_score_capture": ([ctypes.POINTER(Problem), ctypes.c_int32, ctypes.POINTER(StackLayer), _vp,
+                                  ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t,
+                                  ctypes.POINTER(_vp)], ctypes.c_int),
+    "hstu_graph_launch": ([_vp, _vp], ctypes.c_int),
+    "hstu_graph_destroy": ([_vp], ctypes.c_int),
 }
 
 

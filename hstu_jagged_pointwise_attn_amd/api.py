@@ -32,7 +32,8 @@ def _need(t, name, dtype=None, device=None, numel=None):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on the GPU, got {t.device}")
-    if device is not None and t.device != device:
+    if device is not None and (t.device.type != device.type or
+                               (device.index is not None and t.device.index != device.index)):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -361,3 +362,102 @@ def layer_bwd(p, w, X, f, dOut, *, dX=None, dW1=None, db1=None, dW2=None, db2=No
         _ptr(d_gamma), _ptr(d_beta), _ptr(ws), ws.numel(), _stream(stream)))
     return SimpleNamespace(dX=dX, dW1=dW1, db1=db1, dW2=dW2, db2=db2, d_rab_p=d_rab_p, d_rab_t=d_rab_t,
                            d_gamma=d_gamma, d_beta=d_beta, ws=ws)
+
+
+def stack_layers(layers, H, d, dtype, device, K_caches=None, V_caches=None, hist_tokens=0):
+    """The hstu_stack_layer_t array of a list of per-layer dicts (W1, W2 in
+    dtype; optional fp32 b1, b2, rab_p, rab_t, gamma, beta; device tensors).
+    K/V caches ([Th, H, d] each per layer) are allocated when not given.
+    Returns (ctypes array, K_caches, V_caches)."""
+    n = len(layers)
+    arr = (L.StackLayer * n)()
+    Ks = K_caches or [torch.empty(hist_tokens, H, d, dtype=dtype, device=device) for _ in range(n)]
+    Vs = V_caches or [torch.empty(hist_tokens, H, d, dtype=dtype, device=device) for _ in range(n)]
+    keep = []
+    for i, lay in enumerate(layers):
+        w = layer_weights(lay["W1"], lay["W2"], lay.get("b1"), lay.get("b2"))
+        arr[i].w = w
+        for name in ("rab_p", "rab_t", "gamma", "beta"):
+            t = lay.get(name)
+            _need(t, name, torch.float32, device)
+            setattr(arr[i], name, _ptr(t))
+        _need(Ks[i], "K_cache", dtype, device, hist_tokens * H * d)
+        _need(Vs[i], "V_cache", dtype, device, hist_tokens * H * d)
+        arr[i].K_cache, arr[i].V_cache = _ptr(Ks[i]), _ptr(Vs[i])
+        keep.append((w, lay))
+    arr._keep = (keep, Ks, Vs)
+    return arr, Ks, Vs
+
+
+def stack_workspace_size(p, d_model, op, microbatch=0, hist_max_len=0, hist_tokens=0) -> int:
+    n = ctypes.c_size_t(0)
+    L.check(L.lib().hstu_stack_workspace_size(ctypes.byref(p), int(d_model), op, int(microbatch), int(hist_max_len),
+                                              int(hist_tokens), ctypes.byref(n)))
+    return int(n.value)
+
+
+def stack_history(hist_p, layers, X, *, Out=None, ws=None, stream=None):
+    """hstu_stack_history. layers: the array from stack_layers. Returns a
+    namespace with Out ([Th, d_model], the last layer's output) and ws."""
+    dm = layers[0].w.d_model
+    T, dev, dt = hist_p.total_tokens, X.device, X.dtype
+    _need(X, "X", dt, dev, T * dm)
+    Out = torch.empty(T, dm, dtype=dt, device=dev) if Out is None else Out
+    _need(Out, "Out", dt, dev, T * dm)
+    if ws is None:
+        ws = workspace(stack_workspace_size(hist_p, dm, HSTU_OP_FWD), dev)
+    L.check(L.lib().hstu_stack_history(ctypes.byref(hist_p), len(layers), layers, _ptr(X), _ptr(Out), _ptr(ws),
+                                       ws.numel(), _stream(stream)))
+    return SimpleNamespace(Out=Out, ws=ws)
+
+
+def _stack_score_args(cand_p, layers, hist_offsets, hist_tokens, hist_max_len, hist_ts, microbatch, Xc, Out, ws):
+    dm = layers[0].w.d_model
+    T, dev, dt = cand_p.total_tokens, Xc.device, Xc.dtype
+    _need(Xc, "Xc", dt, dev, T * dm)
+    _need(hist_offsets, "hist_offsets", torch.int32, dev, cand_p.B + 1)
+    _need(hist_ts, "hist_ts", torch.int64, dev, int(hist_tokens))
+    Out = torch.empty(T, dm, dtype=dt, device=dev) if Out is None else Out
+    _need(Out, "Out", dt, dev, T * dm)
+    if ws is None:
+        ws = workspace(stack_workspace_size(cand_p, dm, HSTU_OP_MFALCON, microbatch, hist_max_len, hist_tokens), dev)
+    args = (ctypes.byref(cand_p), len(layers), layers, _ptr(hist_offsets), int(hist_tokens), int(hist_max_len),
+            _ptr(hist_ts), int(microbatch), _ptr(Xc), _ptr(Out), _ptr(ws), ws.numel())
+    return args, Out, ws
+
+
+def stack_score(cand_p, layers, hist_offsets, hist_tokens, hist_max_len, Xc, *, hist_ts=None, microbatch=0,
+                Out=None, ws=None, stream=None):
+    """hstu_stack_score. Returns a namespace with Out ([Tc, d_model]) and ws."""
+    args, Out, ws = _stack_score_args(cand_p, layers, hist_offsets, hist_tokens, hist_max_len, hist_ts, microbatch,
+                                      Xc, Out, ws)
+    L.check(L.lib().hstu_stack_score(*args, _stream(stream)))
+    return SimpleNamespace(Out=Out, ws=ws)
+
+
+class Graph:
+    """An executable HIP graph of one hstu_stack_score call
+    (hstu_stack_score_capture); launch() replays it, the graph is freed
+    with the object. Keeps the captured buffers alive."""
+
+    def __init__(self, handle, keep):
+        self._h = handle
+        self._keep = keep
+
+    def launch(self, stream=None):
+        L.check(L.lib().hstu_graph_launch(self._h, _stream(stream)))
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            L.lib().hstu_graph_destroy(self._h)
+            self._h = None
+
+
+def stack_score_capture(cand_p, layers, hist_offsets, hist_tokens, hist_max_len, Xc, *, hist_ts=None,
+                        microbatch=0, Out=None, ws=None):
+    """hstu_stack_score_capture. Returns (Graph, namespace with Out and ws)."""
+    args, Out, ws = _stack_score_args(cand_p, layers, hist_offsets, hist_tokens, hist_max_len, hist_ts, microbatch,
+                                      Xc, Out, ws)
+    h = ctypes.c_void_p(0)
+    L.check(L.lib().hstu_stack_score_capture(*args, ctypes.byref(h)))
+    return Graph(h, (cand_p, layers, hist_offsets, hist_ts, Xc, Out, ws)), SimpleNamespace(Out=Out, ws=ws)

@@ -67,6 +67,8 @@ struct Timed {
   Timed(int k, hipStream_t s) : kernel(k), st(s) {
     std::lock_guard<std::mutex> g(g_timing_mu);
     if (!g_timing_on) return;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
     if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
       a = b = nullptr;
       return;
@@ -349,7 +351,7 @@ hstu_status_t gemm_fail(int st, const char *what) {
 #define GEMM_RUN(g, what)                                            \
   do {                                                               \
     Timed t_(HSTU_KERNEL_GEMM, st);                                  \
-    const int gs_ = gemm_rm((g), at<char>(ws, y.gemm), kGemmWsBytes, st); \
+    const int gs_ = gemm_rm((g), gws, kGemmWsBytes, st);           \
     if (gs_ != 0) return gemm_fail(gs_, what);                       \
   } while (0)
 
@@ -366,7 +368,7 @@ GemmRM gemm(bool ta, bool tb, long long M, long long N, long long K, const void 
 // W (fp32 [M, N]) = A^T B for A [T, M], B [T, N] (row-major, dense, element
 // type et), split over T as splits_for() says; `part` holds the slices.
 hstu_status_t weight_grad(const void *A, long long M, const void *B, long long N, long long T, GemmType et, float *W,
-                          float *part, void *ws, const LayerLayout &y, hipStream_t st, const char *what) {
+                          float *part, void *gws, hipStream_t st, const char *what) {
   const size_t esz = et == kGemmBF16 ? 2 : 4;
   const int S = splits_for(M, N, T);
   if (S == 1) {
@@ -658,6 +660,96 @@ hstu_status_t hstu_balance_bins(const int32_t *offsets, int32_t B, int32_t n_bin
   return HSTU_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------- layer stacks
+
+// Workspace of a stack call: the core's workspace first, then per-layer
+// scratch reused by every layer (Z [T, 4D]; U, V, Q, K, Y, O [T, D]; mean,
+// rstd [T]), two [T, d_model] buffers the layers alternate between, and
+// the GEMM workspace.
+struct StackLayout {
+  size_t core_bytes, z, u, v, q, k, yo, o, mean, rstd, x[2], gemm, total;
+};
+
+StackLayout stack_layout(const hstu_problem_t *p, int op, int d_model, int microbatch, int hist_max_len) {
+  StackLayout y{};
+  y.core_bytes = layout(p, op, microbatch, hist_max_len).total;
+  const size_t esz = p->dtype == HSTU_BF16 ? 2 : 4;
+  const size_t T = (size_t)p->total_tokens, D = (size_t)p->H * p->d;
+  size_t off = align256(y.core_bytes);
+  y.z = off;    off += align256(4 * T * D * esz);
+  y.u = off;    off += align256(T * D * esz);
+  y.v = off;    off += align256(T * D * esz);
+  y.q = off;    off += align256(T * D * esz);
+  y.k = off;    off += align256(T * D * esz);
+  y.yo = off;   off += align256(T * D * esz);
+  y.o = off;    off += align256(T * D * esz);
+  y.mean = off; off += align256(T * sizeof(float));
+  y.rstd = off; off += align256(T * sizeof(float));
+  y.x[0] = off; off += align256(T * d_model * esz);
+  y.x[1] = off; off += align256(T * d_model * esz);
+  y.gemm = off; off += kGemmWsBytes;
+  y.total = off;
+  return y;
+}
+
+// The problem of one layer: the caller's batch with this layer's tables and
+// affine.
+hstu_problem_t layer_problem(const hstu_problem_t *p, const hstu_stack_layer_t &L) {
+  hstu_problem_t q = *p;
+  q.rab_p = L.rab_p;
+  q.rab_t = L.rab_t;
+  q.gamma = L.gamma;
+  q.beta = L.beta;
+  return q;
+}
+
+hstu_status_t check_stack(const hstu_problem_t *p, int n_layers, const hstu_stack_layer_t *layers,
+                          long long cache_tokens) {
+  if (n_layers < 1 || n_layers > 64) return fail(HSTU_ERR_INVALID_ARG, "n_layers = %d not in [1, 64]", n_layers);
+  if (!layers) return fail(HSTU_ERR_INVALID_ARG, "layers is NULL");
+  for (int l = 0; l < n_layers; ++l) {
+    const hstu_stack_layer_t &L = layers[l];
+    hstu_status_t s = check_layer(p, &L.w);
+    if (s) return s;
+    if (L.w.d_model != layers[0].w.d_model) return fail(HSTU_ERR_INVALID_ARG, "layer %d: d_model differs", l);
+    if (L.rab_p && p->n_pos < 1) return fail(HSTU_ERR_INVALID_ARG, "layer %d: rab_p given with n_pos = %d", l, p->n_pos);
+    if (L.rab_t && p->n_tb < 1) return fail(HSTU_ERR_INVALID_ARG, "layer %d: rab_t given with n_tb = %d", l, p->n_tb);
+    if (cache_tokens > 0 && (!L.K_cache || !L.V_cache))
+      return fail(HSTU_ERR_INVALID_ARG, "layer %d: K_cache/V_cache must not be NULL", l);
+    if (!aligned16(L.K_cache) || !aligned16(L.V_cache))
+      return fail(HSTU_ERR_INVALID_ARG, "layer %d: K_cache/V_cache must be 16-byte aligned", l);
+  }
+  return HSTU_OK;
+}
+
+// One layer forward with the activations at U, V, Q, K ([T, D] each): f1
+// GEMM, SiLU + split, the attention core (workspace ws_core of core_bytes),
+// f2 GEMM. Arguments are checked by the callers.
+hstu_status_t layer_forward(const hstu_problem_t *p, const hstu_layer_weights_t *w, const void *X, void *Out,
+                            void *Z, void *U, void *V, void *Q, void *K, void *Y, void *O, float *mean, float *rstd,
+                            void *ws_core, size_t core_bytes, void *gws, hipStream_t st) {
+  const long long T = p->total_tokens;
+  const bool bf16 = p->dtype == HSTU_BF16;
+  const GemmType et = bf16 ? kGemmBF16 : kGemmF32;
+  const long long D = (long long)p->H * p->d, dm = w->d_model;
+  if (T > 0) GEMM_RUN(gemm(false, false, T, 4 * D, dm, X, dm, w->W1, 4 * D, Z, 4 * D, et, et, w->b1), "f1 GEMM");
+  {
+    Timed t_(HSTU_KERNEL_LAYER_EW, st);
+    HIP_TRY(launch_silu_split(Z, T, (int)D, bf16, U, V, Q, K, st), "SiLU split launch");
+  }
+  hstu_status_t s = hstu_attn_fwd(p, Q, K, V, U, Y, O, mean, rstd, ws_core, core_bytes, st);
+  if (s) return s;
+  if (T > 0) GEMM_RUN(gemm(false, false, T, dm, D, Y, D, w->W2, dm, Out, dm, et, et, w->b2), "f2 GEMM");
+  return HSTU_OK;
+}
+}  // namespace
+
+extern "C" {
+
 hstu_status_t hstu_layer_workspace_size(const hstu_problem_t *p, int32_t d_model, int32_t op, size_t *bytes) {
   if (!bytes) return fail(HSTU_ERR_INVALID_ARG, "bytes is NULL");
   if (op != HSTU_OP_FWD && op != HSTU_OP_BWD) return fail(HSTU_ERR_INVALID_ARG, "op = %d", op);
@@ -682,22 +774,10 @@ hstu_status_t hstu_layer_fwd(const hstu_problem_t *p, const hstu_layer_weights_t
   const LayerLayout y = layer_layout(p, HSTU_OP_FWD, w->d_model);
   s = check_ws(ws, ws_bytes, y.total);
   if (s) return s;
-  hipStream_t st = (hipStream_t)stream;
-  const bool bf16 = p->dtype == HSTU_BF16;
-  const GemmType et = bf16 ? kGemmBF16 : kGemmF32;
-  const long long D = (long long)p->H * p->d, dm = w->d_model;
-  const size_t td = (size_t)T * D * (bf16 ? 2 : 4);
+  const size_t td = (size_t)T * p->H * p->d * (p->dtype == HSTU_BF16 ? 2 : 4);
   char *act = UVQK ? static_cast<char *>(UVQK) : at<char>(ws, y.act);
-  void *U = act, *V = act + td, *Q = act + 2 * td, *K = act + 3 * td;
-  if (T > 0) GEMM_RUN(gemm(false, false, T, 4 * D, dm, X, dm, w->W1, 4 * D, Z, 4 * D, et, et, w->b1), "f1 GEMM");
-  {
-    Timed t_(HSTU_KERNEL_LAYER_EW, st);
-    HIP_TRY(launch_silu_split(Z, T, (int)D, bf16, U, V, Q, K, st), "SiLU split launch");
-  }
-  s = hstu_attn_fwd(p, Q, K, V, U, Y, O, mean, rstd, ws, y.core_bytes, stream);
-  if (s) return s;
-  if (T > 0) GEMM_RUN(gemm(false, false, T, dm, D, Y, D, w->W2, dm, Out, dm, et, et, w->b2), "f2 GEMM");
-  return HSTU_OK;
+  return layer_forward(p, w, X, Out, Z, act, act + td, act + 2 * td, act + 3 * td, Y, O, mean, rstd, ws,
+                       y.core_bytes, at<char>(ws, y.gemm), (hipStream_t)stream);
 }
 
 hstu_status_t hstu_layer_bwd(const hstu_problem_t *p, const hstu_layer_weights_t *w, const void *X,
@@ -729,6 +809,7 @@ hstu_status_t hstu_layer_bwd(const hstu_problem_t *p, const hstu_layer_weights_t
   void *dY = at<char>(ws, y.dy);
   float *partial = at<float>(ws, y.sums);
   float *wpart = at<float>(ws, y.wpart);
+  void *gws = at<char>(ws, y.gemm);
   // U, V, Q, K: the forward's saved activations, or recomputed from Z into ws
   const char *sv = UVQK ? static_cast<const char *>(UVQK) : act;
   const void *U = sv, *V = sv + td, *Q = sv + 2 * td, *K = sv + 3 * td;
@@ -737,7 +818,7 @@ hstu_status_t hstu_layer_bwd(const hstu_problem_t *p, const hstu_layer_weights_t
   // f2: dY = dOut W2^T, dW2 = Y^T dOut, db2 = column sums of dOut
   if (T > 0) {
     GEMM_RUN(gemm(false, true, T, D, dm, dOut, dm, w->W2, dm, dY, D, et, et, nullptr), "f2 input-gradient GEMM");
-    s = weight_grad(Y, D, dOut, dm, T, et, dW2, wpart, ws, y, st, "f2 weight-gradient GEMM");
+    s = weight_grad(Y, D, dOut, dm, T, et, dW2, wpart, gws, st, "f2 weight-gradient GEMM");
     if (s) return s;
   }
   {
@@ -760,11 +841,149 @@ hstu_status_t hstu_layer_bwd(const hstu_problem_t *p, const hstu_layer_weights_t
     if (T == 0) HIP_TRY(launch_fill_f32(dW1, dm * 4 * D, 0.f, st), "fill");
   }
   if (T > 0) {
-    s = weight_grad(X, dm, dZ, 4 * D, T, et, dW1, wpart, ws, y, st, "f1 weight-gradient GEMM");
+    s = weight_grad(X, dm, dZ, 4 * D, T, et, dW1, wpart, gws, st, "f1 weight-gradient GEMM");
     if (s) return s;
     GEMM_RUN(gemm(false, true, T, dm, 4 * D, dZ, 4 * D, w->W1, 4 * D, dX, dm, et, et, nullptr),
              "f1 input-gradient GEMM");
   }
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_stack_workspace_size(const hstu_problem_t *p, int32_t d_model, int32_t op, int32_t microbatch,
+                                        int32_t hist_max_len, int64_t hist_tokens, size_t *bytes) {
+  if (!bytes) return fail(HSTU_ERR_INVALID_ARG, "bytes is NULL");
+  if (op != HSTU_OP_FWD && op != HSTU_OP_MFALCON) return fail(HSTU_ERR_INVALID_ARG, "op = %d", op);
+  hstu_status_t s = check_problem(p, op);
+  if (s) return s;
+  if (op == HSTU_OP_MFALCON && microbatch < 0) return fail(HSTU_ERR_INVALID_ARG, "microbatch = %d < 0", microbatch);
+  if (d_model < 1 || d_model > 65536) return fail(HSTU_ERR_INVALID_ARG, "d_model = %d not in [1, 65536]", d_model);
+  (void)hist_tokens;
+  *bytes = stack_layout(p, op, d_model, microbatch, hist_max_len).total;
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_stack_history(const hstu_problem_t *hist, int32_t n_layers, const hstu_stack_layer_t *layers,
+                                 const void *X, void *Out, void *ws, size_t ws_bytes, void *stream) {
+  hstu_status_t s = check_problem(hist, HSTU_OP_FWD);
+  if (s) return s;
+  s = check_stack(hist, n_layers, layers, hist->total_tokens);
+  if (s) return s;
+  const long long T = hist->total_tokens;
+  const int dm = layers[0].w.d_model;
+  if (T > 0 && !X) return fail(HSTU_ERR_INVALID_ARG, "X must not be NULL");
+  if (!aligned16(X) || !aligned16(Out)) return fail(HSTU_ERR_INVALID_ARG, "X/Out must be 16-byte aligned");
+  const StackLayout y = stack_layout(hist, HSTU_OP_FWD, dm, 0, 0);
+  s = check_ws(ws, ws_bytes, y.total);
+  if (s) return s;
+  hipStream_t st = (hipStream_t)stream;
+  for (int l = 0; l < n_layers; ++l) {
+    const hstu_stack_layer_t &L = layers[l];
+    hstu_problem_t q = layer_problem(hist, L);
+    const void *in = l == 0 ? X : at<char>(ws, y.x[(l - 1) & 1]);
+    void *out = (l == n_layers - 1 && Out) ? Out : at<char>(ws, y.x[l & 1]);
+    s = layer_forward(&q, &L.w, in, out, at<char>(ws, y.z), at<char>(ws, y.u), L.V_cache, at<char>(ws, y.q),
+                      L.K_cache, at<char>(ws, y.yo), at<char>(ws, y.o), at<float>(ws, y.mean), at<float>(ws, y.rstd),
+                      ws, y.core_bytes, at<char>(ws, y.gemm), st);
+    if (s) return s;
+  }
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_stack_score(const hstu_problem_t *cand, int32_t n_layers, const hstu_stack_layer_t *layers,
+                               const int32_t *hist_offsets, int64_t hist_tokens, int32_t hist_max_len,
+                               const int64_t *hist_ts, int32_t microbatch, const void *Xc, void *Out, void *ws,
+                               size_t ws_bytes, void *stream) {
+  hstu_status_t s = check_problem(cand, HSTU_OP_MFALCON);
+  if (s) return s;
+  s = check_mfalcon(cand, hist_offsets, hist_tokens, hist_max_len, microbatch);
+  if (s) return s;
+  s = check_stack(cand, n_layers, layers, hist_tokens);
+  if (s) return s;
+  const long long T = cand->total_tokens;
+  if (T > 0 && (!Xc || !Out)) return fail(HSTU_ERR_INVALID_ARG, "Xc/Out must not be NULL");
+  if (!aligned16(Xc) || !aligned16(Out)) return fail(HSTU_ERR_INVALID_ARG, "Xc/Out must be 16-byte aligned");
+  const int dm = layers[0].w.d_model;
+  const StackLayout y = stack_layout(cand, HSTU_OP_MFALCON, dm, microbatch, hist_max_len);
+  s = check_ws(ws, ws_bytes, y.total);
+  if (s) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf16 = cand->dtype == HSTU_BF16;
+  const GemmType et = bf16 ? kGemmBF16 : kGemmF32;
+  const long long D = (long long)cand->H * cand->d;
+  void *gws = at<char>(ws, y.gemm);
+  for (int l = 0; l < n_layers; ++l) {
+    const hstu_stack_layer_t &L = layers[l];
+    hstu_problem_t q = layer_problem(cand, L);
+    const void *in = l == 0 ? Xc : at<char>(ws, y.x[(l - 1) & 1]);
+    void *out = l == n_layers - 1 ? Out : at<char>(ws, y.x[l & 1]);
+    void *Z = at<char>(ws, y.z), *U = at<char>(ws, y.u), *V = at<char>(ws, y.v), *Q = at<char>(ws, y.q),
+         *K = at<char>(ws, y.k), *Yc = at<char>(ws, y.yo);
+    if (T > 0) GEMM_RUN(gemm(false, false, T, 4 * D, dm, in, dm, L.w.W1, 4 * D, Z, 4 * D, et, et, L.w.b1), "f1 GEMM");
+    {
+      Timed t_(HSTU_KERNEL_LAYER_EW, st);
+      HIP_TRY(launch_silu_split(Z, T, (int)D, bf16, U, V, Q, K, st), "SiLU split launch");
+    }
+    s = hstu_mfalcon_score(&q, hist_offsets, hist_tokens, hist_max_len, L.K_cache, L.V_cache, hist_ts, Q, K, V, U,
+                           microbatch, Yc, at<char>(ws, y.o), at<float>(ws, y.mean), at<float>(ws, y.rstd), ws,
+                           y.core_bytes, stream);
+    if (s) return s;
+    if (T > 0) GEMM_RUN(gemm(false, false, T, dm, D, Yc, D, L.w.W2, dm, out, dm, et, et, L.w.b2), "f2 GEMM");
+  }
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_stack_score_capture(const hstu_problem_t *cand, int32_t n_layers,
+                                       const hstu_stack_layer_t *layers, const int32_t *hist_offsets,
+                                       int64_t hist_tokens, int32_t hist_max_len, const int64_t *hist_ts,
+                                       int32_t microbatch, const void *Xc, void *Out, void *ws, size_t ws_bytes,
+                                       void **graph) {
+  if (!graph) return fail(HSTU_ERR_INVALID_ARG, "graph is NULL");
+  *graph = nullptr;
+  // host-side checks first, so that a bad argument never leaves a capture open
+  hstu_status_t s = check_problem(cand, HSTU_OP_MFALCON);
+  if (s) return s;
+  s = check_mfalcon(cand, hist_offsets, hist_tokens, hist_max_len, microbatch);
+  if (s) return s;
+  s = check_stack(cand, n_layers, layers, hist_tokens);
+  if (s) return s;
+  if (int g = gemm_init()) return gemm_fail(g, "hipBLASLt handle");
+  hipStream_t cs = nullptr;
+  HIP_TRY(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "stream create");
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    hipStreamDestroy(cs);
+    return hip_fail(e, "begin capture");
+  }
+  s = hstu_stack_score(cand, n_layers, layers, hist_offsets, hist_tokens, hist_max_len, hist_ts, microbatch, Xc, Out,
+                       ws, ws_bytes, cs);
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(cs, &g);
+  hipStreamDestroy(cs);
+  if (s) {
+    if (g) hipGraphDestroy(g);
+    return s;
+  }
+  if (e != hipSuccess) {
+    if (g) hipGraphDestroy(g);
+    return hip_fail(e, "end capture");
+  }
+  hipGraphExec_t ex = nullptr;
+  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  hipGraphDestroy(g);
+  if (e != hipSuccess) return hip_fail(e, "graph instantiate");
+  *graph = ex;
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_graph_launch(void *graph, void *stream) {
+  if (!graph) return fail(HSTU_ERR_INVALID_ARG, "graph is NULL");
+  HIP_TRY(hipGraphLaunch((hipGraphExec_t)graph, (hipStream_t)stream), "graph launch");
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_graph_destroy(void *graph) {
+  if (!graph) return fail(HSTU_ERR_INVALID_ARG, "graph is NULL");
+  HIP_TRY(hipGraphExecDestroy((hipGraphExec_t)graph), "graph destroy");
   return HSTU_OK;
 }
 

@@ -86,21 +86,35 @@ const char *gemm_status_text(int st) {
 
 bool gemm_unsupported(int st) { return st == HIPBLAS_STATUS_NOT_SUPPORTED; }
 
-int gemm_rm(const GemmRM &g, void *ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+// The current device's handle, created on first use.
+int handle_for_current(hipblasLtHandle_t *h, int *dev_out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HIPBLAS_STATUS_NOT_INITIALIZED;
-  hipblasLtHandle_t h;
-  {
-    std::lock_guard<std::mutex> lk(g_mu);
-    if (!g_handle[dev]) {
-      hipblasStatus_t st = hipblasLtCreate(&g_handle[dev]);
-      if (st != HIPBLAS_STATUS_SUCCESS) {
-        g_handle[dev] = nullptr;
-        return st;
-      }
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_handle[dev]) {
+    hipblasStatus_t st = hipblasLtCreate(&g_handle[dev]);
+    if (st != HIPBLAS_STATUS_SUCCESS) {
+      g_handle[dev] = nullptr;
+      return st;
     }
-    h = g_handle[dev];
   }
+  *h = g_handle[dev];
+  *dev_out = dev;
+  return HIPBLAS_STATUS_SUCCESS;
+}
+}  // namespace
+
+int gemm_init() {
+  hipblasLtHandle_t h;
+  int dev;
+  return handle_for_current(&h, &dev);
+}
+
+int gemm_rm(const GemmRM &g, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int dev = 0;
+  hipblasLtHandle_t h;
+  if (int e = handle_for_current(&h, &dev)) return e;
   const hipDataType tab = hip_type(g.ab), tc = hip_type(g.c);
   // column-major problem: m = N, n = M, k = K; A' = B, B' = A
   const uint64_t m = g.N, n = g.M, k = g.K;

@@ -175,6 +175,8 @@ struct GemmRM {
   long long sA, sB, sC;     // element offsets between consecutive batch entries
 };
 int gemm_rm(const GemmRM &g, void *ws, size_t ws_bytes, hipStream_t s);
+// Creates the current device's hipBLASLt handle if needed (before a stream capture).
+int gemm_init();
 const char *gemm_status_text(int st);
 bool gemm_unsupported(int st);  // no algorithm for the problem
 

@@ -96,3 +96,54 @@ def run_layer_fwd(ns, **kw):
 
 def run_layer_bwd(ns, f, **kw):
     return api.layer_bwd(ns.problem, ns.weights, ns.X, f, ns.dOut, **kw)
+
+
+def upload_stack(sp, device="cuda"):
+    """Device tensors of a synth.StackProblem: the history and candidate
+    problems, the layer array with its K/V caches, X_hist and X_cand."""
+    dev = torch.device(device)
+    ns = SimpleNamespace(src=sp, device=dev)
+    ns.hist_offsets = _t(sp.hist_offsets, torch.int32, dev)
+    ns.cand_offsets = _t(sp.cand_offsets, torch.int32, dev)
+    ns.hist_ts = _t(sp.hist_ts, torch.int64, dev)
+    ns.cand_ts = _t(sp.cand_ts, torch.int64, dev)
+    ns.hist_group = _t(sp.hist_group, torch.uint8, dev)
+    ns.cand_group = _t(sp.cand_group, torch.uint8, dev)
+    ns.hist_tokens = int(sp.hist_offsets[-1])
+    ns.hist_max_len = int(np.diff(sp.hist_offsets).max()) if sp.B else 0
+    cand_max = int(np.diff(sp.cand_offsets).max()) if sp.B else 0
+    n_pos = max([len(l["rab_p"]) for l in sp.layers if "rab_p" in l] or [0])
+    n_tb = max([len(l["rab_t"]) for l in sp.layers if "rab_t" in l] or [0])
+    ns.layer_tensors = []
+    for lay in sp.layers:
+        t = {"W1": lay["W1"].contiguous().to(dev), "W2": lay["W2"].contiguous().to(dev)}
+        for k in ("b1", "b2", "rab_p", "rab_t", "gamma", "beta"):
+            if k in lay:
+                t[k] = _t(lay[k], torch.float32, dev)
+        ns.layer_tensors.append(t)
+    ns.layers, ns.K_caches, ns.V_caches = api.stack_layers(ns.layer_tensors, sp.H, sp.d, sp.dtype, dev,
+                                                           hist_tokens=ns.hist_tokens)
+    ns.X_hist = sp.X_hist.contiguous().to(dev)
+    ns.X_cand = sp.X_cand.contiguous().to(dev)
+
+    def prob(offsets, T, max_len, ts, group, time_filter):
+        p = api.problem(offsets, H=sp.H, d=sp.d, dtype=sp.dtype, total_tokens=T, max_len=max_len, n_max=sp.n_max,
+                        timestamps=ts, norm=sp.norm, eps=sp.eps, token_group=group, n_groups=sp.n_groups,
+                        time_filter=time_filter)
+        p.n_pos, p.n_tb = n_pos, n_tb
+        return p
+
+    ns.hist_problem = prob(ns.hist_offsets, ns.hist_tokens, ns.hist_max_len, ns.hist_ts, ns.hist_group, False)
+    ns.cand_problem = prob(ns.cand_offsets, int(sp.cand_offsets[-1]), cand_max, ns.cand_ts, ns.cand_group,
+                           sp.time_filter)
+    return ns
+
+
+def run_stack_history(ns, **kw):
+    return api.stack_history(ns.hist_problem, ns.layers, ns.X_hist, **kw)
+
+
+def run_stack_score(ns, Xc=None, microbatch=None, **kw):
+    mb = ns.src.microbatch if microbatch is None else microbatch
+    return api.stack_score(ns.cand_problem, ns.layers, ns.hist_offsets, ns.hist_tokens, ns.hist_max_len,
+                           ns.X_cand if Xc is None else Xc, hist_ts=ns.hist_ts, microbatch=mb, **kw)

@@ -266,7 +266,7 @@ enum {
   HSTU_KERNEL_BALANCE = 9,        /* hstu_balance_bins */
   HSTU_KERNEL_GEMM = 10,          /* the layer's projection GEMMs (hipBLASLt) */
   HSTU_KERNEL_LAYER_EW = 11,      /* the layer's SiLU / SiLU' / bias-gradient passes */
-  HSTU_KERNEL_COUNT = 12
+  HSTU_KERNEL_COUNT = 12          /* (launches recorded into a graph are not timed) */
 };
 hstu_status_t hstu_kernel_timing(int32_t enable);
 hstu_status_t hstu_kernel_timing_read(int32_t kernel, double *total_ms, int64_t *launches);
@@ -386,6 +386,91 @@ hstu_status_t hstu_layer_bwd(const hstu_problem_t *p, const hstu_layer_weights_t
                              const float *rstd, const void *dOut, void *dX, float *dW1, float *db1, float *dW2,
                              float *db2, float *d_rab_p, float *d_rab_t, float *d_gamma, float *d_beta, void *ws,
                              size_t ws_bytes, void *stream);
+
+/*
+ * Candidate scoring through a stack of HSTU layers with per-layer history
+ * K/V caches (HSTU blog, section 4.2 "批量推理": candidates are scored in
+ * microbatches against one encoding of the user's history; section 4.3
+ * "KV Caching": the history's keys and values are computed once and reused).
+ * The result equals running every user's sequence [history | candidates]
+ * through all layers with the candidate mask (P = 0, C = m_b) and taking
+ * the candidate rows: a history row never sees a candidate, so each layer's
+ * history K and V are all a candidate needs.
+ *
+ * Each layer is described by hstu_stack_layer_t: its projections, its own
+ * rab tables and norm affine (NULL = off / identity; the table sizes n_pos,
+ * n_tb and the group count come from the problem), and its cache buffers
+ * K_cache, V_cache [Th, H, d] (caller-owned, in the problem's dtype). All
+ * layers share H, d, d_model, the norm kind and N_max, which the problem
+ * passed to each call gives. Xc/X/Out are [tokens, d_model].
+ */
+typedef struct hstu_stack_layer {
+  hstu_layer_weights_t w;
+  const float *rab_p;
+  const float *rab_t;
+  const float *gamma;
+  const float *beta;
+  void *K_cache;
+  void *V_cache;
+} hstu_stack_layer_t;
+
+/*
+ * Workspace bytes (host only) of hstu_stack_history (op = HSTU_OP_FWD; p =
+ * the histories) or hstu_stack_score / hstu_stack_score_capture (op =
+ * HSTU_OP_MFALCON; p = the candidates, with microbatch, hist_max_len and
+ * hist_tokens as for hstu_workspace_size).
+ */
+hstu_status_t hstu_stack_workspace_size(const hstu_problem_t *p, int32_t d_model, int32_t op, int32_t microbatch,
+                                        int32_t hist_max_len, int64_t hist_tokens, size_t *bytes);
+
+/*
+ * History pass: runs the histories (a jagged batch `hist`, any mask it
+ * describes, normally causal) through the n_layers layers (1..64), writing
+ * each layer's K and V into that layer's K_cache and V_cache, and the last
+ * layer's output into Out [Th, d_model] (NULL skips it). The rab/gamma/beta
+ * pointers of `hist` are ignored in favour of each layer's.
+ */
+hstu_status_t hstu_stack_history(const hstu_problem_t *hist, int32_t n_layers, const hstu_stack_layer_t *layers,
+                                 const void *X, void *Out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Candidate pass: for each layer, the candidates' projections and
+ * hstu_mfalcon_score against that layer's K_cache/V_cache (same microbatch
+ * semantics; the result does not depend on microbatch), the output feeding
+ * the next layer; Out [Tc, d_model] gets the last layer's output. `cand` is
+ * the candidate problem as for hstu_mfalcon_score (its rab/gamma/beta
+ * pointers are ignored in favour of each layer's). The caches may be reused
+ * by any number of calls (new candidates of the same users) until the next
+ * hstu_stack_history that writes them.
+ */
+hstu_status_t hstu_stack_score(const hstu_problem_t *cand, int32_t n_layers, const hstu_stack_layer_t *layers,
+                               const int32_t *hist_offsets, int64_t hist_tokens, int32_t hist_max_len,
+                               const int64_t *hist_ts, int32_t microbatch, const void *Xc, void *Out, void *ws,
+                               size_t ws_bytes, void *stream);
+
+/*
+ * Records one hstu_stack_score call (same arguments) into an executable HIP
+ * graph and returns it in *graph (host). Nothing runs until
+ * hstu_graph_launch. A launch replays every kernel of the call with the
+ * pointers and host scalars given here: between launches the caller may
+ * change the contents of the device buffers (new candidate features, new
+ * caches from a history pass of the same shapes), not their addresses or the
+ * batch's sizes. Run one eager hstu_stack_score of the same sizes first so
+ * that the GEMMs use timed algorithm choices (capture takes the heuristic's
+ * first choice for sizes not seen before). Concurrent launches of one graph,
+ * or of graphs sharing a workspace, race.
+ */
+hstu_status_t hstu_stack_score_capture(const hstu_problem_t *cand, int32_t n_layers,
+                                       const hstu_stack_layer_t *layers, const int32_t *hist_offsets,
+                                       int64_t hist_tokens, int32_t hist_max_len, const int64_t *hist_ts,
+                                       int32_t microbatch, const void *Xc, void *Out, void *ws, size_t ws_bytes,
+                                       void **graph);
+
+/* Launches a graph from hstu_stack_score_capture on `stream`. */
+hstu_status_t hstu_graph_launch(void *graph, void *stream);
+
+/* Frees a graph from hstu_stack_score_capture (host; waits for nothing). */
+hstu_status_t hstu_graph_destroy(void *graph);
 
 #ifdef __cplusplus
 }

@@ -63,3 +63,9 @@ def oracle_layer_bwd(lp):
     p = lp.core
     return oracle.layer_bwd(p.offsets, f64(lp.X), f64(lp.W1), f64(lp.W2), f64(lp.dOut), b1=f64(lp.b1),
                             b2=f64(lp.b2), **oracle_opts(p))
+
+
+def f64_layers(layers):
+    """Per-layer dicts with every tensor as a float64 numpy array (the
+    oracle takes numpy; bf16 weights are represented exactly)."""
+    return [{k: f64(v) for k, v in lay.items()} for lay in layers]

@@ -157,3 +157,39 @@ def test_layer_entry_points_reject_bad_arguments(L):
     assert bwd(None) == L.HSTU_ERR_INVALID_ARG
     assert bwd(ctypes.c_void_p(0x2004)) == L.HSTU_ERR_INVALID_ARG  # misaligned dW1
     assert bwd(dummy, n=1024) == L.HSTU_ERR_WORKSPACE
+
+
+def test_stack_entry_points_reject_bad_arguments(L):
+    p = _problem(L)
+    lib = L.lib()
+    dummy = ctypes.c_void_p(0x2000)
+    n = ctypes.c_size_t(0)
+    assert lib.hstu_stack_workspace_size(ctypes.byref(p), 16, L.HSTU_OP_FWD, 0, 0, 0, ctypes.byref(n)) == 0
+    assert n.value % 256 == 0 and n.value > (64 << 20)
+    assert lib.hstu_stack_workspace_size(ctypes.byref(p), 16, L.HSTU_OP_BWD, 0, 0, 0,
+                                         ctypes.byref(n)) == L.HSTU_ERR_INVALID_ARG
+    layers = (L.StackLayer * 2)()
+    for i in range(2):
+        layers[i].w = _weights(L)
+        layers[i].K_cache = layers[i].V_cache = ctypes.c_void_p(0x10000)
+    big = ctypes.c_void_p(0x100000)
+    hist = lambda nl, lay: lib.hstu_stack_history(ctypes.byref(p), nl, lay, dummy, None, big, 1 << 40, None)
+    assert hist(0, layers) == L.HSTU_ERR_INVALID_ARG
+    assert hist(65, layers) == L.HSTU_ERR_INVALID_ARG
+    assert hist(2, None) == L.HSTU_ERR_INVALID_ARG
+    layers[1].w = _weights(L, dm=32)  # d_model differs between layers
+    assert hist(2, layers) == L.HSTU_ERR_INVALID_ARG
+    layers[1].w = _weights(L)
+    layers[1].rab_p = ctypes.c_void_p(0x3000)  # the problem has n_pos = 0
+    assert hist(2, layers) == L.HSTU_ERR_INVALID_ARG
+    layers[1].rab_p = None
+    layers[0].K_cache = ctypes.c_void_p(0x10008)  # misaligned cache
+    assert hist(2, layers) == L.HSTU_ERR_INVALID_ARG
+    layers[0].K_cache = ctypes.c_void_p(0x10000)
+    assert lib.hstu_stack_history(ctypes.byref(p), 2, layers, dummy, None, big, 1024, None) == L.HSTU_ERR_WORKSPACE
+    g = ctypes.c_void_p(0)
+    assert lib.hstu_stack_score_capture(ctypes.byref(p), 2, layers, dummy, 16, 8, None, 0, dummy, dummy, big, 1 << 40,
+                                        None) == L.HSTU_ERR_INVALID_ARG
+    assert lib.hstu_graph_launch(None, None) == L.HSTU_ERR_INVALID_ARG
+    assert lib.hstu_graph_destroy(None) == L.HSTU_ERR_INVALID_ARG
+    del g
