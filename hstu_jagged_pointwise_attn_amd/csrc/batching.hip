@@ -160,6 +160,44 @@ __global__ void gather_rows_kernel(const W *src, const int *idx, long long n, lo
 
 // Longest-first greedy assignment of sequences to bins (one workgroup).
 constexpr int kBalCap = 8192;
+// One step of a wave prefix minimum of (v, w) ordered by v then w: each
+// lane takes its DPP source lane's pair when that is smaller; lanes without
+// a source keep their own (the old value is the lane's own).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_min_step(long long &v, int &w) {
+  const int lo = (int)(unsigned)(unsigned long long)v, hi = (int)((unsigned long long)v >> 32);
+  const int olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false);
+  const int ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false);
+  const int ow = __builtin_amdgcn_update_dpp(w, w, CTRL, ROW_MASK, 0xf, false);
+  const long long ov = (long long)(((unsigned long long)(unsigned)ohi << 32) | (unsigned)olo);
+  const bool take = ov < v || (ov == v && ow < w);
+  v = take ? ov : v;
+  w = take ? ow : w;
+}
+
+// The greedy assignment of the sorted items (wave 0, lane = bin): STEPS
+// prefix-minimum steps cover 2^STEPS lanes.
+template <int STEPS>
+__device__ __forceinline__ void greedy(long long &load, int B, const long long *s_cost, const int *s_idx, int *bin) {
+  const int tid = threadIdx.x;
+  constexpr int kLast = (1 << STEPS) - 1;
+  for (int r = 0; r < B; ++r) {
+    const long long c = s_cost[r];  // same address in every lane: read early, off the critical path
+    const int item = s_idx[r];
+    long long best = load;
+    int who = tid;
+    dpp_min_step<0x111, 0xf>(best, who);                    // row_shr:1
+    dpp_min_step<0x112, 0xf>(best, who);                    // row_shr:2
+    dpp_min_step<0x114, 0xf>(best, who);                    // row_shr:4
+    if constexpr (STEPS >= 4) dpp_min_step<0x118, 0xf>(best, who);  // row_shr:8
+    if constexpr (STEPS >= 5) dpp_min_step<0x142, 0xa>(best, who);  // row_bcast:15
+    if constexpr (STEPS >= 6) dpp_min_step<0x143, 0xc>(best, who);  // row_bcast:31
+    const int winner = __builtin_amdgcn_readlane(who, kLast);
+    if (tid == winner) load += c;
+    if (tid == 0) bin[item] = winner;
+  }
+}
+
 __global__ __launch_bounds__(kBatchThreads) void balance_kernel(const int *offsets, int B, int n_bins,
                                                                 int cost_kind, int *bin, long long *bin_cost) {
   __shared__ long long s_cost[kBalCap];
@@ -200,25 +238,16 @@ __global__ __launch_bounds__(kBatchThreads) void balance_kernel(const int *offse
     }
   }
   if (tid >= 64) return;
-  // Wave 0: lane = bin; each step takes the least loaded bin (lowest on ties).
-  long long load = 0;
-  for (int r = 0; r < B; ++r) {
-    long long best = tid < n_bins ? load : 0x7fffffffffffffffLL;
-    int who = tid;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const long long ob = __shfl_xor(best, o, 64);
-      const int ow = __shfl_xor(who, o, 64);
-      if (ob < best || (ob == best && ow < who)) {
-        best = ob;
-        who = ow;
-      }
-    }
-    if (tid == who) {
-      load += s_cost[r];
-      bin[s_idx[r]] = who;
-    }
-  }
+  // Wave 0: lane = bin. Each step takes the least loaded bin (lowest on ties):
+  // an inclusive prefix minimum of (load, lane) with DPP row shifts (and row
+  // broadcasts beyond 16 bins) leaves the winner in the last lane that holds
+  // a bin's prefix; only as many steps as the bin count needs are taken.
+  const long long kInf = 0x7fffffffffffffffLL;
+  long long load = tid < n_bins ? 0 : kInf;
+  if (n_bins <= 8) greedy<3>(load, B, s_cost, s_idx, bin);
+  else if (n_bins <= 16) greedy<4>(load, B, s_cost, s_idx, bin);
+  else if (n_bins <= 32) greedy<5>(load, B, s_cost, s_idx, bin);
+  else greedy<6>(load, B, s_cost, s_idx, bin);
   if (tid < n_bins) bin_cost[tid] = load;
 }
 

@@ -81,7 +81,10 @@ def test_stochastic_length_flags_bad_offsets():
 
 
 @pytest.mark.parametrize("n_bins,cost", [(8, _lib.HSTU_COST_TOKENS), (8, _lib.HSTU_COST_ATTENTION),
-                                         (3, _lib.HSTU_COST_TOKENS), (64, _lib.HSTU_COST_ATTENTION)])
+                                         (3, _lib.HSTU_COST_TOKENS), (64, _lib.HSTU_COST_ATTENTION),
+                                         (1, _lib.HSTU_COST_TOKENS), (9, _lib.HSTU_COST_ATTENTION),
+                                         (16, _lib.HSTU_COST_TOKENS), (17, _lib.HSTU_COST_ATTENTION),
+                                         (32, _lib.HSTU_COST_TOKENS), (33, _lib.HSTU_COST_TOKENS)])
 def test_balance_bins_bit_exact(n_bins, cost):
     lengths = np.concatenate([synth._train_lengths(2, False), synth._train_lengths(2, True)])  # 256 seqs
     lengths[::17] = 0
