@@ -135,6 +135,9 @@ Layout layout(const hstu_problem_t *p, int op, int microbatch, int hist_max_len)
   return L;
 }
 
+// The kernels move 16-byte vectors; every dense array must start on a 16-byte boundary.
+bool aligned16(const void *q) { return ((uintptr_t)q & 15) == 0; }
+
 hstu_status_t check_problem(const hstu_problem_t *p, int op) {
   if (!p) return fail(HSTU_ERR_INVALID_ARG, "problem is NULL");
   if (p->B < 0) return fail(HSTU_ERR_INVALID_ARG, "B = %d < 0", p->B);
@@ -167,6 +170,8 @@ hstu_status_t check_problem(const hstu_problem_t *p, int op) {
     return fail(HSTU_ERR_INVALID_ARG, "mask_flags = %d has unknown bits", p->mask_flags);
   if ((p->mask_flags & HSTU_MASK_CAND_TIME_FILTER) && !p->timestamps)
     return fail(HSTU_ERR_INVALID_ARG, "the candidate timestamp filter needs timestamps");
+  if (!aligned16(p->gamma) || !aligned16(p->beta))
+    return fail(HSTU_ERR_INVALID_ARG, "gamma/beta must be 16-byte aligned");
   const long long D = (long long)p->H * p->d;
   const long long dmax = p->dtype == HSTU_BF16 ? 4096 : 2048;
   if (D > dmax) return fail(HSTU_ERR_UNSUPPORTED, "H*d = %lld > %lld", D, dmax);
@@ -331,7 +336,6 @@ LayerLayout layer_layout(const hstu_problem_t *p, int op, int d_model) {
   return y;
 }
 
-bool aligned16(const void *q) { return ((uintptr_t)q & 15) == 0; }
 
 hstu_status_t check_layer(const hstu_problem_t *p, const hstu_layer_weights_t *w) {
   if (!w) return fail(HSTU_ERR_INVALID_ARG, "layer weights are NULL");
@@ -430,6 +434,8 @@ hstu_status_t hstu_attn_fwd(const hstu_problem_t *p, const void *Q, const void *
   if (s) return s;
   if (p->total_tokens > 0 && (!Q || !K || !V || !U || !Y || !O))
     return fail(HSTU_ERR_INVALID_ARG, "Q/K/V/U/Y/O must not be NULL");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(U) || !aligned16(Y) || !aligned16(O))
+    return fail(HSTU_ERR_INVALID_ARG, "Q/K/V/U/Y/O must be 16-byte aligned");
   if (p->norm != HSTU_NORM_NONE && p->total_tokens > 0 && (!mean || !rstd))
     return fail(HSTU_ERR_INVALID_ARG, "mean/rstd must not be NULL with a norm");
   Layout L = layout(p, HSTU_OP_FWD, 0, 0);
@@ -460,6 +466,9 @@ hstu_status_t hstu_mfalcon_score(const hstu_problem_t *cand, const int32_t *hist
     return fail(HSTU_ERR_INVALID_ARG, "give both candidate and history timestamps, or neither");
   if (cand->total_tokens > 0 && (!Qc || !Kc || !Vc || !Uc || !Yc || !Oc))
     return fail(HSTU_ERR_INVALID_ARG, "Qc/Kc/Vc/Uc/Yc/Oc must not be NULL");
+  if (!aligned16(Qc) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(Uc) || !aligned16(Yc) || !aligned16(Oc) ||
+      !aligned16(K_cache) || !aligned16(V_cache))
+    return fail(HSTU_ERR_INVALID_ARG, "Qc/Kc/Vc/Uc/Yc/Oc/K_cache/V_cache must be 16-byte aligned");
   if (hist_tokens > 0 && (!K_cache || !V_cache))
     return fail(HSTU_ERR_INVALID_ARG, "K_cache/V_cache must not be NULL");
   if (cand->norm != HSTU_NORM_NONE && cand->total_tokens > 0 && (!mean || !rstd))
@@ -488,6 +497,9 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
   const long long T = p->total_tokens;
   if (T > 0 && (!Q || !K || !V || !U || !O || !dY || !dQ || !dK || !dV || !dU))
     return fail(HSTU_ERR_INVALID_ARG, "Q/K/V/U/O/dY/dQ/dK/dV/dU must not be NULL");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(U) || !aligned16(O) || !aligned16(dY) ||
+      !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(dU))
+    return fail(HSTU_ERR_INVALID_ARG, "Q/K/V/U/O/dY/dQ/dK/dV/dU must be 16-byte aligned");
   if (p->norm != HSTU_NORM_NONE && T > 0 && (!mean || !rstd))
     return fail(HSTU_ERR_INVALID_ARG, "mean/rstd must not be NULL with a norm");
   const bool tf = (p->mask_flags & HSTU_MASK_CAND_TIME_FILTER) != 0;

@@ -60,6 +60,19 @@ struct Vec<false> {
   }
 };
 
+// N consecutive fp32 values of an affine row (gamma or beta), as 16-byte loads.
+template <int N>
+__device__ __forceinline__ void load_affine(const float *p, int c, float *x) {
+#pragma unroll
+  for (int e = 0; e < N; e += 4) {
+    const float4 v = *(const float4 *)(p + c + e);
+    x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
+  }
+}
+
+// The token's group and its X and U rows are all requested before the first
+// reduction, so one wave has its whole row in flight at once; gamma and beta
+// (fp32, a few KB per group, L2-resident) are read as 16-byte vectors.
 template <bool BF16, int MAXCH>
 __global__ __launch_bounds__(256) void norm_fwd_kernel(NormArgs a) {
   using V = Vec<BF16>;
@@ -69,19 +82,20 @@ __global__ __launch_bounds__(256) void norm_fwd_kernel(NormArgs a) {
   const int lane = threadIdx.x & 63;
   const int D = a.D, nch = D / N;
   const long long row = t * D;
-  float x[MAXCH][N];
+  int g = a.mode == HSTU_NORM_GLN ? (int)a.group[t] : 0;
+  float x[MAXCH][N], u[MAXCH][N];
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < MAXCH; ++k) {
     const int ch = lane + 64 * k;
     if (ch < nch) {
       V::load(a.X, row + ch * N, x[k]);
+      V::load(a.U, row + ch * N, u[k]);
 #pragma unroll
       for (int e = 0; e < N; ++e) s += x[k][e];
     }
   }
   float mean = 0.f, rstd = 1.f;
-  int g = -1;
   if (a.mode != HSTU_NORM_NONE) {
     mean = wave_sum(s) / (float)D;
     float v = 0.f;
@@ -98,31 +112,27 @@ __global__ __launch_bounds__(256) void norm_fwd_kernel(NormArgs a) {
     }
     const float var = wave_sum(v) / (float)D;
     rstd = 1.0f / sqrtf(var + a.eps);
-    g = 0;
-    if (a.mode == HSTU_NORM_GLN) {
-      g = a.group[t];
-      if (g >= a.n_groups) {
-        if (lane == 0) atomicOr(&a.hdr[kHdrStatus], HSTU_DEV_BAD_GROUP);
-        g = -1;
-      }
+    if (g >= a.n_groups) {
+      if (lane == 0) atomicOr(&a.hdr[kHdrStatus], HSTU_DEV_BAD_GROUP);
+      g = -1;
     }
   }
+  const bool norm = a.mode != HSTU_NORM_NONE;
+  const float *gm = (norm && g >= 0 && a.gamma) ? a.gamma + (long long)g * D : nullptr;
+  const float *bt = (norm && g >= 0 && a.beta) ? a.beta + (long long)g * D : nullptr;
 #pragma unroll
   for (int k = 0; k < MAXCH; ++k) {
     const int ch = lane + 64 * k;
     if (ch < nch) {
-      float u[N], y[N];
-      V::load(a.U, row + ch * N, u);
+      float gam[N], bet[N], y[N];
+#pragma unroll
+      for (int e = 0; e < N; ++e) gam[e] = 1.f, bet[e] = 0.f;
+      if (gm) load_affine<N>(gm, ch * N, gam);
+      if (bt) load_affine<N>(bt, ch * N, bet);
 #pragma unroll
       for (int e = 0; e < N; ++e) {
-        float n = x[k][e];
-        if (a.mode != HSTU_NORM_NONE) {
-          n = (n - mean) * rstd;
-          const int c = ch * N + e;
-          if (g >= 0 && a.gamma) n *= a.gamma[(long long)g * D + c];
-          if (g >= 0 && a.beta) n += a.beta[(long long)g * D + c];
-        }
-        y[e] = n * u[e];
+        const float n = norm ? (x[k][e] - mean) * rstd * gam[e] + bet[e] : x[k][e];
+        y[e] = n * u[k][e];
       }
       V::store(a.Y, row + ch * N, y);
     }
@@ -234,20 +244,22 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
     for (int k = 0; k < MAXCH; ++k) {
       const int ch = lane + 64 * k;
       if (ch < nch) {
-        float du[N];
+        float du[N], gam[N], bet[N];
+#pragma unroll
+        for (int e = 0; e < N; ++e) gam[e] = 1.f, bet[e] = 0.f;
+        if (gm) load_affine<N>(gm, ch * N, gam);
+        if (bt) load_affine<N>(bt, ch * N, bet);
 #pragma unroll
         for (int e = 0; e < N; ++e) {
-          const int c = ch * N + e;
           xh[k][e] = (x[k][e] - mean) * rstd;
-          const float gam = gm ? gm[c] : 1.f;
-          const float n = xh[k][e] * gam + (bt ? bt[c] : 0.f);
+          const float n = xh[k][e] * gam[e] + bet[e];
           du[e] = n * dy[k][e];
           const float dn = dy[k][e] * u[k][e];
           if (affine && g >= 0) {
             dg[k][e] += dn * xh[k][e];
             db[k][e] += dn;
           }
-          gh[k][e] = dn * gam;
+          gh[k][e] = dn * gam[e];
           s1 += gh[k][e];
           s2 += gh[k][e] * xh[k][e];
         }

@@ -31,6 +31,9 @@
  *   - Element type of Q, K, V, U, O, Y, dY and the gradients: bf16 or fp32,
  *     one type per call (hstu_problem_t.dtype). rab tables, gamma/beta, the
  *     normalisation statistics and their gradients are fp32.
+ *   - Q, K, V, U, Y, O, dY, dQ, dK, dV, dU, the K/V caches, gamma and beta
+ *     must start on a 16-byte boundary (the kernels move 16-byte vectors);
+ *     a misaligned pointer is rejected with HSTU_ERR_INVALID_ARG.
  *   - The caller owns every buffer. The library never allocates device
  *     memory: scratch comes from the workspace `ws` of at least
  *     hstu_workspace_size() bytes (256-byte aligned). Concurrent calls need

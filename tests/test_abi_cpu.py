@@ -98,6 +98,34 @@ def test_fwd_rejects_null_and_small_workspace(L):
     assert st == L.HSTU_ERR_INVALID_ARG  # misaligned workspace
 
 
+def test_attention_rejects_misaligned_arrays(L):
+    """Every dense array is moved in 16-byte vectors: a pointer off a 16-byte
+    boundary is refused before anything is enqueued."""
+    lib = L.lib()
+    dummy, odd = ctypes.c_void_p(0x2000), ctypes.c_void_p(0x2008)
+    ws = ctypes.c_void_p(0x10000)
+    p = _problem(L)
+    for i in range(6):
+        args = [dummy] * 6
+        args[i] = odd
+        assert lib.hstu_attn_fwd(ctypes.byref(p), *args, dummy, dummy, ws, 1 << 30, None) == L.HSTU_ERR_INVALID_ARG
+    for i in range(10):
+        args = [dummy] * 10
+        args[i] = odd
+        st = lib.hstu_attn_bwd(ctypes.byref(p), *args[:5], dummy, dummy, *args[5:], None, None, None, None,
+                               ws, 1 << 30, None)
+        assert st == L.HSTU_ERR_INVALID_ARG
+    q = _problem(L, norm=L.HSTU_NORM_LN, eps=1e-5, gamma=odd)
+    assert lib.hstu_attn_fwd(ctypes.byref(q), *([dummy] * 8), ws, 1 << 30, None) == L.HSTU_ERR_INVALID_ARG
+    c = _problem(L)
+    for i in range(8):
+        args = [dummy] * 8          # K_cache, V_cache, then Qc, Kc, Vc, Uc, then Yc, Oc
+        args[i] = odd
+        st = lib.hstu_mfalcon_score(ctypes.byref(c), dummy, 16, 8, args[0], args[1], None, *args[2:6], 0,
+                                    args[6], args[7], dummy, dummy, ws, 1 << 30, None)
+        assert st == L.HSTU_ERR_INVALID_ARG
+
+
 def test_mfalcon_rejects_prefix_and_cand_len(L):
     p = _problem(L, prefix_len=ctypes.c_void_p(0x3000))
     n = ctypes.c_size_t(0)
