@@ -116,9 +116,13 @@ __device__ __forceinline__ void fwd_epilogue(const f32x4 (&st)[4][2], bf16x8 (&p
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x = st[mk][nq][i];
-          if (USE_T) x += TCONST ? tcv : t2tab[ffbh_u32(absdiff_u32(tq[nq], tk4[i])) + 1];
-          p[i] = silu_fast(x);
+          // t = -log2(e) (S + rab_t) (t2tab and tcv hold -log2(e) rab_t), and
+          // t / (1 + 2^t) = -log2(e) SiLU(S + rab_t); the output scale undoes
+          // the factor.
+          float t;
+          if (USE_T) t = fmaf(st[mk][nq][i], -kLog2e, TCONST ? tcv : t2tab[ffbh_u32(absdiff_u32(tq[nq], tk4[i])) + 1]);
+          else t = st[mk][nq][i] * -kLog2e;
+          p[i] = t * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
           bool vis = hirel[nq] > mk * 16 + i;
           if (TF) vis = vis && (!tfr[nq] || prel > mk * 16 + i || tk4[i] < tq[nq]);
           if (!FULL) p[i] = vis ? p[i] : 0.f;
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   if (USE_T && tid < 33) {
     const int c = tid - 1;
     const int bkt = c < 0 ? 0 : 31 - c;
-    t2tab[tid] = has_rt ? a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1] : 0.f;
+    t2tab[tid] = has_rt ? -kLog2e * a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1] : 0.f;
   }
   __syncthreads();
 
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       }
       const int blo = bucket_u32(dlo, a.n_tb), bhi = bucket_u32(dhi, a.n_tb);
       tconst = blo == bhi;
-      tcv = has_rt ? a.rab_t[blo] : 0.f;
+      tcv = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t2tab[ffbh_u32(dlo) + 1])));
     }
 
     const unsigned *tkb = tkey + b * (USE_T ? BN : 0);
@@ -387,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       }
       part += __shfl_xor(part, 16, 64);
       part += __shfl_xor(part, 32, 64);
-      as[nq] = cand ? silu_fast(part + bias0) : 0.f;
+      as[nq] = cand ? -kLog2e * silu_fast(part + bias0) : 0.f;
     }
 #pragma unroll
     for (int nq = 0; nq < 2; ++nq) {
@@ -406,6 +410,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   }
 
   if (USE_T && bad_t) atomicOr(&s_bad, 1);
+  // The key loop summed -log2(e) SiLU(.) v; -ln(2) / N_max restores the scale.
+  const float oscale = a.inv_nmax * -0.69314718055994531f;
   // Stage O through LDS (the K buffers) so that global stores are 16-byte rows.
   __syncthreads();
   u16 *os = Ks;
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       const int lrow = w * 32 + nq * 16 + lg * 4 + i;
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) {
-        const __bf16 v = (__bf16)(acc[nq][nd][i] * a.inv_nmax);
+        const __bf16 v = (__bf16)(acc[nq][nd][i] * oscale);
         os[lrow * OST + nd * 16 + lr] = __builtin_bit_cast(u16, v);
       }
     }

@@ -67,16 +67,22 @@ __device__ __forceinline__ int bucket_u32(unsigned x, int n_tb) {
   return b < n_tb - 1 ? b : n_tb - 1;
 }
 
-__device__ __forceinline__ unsigned wave_min_u32(unsigned v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (unsigned)__shfl_xor((int)v, o, 64));
-  return v;
+// Wave-wide unsigned min / max, returned in every lane: DPP moves reduce each
+// row of 16 lanes (quad swaps, then rotations by 4 and 8), four lane reads
+// combine the rows. No LDS traffic; every lane of the wave must be active.
+template <bool MAX>
+__device__ __forceinline__ unsigned wave_ext_u32(unsigned v) {
+  auto f = [](unsigned a, unsigned b) { return MAX ? max(a, b) : min(a, b); };
+  v = f(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = f(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = f(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror 4
+  v = f(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror 8
+  const unsigned a = f((unsigned)__builtin_amdgcn_readlane((int)v, 0), (unsigned)__builtin_amdgcn_readlane((int)v, 16));
+  const unsigned b = f((unsigned)__builtin_amdgcn_readlane((int)v, 32), (unsigned)__builtin_amdgcn_readlane((int)v, 48));
+  return f(a, b);
 }
-__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, o, 64));
-  return v;
-}
+__device__ __forceinline__ unsigned wave_min_u32(unsigned v) { return wave_ext_u32<false>(v); }
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v) { return wave_ext_u32<true>(v); }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
