@@ -552,7 +552,10 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
     n.mode = p->norm;
     n.T = T;
     n.D = D;
-    n.tokens_per_wave = 32;
+    // One token per wave when no affine gradient is summed (as many waves as
+    // tokens keep the loads in flight); otherwise runs of 32 tokens, whose
+    // dgamma / dbeta partials leave with one atomic per column and run.
+    n.tokens_per_wave = (dg || db) ? 32 : 1;
     n.dU = dU; n.dX = dO;
     n.dgamma = dg; n.dbeta = db;
     Timed t_(HSTU_KERNEL_NORM_BWD, st);

@@ -14,10 +14,21 @@ namespace {
 typedef unsigned short u16;
 typedef unsigned int u32;
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the wave, returned in every lane: DPP moves add within each row of
+// 16 lanes (quad swaps, then rotations by 4 and 8) and four lane reads add
+// the rows, with no LDS round trips. Every lane of the wave must be active.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_mov<0xB1>(v);   // quad_perm 1,0,3,2
+  v += dpp_mov<0x4E>(v);   // quad_perm 2,3,0,1
+  v += dpp_mov<0x124>(v);  // row_ror 4
+  v += dpp_mov<0x128>(v);  // row_ror 8
+  auto lane = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  return (lane(0) + lane(16)) + (lane(32) + lane(48));
 }
 
 template <bool BF16>
