@@ -369,6 +369,24 @@ GemmRM gemm(bool ta, bool tb, long long M, long long N, long long K, const void 
   return g;
 }
 
+// U | V | Q | K = SiLU(X W1 + b1) split into four dense [T, D] arrays, as
+// four GEMMs over the column blocks of W1 with the SiLU in their epilogue
+// (no pre-activation Z is kept: the serving paths have no backward).
+hstu_status_t silu_projection(const void *X, long long T, long long dm, const hstu_layer_weights_t &w, long long D,
+                              GemmType et, void *U, void *V, void *Q, void *K, void *gws, hipStream_t st) {
+  if (T <= 0) return HSTU_OK;
+  const size_t esz = et == kGemmBF16 ? 2 : 4;
+  void *out[4] = {U, V, Q, K};
+  static const char *what[4] = {"f1 GEMM (U)", "f1 GEMM (V)", "f1 GEMM (Q)", "f1 GEMM (K)"};
+  for (int j = 0; j < 4; ++j) {
+    GemmRM g = gemm(false, false, T, D, dm, X, dm, static_cast<const char *>(w.W1) + j * D * esz, 4 * D, out[j], D,
+                    et, et, w.b1 ? w.b1 + j * D : nullptr);
+    g.silu = true;
+    GEMM_RUN(g, what[j]);
+  }
+  return HSTU_OK;
+}
+
 // W (fp32 [M, N]) = A^T B for A [T, M], B [T, N] (row-major, dense, element
 // type et), split over T as splits_for() says; `part` holds the slices.
 hstu_status_t weight_grad(const void *A, long long M, const void *B, long long N, long long T, GemmType et, float *W,
@@ -686,7 +704,7 @@ namespace {
 // rstd [T]), two [T, d_model] buffers the layers alternate between, and
 // the GEMM workspace.
 struct StackLayout {
-  size_t core_bytes, z, u, v, q, k, yo, o, mean, rstd, x[2], gemm, total;
+  size_t core_bytes, u, v, q, k, yo, o, mean, rstd, x[2], gemm, total;
 };
 
 StackLayout stack_layout(const hstu_problem_t *p, int op, int d_model, int microbatch, int hist_max_len) {
@@ -695,7 +713,6 @@ StackLayout stack_layout(const hstu_problem_t *p, int op, int d_model, int micro
   const size_t esz = p->dtype == HSTU_BF16 ? 2 : 4;
   const size_t T = (size_t)p->total_tokens, D = (size_t)p->H * p->d;
   size_t off = align256(y.core_bytes);
-  y.z = off;    off += align256(4 * T * D * esz);
   y.u = off;    off += align256(T * D * esz);
   y.v = off;    off += align256(T * D * esz);
   y.q = off;    off += align256(T * D * esz);
@@ -891,15 +908,22 @@ hstu_status_t hstu_stack_history(const hstu_problem_t *hist, int32_t n_layers, c
   s = check_ws(ws, ws_bytes, y.total);
   if (s) return s;
   hipStream_t st = (hipStream_t)stream;
+  const GemmType et = hist->dtype == HSTU_BF16 ? kGemmBF16 : kGemmF32;
+  const long long D = (long long)hist->H * hist->d;
+  void *gws = at<char>(ws, y.gemm);
   for (int l = 0; l < n_layers; ++l) {
     const hstu_stack_layer_t &L = layers[l];
     hstu_problem_t q = layer_problem(hist, L);
     const void *in = l == 0 ? X : at<char>(ws, y.x[(l - 1) & 1]);
     void *out = (l == n_layers - 1 && Out) ? Out : at<char>(ws, y.x[l & 1]);
-    s = layer_forward(&q, &L.w, in, out, at<char>(ws, y.z), at<char>(ws, y.u), L.V_cache, at<char>(ws, y.q),
-                      L.K_cache, at<char>(ws, y.yo), at<char>(ws, y.o), at<float>(ws, y.mean), at<float>(ws, y.rstd),
-                      ws, y.core_bytes, at<char>(ws, y.gemm), st);
+    void *U = at<char>(ws, y.u), *Q = at<char>(ws, y.q), *Yh = at<char>(ws, y.yo);
+    // K and V of the history go straight into this layer's caches.
+    s = silu_projection(in, T, dm, L.w, D, et, U, L.V_cache, Q, L.K_cache, gws, st);
     if (s) return s;
+    s = hstu_attn_fwd(&q, Q, L.K_cache, L.V_cache, U, Yh, at<char>(ws, y.o), at<float>(ws, y.mean),
+                      at<float>(ws, y.rstd), ws, y.core_bytes, st);
+    if (s) return s;
+    if (T > 0) GEMM_RUN(gemm(false, false, T, dm, D, Yh, D, L.w.W2, dm, out, dm, et, et, L.w.b2), "f2 GEMM");
   }
   return HSTU_OK;
 }
@@ -931,13 +955,10 @@ hstu_status_t hstu_stack_score(const hstu_problem_t *cand, int32_t n_layers, con
     hstu_problem_t q = layer_problem(cand, L);
     const void *in = l == 0 ? Xc : at<char>(ws, y.x[(l - 1) & 1]);
     void *out = l == n_layers - 1 ? Out : at<char>(ws, y.x[l & 1]);
-    void *Z = at<char>(ws, y.z), *U = at<char>(ws, y.u), *V = at<char>(ws, y.v), *Q = at<char>(ws, y.q),
-         *K = at<char>(ws, y.k), *Yc = at<char>(ws, y.yo);
-    if (T > 0) GEMM_RUN(gemm(false, false, T, 4 * D, dm, in, dm, L.w.W1, 4 * D, Z, 4 * D, et, et, L.w.b1), "f1 GEMM");
-    {
-      Timed t_(HSTU_KERNEL_LAYER_EW, st);
-      HIP_TRY(launch_silu_split(Z, T, (int)D, bf16, U, V, Q, K, st), "SiLU split launch");
-    }
+    void *U = at<char>(ws, y.u), *V = at<char>(ws, y.v), *Q = at<char>(ws, y.q), *K = at<char>(ws, y.k),
+         *Yc = at<char>(ws, y.yo);
+    s = silu_projection(in, T, dm, L.w, D, et, U, V, Q, K, gws, st);
+    if (s) return s;
     s = hstu_mfalcon_score(&q, hist_offsets, hist_tokens, hist_max_len, L.K_cache, L.V_cache, hist_ts, Q, K, V, U,
                            microbatch, Yc, at<char>(ws, y.o), at<float>(ws, y.mean), at<float>(ws, y.rstd), ws,
                            y.core_bytes, stream);

@@ -6,7 +6,8 @@
 // swapped and each one's transpose flag kept (a row-major matrix read in
 // place is its own transpose in column-major). A bias over the N columns of
 // the row-major C is then a bias over the rows of the column-major result,
-// which is hipBLASLt's BIAS epilogue.
+// which is hipBLASLt's BIAS epilogue; SiLU after it is the SWISH epilogue
+// (x sigmoid(x)), applied in fp32 before C is rounded.
 //
 // One hipBLASLt handle per device is created on first use and kept for the
 // life of the process. For a new problem (types, flags, sizes, epilogue) the
@@ -32,11 +33,11 @@ constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 hipblasLtHandle_t g_handle[kMaxDevices] = {};
 
-// Algorithm cache key: device, types, transposes, bias, accumulate, the
+// Algorithm cache key: device, types, transposes, epilogue, accumulate, the
 // sizes rounded up to a grid of four steps per octave (a batch of jagged
 // sequences changes the token count every step), whether each matrix is
 // dense, the workspace size and the batch count.
-using Key = std::tuple<int, int, int, int, int, bool, bool, long long, long long, long long, bool, bool, bool, size_t,
+using Key = std::tuple<int, int, int, int, int, int, bool, long long, long long, long long, bool, bool, bool, size_t,
                        int>;
 constexpr int kCandidates = 8;
 constexpr int kTuneRuns = 3;
@@ -131,11 +132,14 @@ int gemm_rm(const GemmRM &g, void *ws, size_t ws_bytes, hipStream_t stream) {
   const int32_t ta = opa, tb = opb;
   GEMM_TRY(hipblasLtMatmulDescSetAttribute(d.op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof ta));
   GEMM_TRY(hipblasLtMatmulDescSetAttribute(d.op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof tb));
+  if (g.bias || g.silu) {
+    const uint32_t epi = g.silu ? (g.bias ? HIPBLASLT_EPILOGUE_SWISH_BIAS_EXT : HIPBLASLT_EPILOGUE_SWISH_EXT)
+                                : HIPBLASLT_EPILOGUE_BIAS;
+    GEMM_TRY(hipblasLtMatmulDescSetAttribute(d.op, HIPBLASLT_MATMUL_DESC_EPILOGUE, &epi, sizeof epi));
+  }
   if (g.bias) {
-    const uint32_t epi = HIPBLASLT_EPILOGUE_BIAS;
     const int32_t bt = HIP_R_32F;
     const void *bp = g.bias;
-    GEMM_TRY(hipblasLtMatmulDescSetAttribute(d.op, HIPBLASLT_MATMUL_DESC_EPILOGUE, &epi, sizeof epi));
     GEMM_TRY(hipblasLtMatmulDescSetAttribute(d.op, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bt, sizeof bt));
     GEMM_TRY(hipblasLtMatmulDescSetAttribute(d.op, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bp, sizeof bp));
   }
@@ -154,7 +158,7 @@ int gemm_rm(const GemmRM &g, void *ws, size_t ws_bytes, hipStream_t stream) {
     GEMM_TRY(hipblasLtMatrixLayoutSetAttribute(d.c, HIPBLASLT_MATRIX_LAYOUT_STRIDED_BATCH_OFFSET, &sc, sizeof sc));
   }
 
-  const Key key{dev, (int)g.ab, (int)g.c, (int)opa, (int)opb, g.bias != nullptr, g.accumulate, bucket(g.M),
+  const Key key{dev, (int)g.ab, (int)g.c, (int)opa, (int)opb, (g.bias != nullptr) + 2 * g.silu, g.accumulate, bucket(g.M),
                 bucket(g.N), bucket(g.K), g.lda == g.K || g.lda == g.M, g.ldb == g.N || g.ldb == g.K, g.ldc == g.N,
                 ws_bytes, g.batch > 1 ? g.batch : 1};
   const float alpha = 1.0f, beta = g.accumulate ? 1.0f : 0.0f;

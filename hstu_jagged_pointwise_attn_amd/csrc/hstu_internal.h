@@ -170,6 +170,7 @@ struct GemmRM {
   long long ldc;
   GemmType ab, c;           // element type of A and B, and of C
   const float *bias;        // fp32 [N] or NULL
+  bool silu;                // C = SiLU(op(A) op(B) + bias) (the epilogue applies it before rounding)
   bool accumulate;
   int batch;                // > 1: a strided batch of GEMMs of these sizes
   long long sA, sB, sC;     // element offsets between consecutive batch entries

@@ -405,7 +405,10 @@ hstu_status_t hstu_layer_bwd(const hstu_problem_t *p, const hstu_layer_weights_t
  * n_tb and the group count come from the problem), and its cache buffers
  * K_cache, V_cache [Th, H, d] (caller-owned, in the problem's dtype). All
  * layers share H, d, d_model, the norm kind and N_max, which the problem
- * passed to each call gives. Xc/X/Out are [tokens, d_model].
+ * passed to each call gives. Xc/X/Out are [tokens, d_model]. The serving
+ * passes keep no pre-activation: f1 runs as four GEMMs (the U, V, Q, K
+ * column blocks of W1) with the SiLU applied in fp32 in the GEMM epilogue,
+ * so U, V, Q, K are rounded once (hstu_layer_fwd rounds Z, then SiLU(Z)).
  */
 typedef struct hstu_stack_layer {
   hstu_layer_weights_t w;
