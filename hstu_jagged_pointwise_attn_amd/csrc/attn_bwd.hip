@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   if (USE_T && tid < 33) {
     const int c = tid - 1;
     const int bkt = c < 0 ? 0 : 31 - c;
-    t2tab[tid] = has_rt ? a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1] : 0.f;
+    t2tab[tid] = has_rt ? -kLog2e * a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1] : 0.f;
     hts[tid] = 0.f;
     if (tid < 32) htb[tid] = 0.f;
   }
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       }
       const int blo = bucket_u32(dlo, a.n_tb), bhi = bucket_u32(dhi, a.n_tb);
       tconst = __builtin_amdgcn_readfirstlane(blo == bhi ? 1 : 0) != 0;
-      tcv = has_rt ? a.rab_t[blo] : 0.f;
+      tcv = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t2tab[ffbh_u32(dlo) + 1])));
       tcidx = blo;
     }
 
@@ -318,18 +318,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           float dsv[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float x = st[mk][nq][i];
+            // t = -log2(e) x with x = S + rab_t (t2tab and tcv hold
+            // -log2(e) rab_t); sig(x) = 1 / (1 + 2^t) and
+            // SiLU'(x) = sig + x sig (1 - sig) = sig + (t sig) (-ln 2) (1 - sig).
             int tix = 0;
+            float t;
             if (USE_T) {
-              if (TC) {
-                x += tcv;
-              } else {
-                tix = ffbh_u32(absdiff_u32(tq[nq], tk4[i])) + 1;
-                x += t2tab[tix];
-              }
+              if (!TC) tix = ffbh_u32(absdiff_u32(tq[nq], tk4[i])) + 1;
+              t = fmaf(st[mk][nq][i], -kLog2e, TC ? tcv : t2tab[tix]);
+            } else {
+              t = st[mk][nq][i] * -kLog2e;
             }
-            const float sg = sigmoid_fast(x);
-            float ds = dpt[mk][nq][i] * sg * (1.0f + x * (1.0f - sg));
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+            float ds = dpt[mk][nq][i] * fmaf(t * sg, fmaf(sg, kLn2, -kLn2), sg);
             bool vis = hirel[nq] > mk * 16 + i;
             if (TFV) vis = vis && (!tfr[nq] || prel > mk * 16 + i || tk4[i] < tq[nq]);
             if (!FULL) ds = vis ? ds : 0.f;
@@ -565,7 +566,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   if (USE_T && tid < 33) {
     const int c = tid - 1;
     const int bkt = c < 0 ? 0 : 31 - c;
-    t2tab[tid] = has_rt ? a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1] : 0.f;
+    t2tab[tid] = has_rt ? -kLog2e * a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1] : 0.f;
   }
 
   // This lane's key (B-operand and C-column layout): k0 + w*16 + lr.
@@ -693,7 +694,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       }
       const int blo = bucket_u32(dlo, a.n_tb), bhi = bucket_u32(dhi, a.n_tb);
       tconst = blo == bhi;
-      tcv = has_rt ? a.rab_t[blo] : 0.f;
+      tcv = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t2tab[ffbh_u32(dlo) + 1])));
     }
     // Under the timestamp filter, candidate rows of this step see the tile's
     // causal keys by time: such a step is partial and takes the gathered path.
@@ -713,11 +714,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         float pv[4], dv4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x = s[mr][i];
-          if (USE_T) x += tconst ? tcv : t2tab[ffbh_u32(absdiff_u32(tr4[i], tk)) + 1];
-          const float sg = sigmoid_fast(x);
-          float p = x * sg;
-          float d = dp[mr][i] * sg * (1.0f + x * (1.0f - sg));
+          // t = -log2(e) x with x = S + rab_t (t2tab and tcv hold
+          // -log2(e) rab_t); p = t sig(x) = -log2(e) SiLU(x), which the dV
+          // scale undoes, and SiLU'(x) = sig + p (-ln 2) (1 - sig).
+          float t;
+          if (USE_T) t = fmaf(s[mr][i], -kLog2e, tconst ? tcv : t2tab[ffbh_u32(absdiff_u32(tr4[i], tk)) + 1]);
+          else t = s[mr][i] * -kLog2e;
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+          float p = t * sg;
+          float d = dp[mr][i] * fmaf(p, fmaf(sg, kLn2, -kLn2), sg);
           bool vis = mr * 16 + i >= rrel;
           if (TF && tf_step) {
             const int row = fr0 + lg * 4 + mr * 16 + i;
@@ -759,7 +764,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  // Stage dK and dV (C layout: key 4 lg + i, column 16 nd + lr) through LDS.
+  // Stage dK and dV (C layout: key 4 lg + i, column 16 nd + lr) through LDS;
+  // dV summed -log2(e) SiLU(.) dO, which -ln(2) / N_max restores.
+  const float vscale = a.inv_nmax * -kLn2;
   u16 *sk = Qs, *sv = Os;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -767,7 +774,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) {
       sk[kr * ST + nd * 16 + lr] = __builtin_bit_cast(u16, (__bf16)(dk[nd][i] * a.inv_nmax));
-      sv[kr * ST + nd * 16 + lr] = __builtin_bit_cast(u16, (__bf16)(dv[nd][i] * a.inv_nmax));
+      sv[kr * ST + nd * 16 + lr] = __builtin_bit_cast(u16, (__bf16)(dv[nd][i] * vscale));
     }
   }
   __syncthreads();

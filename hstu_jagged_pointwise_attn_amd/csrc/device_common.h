@@ -15,6 +15,7 @@ typedef unsigned int u32;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bf2f(u16 x) { return __uint_as_float((u32)x << 16); }
 
