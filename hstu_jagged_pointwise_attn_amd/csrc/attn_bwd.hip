@@ -355,9 +355,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         dsa[nq] = __builtin_bit_cast(bf16x8, wds);
       }
       if (USE_T && TC) {
-        float t = tsum;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+        const float t = wave_sum_f32(tsum);
         if (lane == 0) atomicAdd(&htb[tcidx], t);
       }
       if (USE_T && !TC && run_b >= 0) atomicAdd(&hts[run_b], run_s);

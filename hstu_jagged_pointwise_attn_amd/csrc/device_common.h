@@ -85,6 +85,20 @@ __device__ __forceinline__ unsigned wave_ext_u32(unsigned v) {
 __device__ __forceinline__ unsigned wave_min_u32(unsigned v) { return wave_ext_u32<false>(v); }
 __device__ __forceinline__ unsigned wave_max_u32(unsigned v) { return wave_ext_u32<true>(v); }
 
+// Wave-wide fp32 sum by the same DPP pattern (every lane active).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x124>(v);
+  v += dpp_f32<0x128>(v);
+  auto at = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  return (at(0) + at(16)) + (at(32) + at(48));
+}
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
