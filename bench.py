@@ -496,7 +496,8 @@ def bench_stack(args):
                                      "latency_ms": {"eager": eager_lat, "graph": graph_lat}}},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": dom + (" (2 launches per layer)" if dom == "gemm" else f" ({nl} launches)"),
+                     "kernel": dom + (" (5 launches per layer: f1 as four SiLU-epilogue GEMMs, f2)" if dom == "gemm"
+                                      else f" ({nl} launches)"),
                      "kernel_ms": per_step[dom], "per_kernel_ms_per_step": per_step},
         "cpu_baseline": cpu,
     }
