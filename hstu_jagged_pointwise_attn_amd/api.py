@@ -292,19 +292,21 @@ def layer_workspace_size(p, d_model: int, op) -> int:
     return int(n.value)
 
 
-def layer_fwd(p, w, X, *, Out=None, Z=None, UVQK=None, save_act=False, Y=None, O=None, mean=None, rstd=None,
-              ws=None, stream=None):
+def layer_fwd(p, w, X, *, Out=None, Z=None, UVQK=None, save_act=False, keep_z=True, Y=None, O=None, mean=None,
+              rstd=None, ws=None, stream=None):
     """hstu_layer_fwd. X: [T, d_model]. Returns a namespace with Out
-    [T, d_model] and the saved Z [T, 4D], Y, O [T, D], mean, rstd, ws, and
-    UVQK [4, T, D] (the activations, kept for the backward) when save_act is
-    set or UVQK is given (else None)."""
+    [T, d_model] and the saved Z [T, 4D] (None when keep_z is false and no Z
+    is given: the inference form, SiLU in the f1 GEMMs' epilogue), Y, O
+    [T, D], mean, rstd, ws, and UVQK [4, T, D] (the activations, kept for the
+    backward) when save_act is set or UVQK is given (else None)."""
     T, D, dm = p.total_tokens, p.H * p.d, w.d_model
     dev, dt = X.device, X.dtype
     if _DTYPES.get(dt) != p.dtype:
         raise TypeError("tensor dtype differs from the problem's dtype")
     _need(X, "X", dt, dev, T * dm)
     Out = torch.empty(T, dm, dtype=dt, device=dev) if Out is None else Out
-    Z = torch.empty(T, 4 * D, dtype=dt, device=dev) if Z is None else Z
+    if Z is None and keep_z:
+        Z = torch.empty(T, 4 * D, dtype=dt, device=dev)
     if UVQK is None and save_act:
         UVQK = torch.empty(4, T, D, dtype=dt, device=dev)
     _need(UVQK, "UVQK", dt, dev, 4 * T * D)

@@ -768,10 +768,13 @@ hstu_status_t layer_forward(const hstu_problem_t *p, const hstu_layer_weights_t 
   const bool bf16 = p->dtype == HSTU_BF16;
   const GemmType et = bf16 ? kGemmBF16 : kGemmF32;
   const long long D = (long long)p->H * p->d, dm = w->d_model;
-  if (T > 0) GEMM_RUN(gemm(false, false, T, 4 * D, dm, X, dm, w->W1, 4 * D, Z, 4 * D, et, et, w->b1), "f1 GEMM");
-  {
+  if (Z) {
+    if (T > 0) GEMM_RUN(gemm(false, false, T, 4 * D, dm, X, dm, w->W1, 4 * D, Z, 4 * D, et, et, w->b1), "f1 GEMM");
     Timed t_(HSTU_KERNEL_LAYER_EW, st);
     HIP_TRY(launch_silu_split(Z, T, (int)D, bf16, U, V, Q, K, st), "SiLU split launch");
+  } else {
+    hstu_status_t s = silu_projection(X, T, dm, *w, D, et, U, V, Q, K, gws, st);
+    if (s) return s;
   }
   hstu_status_t s = hstu_attn_fwd(p, Q, K, V, U, Y, O, mean, rstd, ws_core, core_bytes, st);
   if (s) return s;
@@ -800,7 +803,7 @@ hstu_status_t hstu_layer_fwd(const hstu_problem_t *p, const hstu_layer_weights_t
   s = check_layer(p, w);
   if (s) return s;
   const long long T = p->total_tokens;
-  if (T > 0 && (!X || !Out || !Z || !Y || !O)) return fail(HSTU_ERR_INVALID_ARG, "X/Out/Z/Y/O must not be NULL");
+  if (T > 0 && (!X || !Out || !Y || !O)) return fail(HSTU_ERR_INVALID_ARG, "X/Out/Y/O must not be NULL");
   if (!aligned16(X) || !aligned16(Out) || !aligned16(Z) || !aligned16(UVQK) || !aligned16(Y) || !aligned16(O))
     return fail(HSTU_ERR_INVALID_ARG, "X/Out/Z/UVQK/Y/O must be 16-byte aligned");
   const LayerLayout y = layer_layout(p, HSTU_OP_FWD, w->d_model);

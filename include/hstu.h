@@ -358,7 +358,10 @@ hstu_status_t hstu_layer_workspace_size(const hstu_problem_t *p, int32_t d_model
  * UVQK is optional: NULL keeps the activations U, V, Q, K in ws; else they
  * are written to UVQK [4, T, D] (U, then V, Q, K, each [T, D]) so that the
  * backward can reuse them instead of recomputing them from Z (4*T*D more
- * elements of memory for one pass less).
+ * elements of memory for one pass less). Z may be NULL when no backward
+ * follows (inference): f1 then runs as four GEMMs with the SiLU applied in
+ * fp32 in their epilogue, as the serving stack does, so U, V, Q, K are
+ * rounded once instead of twice and no pre-activation is written.
  * p describes the jagged batch, its masks, rab tables and norm exactly as for
  * hstu_attn_fwd. The first call on a device creates that device's hipBLASLt
  * handle, which loads hipBLASLt's kernels; apart from that handle nothing is

@@ -95,6 +95,25 @@ def test_layer_fwd_bwd_match_oracle(lp, save):
         assert v <= tol(lp.core), (k, v)
 
 
+@pytest.mark.parametrize("lp", _layers()[:4], ids=lambda v: v.name)
+def test_layer_inference_form_without_z(lp):
+    """Z = NULL: f1 as four GEMMs with the SiLU in their epilogue (U, V, Q, K
+    rounded once); Out, Y and O match the oracle and the Z form."""
+    _say("layer inference", lp.name)
+    ns = device.upload_layer(lp)
+    fz = device.run_layer_fwd(ns)
+    fi = device.run_layer_fwd(ns, keep_z=False)
+    torch.cuda.synchronize()
+    assert fi.Z is None and api.device_status(fi.ws) == 0
+    ref = oracle_layer_fwd(lp)
+    for name in ("Out", "Y", "O"):
+        got = getattr(fi, name)
+        e_ref = rel_l2(got.float().cpu().numpy(), ref[name])
+        e_z = rel_l2(got.float().cpu().numpy(), getattr(fz, name).float().cpu().numpy())
+        _say(f"  {name}: vs oracle {e_ref:.2e}, vs the Z form {e_z:.2e}")
+        assert e_ref <= tol(lp.core) and e_z <= tol(lp.core), name
+
+
 def test_layer_bias_gradients_without_bias_inputs_are_column_sums():
     """With b1 = b2 = None the layer still returns db1, db2 (the gradients a
     zero bias would get): they must equal the column sums of dZ and dOut."""
