@@ -102,7 +102,23 @@ struct Layout {
   // backward only: key-major schedule and the gradient of the pre-norm output
   size_t khdr, kdesc, kqoff, ktiles, dO;
   long long max_ktiles;
+  // backward with a norm affine of at most kNormAffineLdsMax entries per
+  // table: per-workgroup partials of d gamma / d beta (npart_blocks rows)
+  size_t npart;
+  long long npart_blocks;
+  int norm_tpw;
 };
+
+// Tokens per wave of the norm backward when it sums d gamma / d beta per
+// workgroup in LDS: at least 8, and few enough workgroups (at most 1024)
+// that the partials stay small.
+int norm_affine_tpw(long long T) { return (int)std::max<long long>(8, (T + 4095) / 4096); }
+
+bool norm_affine_in_lds(const hstu_problem_t *p) {
+  if (p->norm == HSTU_NORM_NONE || (!p->gamma && !p->beta)) return false;
+  const long long G = p->norm == HSTU_NORM_GLN ? p->n_groups : 1;
+  return G * p->H * p->d <= kNormAffineLdsMax;
+}
 
 Layout layout(const hstu_problem_t *p, int op, int microbatch, int hist_max_len) {
   Tiles t = tiles_for(p, op);
@@ -130,6 +146,12 @@ Layout layout(const hstu_problem_t *p, int op, int microbatch, int hist_max_len)
     L.ktiles = off; off += align256(sizeof(QTile) * (size_t)(nk > 0 ? nk : 1));
     const size_t esz = p->dtype == HSTU_BF16 ? 2 : 4;
     L.dO = off;     off += align256(esz * (size_t)p->total_tokens * p->H * p->d + 16);
+    if (norm_affine_in_lds(p) && p->total_tokens > 0) {
+      const long long G = p->norm == HSTU_NORM_GLN ? p->n_groups : 1;
+      L.norm_tpw = norm_affine_tpw(p->total_tokens);
+      L.npart_blocks = norm_bwd_blocks(p->total_tokens, L.norm_tpw);
+      L.npart = off;  off += align256(sizeof(float) * 2 * (size_t)(G * p->H * p->d) * (size_t)L.npart_blocks);
+    }
   }
   L.total = off;
   return L;
@@ -552,12 +574,15 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
   const int G = p->norm == HSTU_NORM_GLN ? p->n_groups : 1;
   float *dg = (p->gamma && p->norm != HSTU_NORM_NONE) ? d_gamma : nullptr;
   float *db = (p->beta && p->norm != HSTU_NORM_NONE) ? d_beta : nullptr;
+  // d gamma / d beta: per-workgroup LDS partials and a reduction when the
+  // tables are small (and there are tokens), else global atomics.
+  const bool aff_lds = (dg || db) && L.npart_blocks > 0;
   {
     Timed t_(HSTU_KERNEL_AUX, st);
     if (p->rab_p) HIP_TRY(launch_fill_f32(d_rab_p, p->n_pos, 0.f, st), "fill");
     if (p->rab_t && d_rab_t) HIP_TRY(launch_fill_f32(d_rab_t, p->n_tb, 0.f, st), "fill");
-    if (dg) HIP_TRY(launch_fill_f32(dg, (long long)G * D, 0.f, st), "fill");
-    if (db) HIP_TRY(launch_fill_f32(db, (long long)G * D, 0.f, st), "fill");
+    if (dg && !aff_lds) HIP_TRY(launch_fill_f32(dg, (long long)G * D, 0.f, st), "fill");
+    if (db && !aff_lds) HIP_TRY(launch_fill_f32(db, (long long)G * D, 0.f, st), "fill");
   }
   void *dO = at<char>(ws, L.dO);
   {
@@ -571,13 +596,17 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
     n.T = T;
     n.D = D;
     // One token per wave when no affine gradient is summed (as many waves as
-    // tokens keep the loads in flight); otherwise runs of 32 tokens, whose
-    // dgamma / dbeta partials leave with one atomic per column and run.
-    n.tokens_per_wave = (dg || db) ? 32 : 1;
+    // tokens keep the loads in flight); with small affine tables, short runs
+    // summed per workgroup in LDS; otherwise runs of 32 tokens, whose
+    // dgamma / dbeta partials leave with one global atomic per column and run.
+    n.tokens_per_wave = aff_lds ? L.norm_tpw : (dg || db) ? 32 : 1;
     n.dU = dU; n.dX = dO;
     n.dgamma = dg; n.dbeta = db;
+    n.partial = aff_lds ? at<float>(ws, L.npart) : nullptr;
     Timed t_(HSTU_KERNEL_NORM_BWD, st);
     HIP_TRY(launch_norm_bwd(n, bf16, st), "norm backward launch");
+    if (aff_lds)
+      HIP_TRY(launch_norm_affine_reduce(n.partial, L.npart_blocks, G * D, dg, db, st), "norm affine reduce launch");
   }
   BwdArgs b;
   std::memset(&b, 0, sizeof b);

@@ -116,8 +116,19 @@ struct NormBwdArgs {
   void *dU;                       // [T, D]
   void *dX;                       // [T, D] gradient w.r.t. the pre-norm output
   float *dgamma, *dbeta;          // [G, D] accumulated with atomics (zeroed by the caller), or NULL
+  // When set, dgamma / dbeta are instead summed per workgroup in LDS into
+  // partial [workgroups][2][G][D] (fp32) and reduced by launch_norm_affine_reduce.
+  float *partial;
 };
 hipError_t launch_norm_bwd(const NormBwdArgs &a, bool bf16, hipStream_t s);
+// Workgroups of the norm backward launch for these sizes.
+long long norm_bwd_blocks(long long T, int tokens_per_wave);
+// dgamma / dbeta (each [G, D], overwritten; either may be NULL) = the sum over
+// `blocks` rows of partial [blocks][2][G][D].
+hipError_t launch_norm_affine_reduce(const float *partial, long long blocks, int GD, float *dgamma, float *dbeta,
+                                     hipStream_t s);
+// Largest G * D whose two affine rows fit the norm backward's LDS accumulator.
+constexpr int kNormAffineLdsMax = 8192;
 
 // Backward attention kernels. dO is the gradient w.r.t. the pre-norm output
 // (computed by the norm backward into the workspace).

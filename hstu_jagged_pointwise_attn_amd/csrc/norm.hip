@@ -173,16 +173,26 @@ hipError_t norm_fwd_dispatch(const NormArgs &a, hipStream_t s) {
 //           dgamma += dN * xhat, dbeta += dN   (row of the token's group)
 //   NONE:   dX = dN.
 // Each wave walks a contiguous run of tokens and keeps the affine gradients
-// of the current group in registers, flushing them with atomics only when
-// the group changes and at the end of its run.
+// of the current group in registers, flushing them only when the group
+// changes and at the end of its run: with `partial` into the workgroup's
+// [2][G][D] rows in LDS (written out per workgroup and reduced by a second
+// kernel), else with global atomics.
 template <bool BF16, int MAXCH>
 __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
   using V = Vec<BF16>;
   constexpr int N = V::N;
+  extern __shared__ float s_aff[];  // [2][G][D] with `partial`
   const int lane = threadIdx.x & 63;
   const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const long long t0 = wave * a.tokens_per_wave;
-  if (t0 >= a.T) return;
+  const bool lds_acc = a.partial != nullptr;
+  const int GD = a.n_groups * a.D;
+  if (lds_acc) {
+    for (int i = threadIdx.x; i < 2 * GD; i += 256) s_aff[i] = 0.f;
+    __syncthreads();
+  } else if (t0 >= a.T) {
+    return;
+  }
   const long long t1 = min(a.T, t0 + a.tokens_per_wave);
   const int D = a.D, nch = D / N;
   const bool affine = a.mode != HSTU_NORM_NONE && (a.dgamma || a.dbeta);
@@ -201,8 +211,13 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
 #pragma unroll
         for (int e = 0; e < N; ++e) {
           const long long c = (long long)g * D + ch * N + e;
-          if (a.dgamma) atomicAdd(a.dgamma + c, dg[k][e]);
-          if (a.dbeta) atomicAdd(a.dbeta + c, db[k][e]);
+          if (lds_acc) {
+            atomicAdd(&s_aff[c], dg[k][e]);
+            atomicAdd(&s_aff[GD + c], db[k][e]);
+          } else {
+            if (a.dgamma) atomicAdd(a.dgamma + c, dg[k][e]);
+            if (a.dbeta) atomicAdd(a.dbeta + c, db[k][e]);
+          }
           dg[k][e] = db[k][e] = 0.f;
         }
       }
@@ -290,19 +305,51 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
     }
   }
   if (affine) flush(gcur);
+  if (lds_acc) {
+    __syncthreads();
+    float *out = a.partial + (long long)blockIdx.x * 2 * GD;
+    for (int i = threadIdx.x; i < 2 * GD; i += 256) out[i] = s_aff[i];
+  }
 }
 
 template <bool BF16>
 hipError_t norm_bwd_dispatch(const NormBwdArgs &a, hipStream_t s) {
   const int nch = a.D / Vec<BF16>::N;
-  const long long waves = (a.T + a.tokens_per_wave - 1) / a.tokens_per_wave;
-  const dim3 grid((unsigned)((waves + 3) / 4));
-  if (nch <= 64) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 1>), grid, dim3(256), 0, s, a);
-  else if (nch <= 128) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 2>), grid, dim3(256), 0, s, a);
-  else if (nch <= 256) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 4>), grid, dim3(256), 0, s, a);
-  else if (nch <= 512) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 8>), grid, dim3(256), 0, s, a);
+  const dim3 grid((unsigned)norm_bwd_blocks(a.T, a.tokens_per_wave));
+  const size_t lds = a.partial ? 2 * sizeof(float) * a.n_groups * a.D : 0;
+  if (nch <= 64) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 1>), grid, dim3(256), lds, s, a);
+  else if (nch <= 128) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 2>), grid, dim3(256), lds, s, a);
+  else if (nch <= 256) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 4>), grid, dim3(256), lds, s, a);
+  else if (nch <= 512) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 8>), grid, dim3(256), lds, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+// Column sums of partial [blocks][2 GD]: a workgroup takes 64 columns, its
+// sixteen waves every sixteenth block row (eight loads in flight each), and
+// LDS adds the sixteen.
+__global__ __launch_bounds__(1024) void norm_affine_reduce_kernel(const float *partial, long long blocks, int GD,
+                                                                  float *dgamma, float *dbeta) {
+  __shared__ float s_sum[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + lane;
+  float acc = 0.f;
+  if (col < 2 * GD) {
+#pragma unroll 8
+    for (long long b = w; b < blocks; b += 16) acc += partial[b * 2 * GD + col];
+  }
+  s_sum[w][lane] = acc;
+  __syncthreads();
+  if (w == 0 && col < 2 * GD) {
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v += s_sum[i][lane];
+    if (col < GD) {
+      if (dgamma) dgamma[col] = v;
+    } else if (dbeta) {
+      dbeta[col - GD] = v;
+    }
+  }
 }
 
 __global__ void fill_f32_kernel(float *p, long long n, float v) {
@@ -322,9 +369,22 @@ hipError_t launch_norm_fwd(const NormArgs &a, bool bf16, hipStream_t s) {
 
 namespace hstu {
 
+long long norm_bwd_blocks(long long T, int tokens_per_wave) {
+  const long long waves = (T + tokens_per_wave - 1) / tokens_per_wave;
+  return (waves + 3) / 4;
+}
+
 hipError_t launch_norm_bwd(const NormBwdArgs &a, bool bf16, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   return bf16 ? norm_bwd_dispatch<true>(a, s) : norm_bwd_dispatch<false>(a, s);
+}
+
+hipError_t launch_norm_affine_reduce(const float *partial, long long blocks, int GD, float *dgamma, float *dbeta,
+                                     hipStream_t s) {
+  if (GD <= 0 || blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(norm_affine_reduce_kernel, dim3((unsigned)((2 * GD + 63) / 64)), dim3(1024), 0, s, partial,
+                     blocks, GD, dgamma, dbeta);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_f32(float *p, long long n, float v, hipStream_t s) {
