@@ -39,7 +39,7 @@ hipblasLtHandle_t g_handle[kMaxDevices] = {};
 // dense, the workspace size and the batch count.
 using Key = std::tuple<int, int, int, int, int, int, bool, long long, long long, long long, bool, bool, bool, size_t,
                        int>;
-constexpr int kCandidates = 8;
+constexpr int kCandidates = 32;
 constexpr int kTuneRuns = 3;
 
 long long bucket(long long x) {
