@@ -271,9 +271,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int nq = 0; nq < 2; ++nq) hirel[nq] = hi_r[nq] - (c0 + lg * 4);
 
-    bool tconst = true;
-    float tcv = 0.f;
-    int tcidx = 0;
+    bool tconst = true, two = false;
+    float tcv = 0.f, tcv_hi = 0.f;
+    int tcidx = 0, tcidx_hi = 0;
+    unsigned thr = 0u;
     if (USE_T) {
       const unsigned kmin = __builtin_amdgcn_readfirstlane(tkst[b * 2]);
       const unsigned kmax = __builtin_amdgcn_readfirstlane(tkst[b * 2 + 1]);
@@ -292,6 +293,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       tconst = __builtin_amdgcn_readfirstlane(blo == bhi ? 1 : 0) != 0;
       tcv = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t2tab[ffbh_u32(dlo) + 1])));
       tcidx = blo;
+      // Two buckets: |dt| >= 2^bhi is bucket bhi, the rest blo (bhi may be
+      // the clamped last bucket; blo is then below the clamp).
+      two = __builtin_amdgcn_readfirstlane(bhi == blo + 1 ? 1 : 0) != 0;
+      if (two) {
+        thr = 1u << bhi;
+        tcv_hi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t2tab[32 - bhi])));
+        tcidx_hi = bhi;
+      }
     }
 
     // dS of this wave's 32 rows x 32 keys (fp32, masked), its bf16 copy as the
@@ -301,12 +310,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     // buckets come in runs that are merged before they go to the histogram.
     // TFV: a candidate row under the timestamp filter also needs its key in
     // the prefix or strictly earlier in time (partial, gathered tiles only).
-    auto epilogue = [&](auto fullc, auto tconstc, auto tfc) __attribute__((always_inline)) {
+    auto epilogue = [&](auto fullc, auto tconstc, auto tfc, auto twoc) __attribute__((always_inline)) {
       constexpr bool FULL = decltype(fullc)::value, TC = decltype(tconstc)::value;
-      constexpr bool TFV = decltype(tfc)::value;
-      static_assert(!TFV || (USE_T && !FULL && !TC), "the filter runs on partial gathered tiles");
+      constexpr bool TFV = decltype(tfc)::value, T2 = decltype(twoc)::value;
+      static_assert(!TFV || (USE_T && !FULL && !TC && !T2), "the filter runs on partial gathered tiles");
+      static_assert(!T2 || !TC, "two buckets is a per-element path");
       const int prel = sd.P - (c0 + lg * 4);
-      float tsum = 0.f, run_s = 0.f;
+      float tsum = 0.f, tsum_hi = 0.f, run_s = 0.f;
       int run_b = -1;
 #pragma unroll
       for (int nq = 0; nq < 2; ++nq) {
@@ -322,10 +332,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
             // -log2(e) rab_t); sig(x) = 1 / (1 + 2^t) and
             // SiLU'(x) = sig + x sig (1 - sig) = sig + (t sig) (-ln 2) (1 - sig).
             int tix = 0;
+            bool hi = false;
             float t;
             if (USE_T) {
-              if (!TC) tix = ffbh_u32(absdiff_u32(tq[nq], tk4[i])) + 1;
-              t = fmaf(st[mk][nq][i], -kLog2e, TC ? tcv : t2tab[tix]);
+              if (T2) {
+                hi = absdiff_u32(tq[nq], tk4[i]) >= thr;
+                t = fmaf(st[mk][nq][i], -kLog2e, hi ? tcv_hi : tcv);
+              } else {
+                if (!TC) tix = ffbh_u32(absdiff_u32(tq[nq], tk4[i])) + 1;
+                t = fmaf(st[mk][nq][i], -kLog2e, TC ? tcv : t2tab[tix]);
+              }
             } else {
               t = st[mk][nq][i] * -kLog2e;
             }
@@ -337,8 +353,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
             dsv[i] = ds;
             if (USE_P) skw[(nq * 16 + lr) * SKW + mk * 16 + lg * 4 + i + 31 - sh_r[nq]] = ds;
             if (USE_T) {
-              if (TC) {
+              if (TC || T2) {
                 tsum += ds;
+                if (T2) tsum_hi += hi ? ds : 0.f;
               } else {
                 if (tix != run_b) {
                   if (run_b >= 0) atomicAdd(&hts[run_b], run_s);
@@ -358,22 +375,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         const float t = wave_sum_f32(tsum);
         if (lane == 0) atomicAdd(&htb[tcidx], t);
       }
-      if (USE_T && !TC && run_b >= 0) atomicAdd(&hts[run_b], run_s);
+      if (USE_T && T2) {
+        const float t = wave_sum_f32(tsum), th = wave_sum_f32(tsum_hi);
+        if (lane == 0) {
+          atomicAdd(&htb[tcidx], t - th);
+          atomicAdd(&htb[tcidx_hi], th);
+        }
+      }
+      if (USE_T && !TC && !T2 && run_b >= 0) atomicAdd(&hts[run_b], run_s);
     };
     bool done = false;
     if constexpr (TF) {
       if (wave_tf && !full) {
-        epilogue(bc<false>(), bc<false>(), bc<true>());
+        epilogue(bc<false>(), bc<false>(), bc<true>(), bc<false>());
         done = true;
       }
     }
     if (!done) {
-      if (USE_T && !tconst) {
-        if (full) epilogue(bc<true>(), bc<false>(), bc<false>());
-        else epilogue(bc<false>(), bc<false>(), bc<false>());
+      if (USE_T && !tconst && two) {
+        if (full) epilogue(bc<true>(), bc<false>(), bc<false>(), bc<true>());
+        else epilogue(bc<false>(), bc<false>(), bc<false>(), bc<true>());
+      } else if (USE_T && !tconst) {
+        if (full) epilogue(bc<true>(), bc<false>(), bc<false>(), bc<false>());
+        else epilogue(bc<false>(), bc<false>(), bc<false>(), bc<false>());
       } else {
-        if (full) epilogue(bc<true>(), bc<true>(), bc<false>());
-        else epilogue(bc<false>(), bc<true>(), bc<false>());
+        if (full) epilogue(bc<true>(), bc<true>(), bc<false>(), bc<false>());
+        else epilogue(bc<false>(), bc<true>(), bc<false>(), bc<false>());
       }
     }
     if (USE_P) {

@@ -92,17 +92,19 @@ __device__ __forceinline__ void fwd_store_tile(const TilePrefetch<NCH> &pf, int 
 // P = SiLU(S + rab_t) (masked on PARTIAL tiles) as the bf16 A operands of
 // P V: pa[nq][kk] holds keys kk*32 + {lg*4 + 0..3, 16 + lg*4 + 0..3}.
 // FULL: every pair of the tile is visible. TCONST: rab_t is the scalar tcv
-// for the whole block, else it is gathered per element.
+// for the whole block; T2: the block spans two buckets, tcv below |dt| = thr
+// and tcv_hi from there on; else rab_t is gathered per element.
 // TF (timestamp filter, partial tiles with the gathered rab_t path only): a
 // row flagged in tfr also needs its key inside the prefix (prel = P - first
 // key of this lane's group) or strictly earlier in time.
-template <bool FULL, bool USE_T, bool TCONST, bool TF = false>
+template <bool FULL, bool USE_T, bool TCONST, bool TF = false, bool T2 = false>
 __device__ __forceinline__ void fwd_epilogue(const f32x4 (&st)[4][2], bf16x8 (&pa)[2][2],
                                              const int (&hirel)[2], const unsigned (&tq)[2],
                                              const unsigned *tkb, const float *t2tab, float tcv,
                                              int lg, const bool (&tfr)[2] = {false, false},
-                                             int prel = 0) {
-  static_assert(!TF || (USE_T && !FULL && !TCONST), "the filter runs on partial gathered tiles");
+                                             int prel = 0, unsigned thr = 0u, float tcv_hi = 0.f) {
+  static_assert(!TF || (USE_T && !FULL && !TCONST && !T2), "the filter runs on partial gathered tiles");
+  static_assert(!T2 || !TCONST, "two buckets is a per-element path");
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     u32x4 w[2];
@@ -120,7 +122,8 @@ __device__ __forceinline__ void fwd_epilogue(const f32x4 (&st)[4][2], bf16x8 (&p
           // t / (1 + 2^t) = -log2(e) SiLU(S + rab_t); the output scale undoes
           // the factor.
           float t;
-          if (USE_T) t = fmaf(st[mk][nq][i], -kLog2e, TCONST ? tcv : t2tab[ffbh_u32(absdiff_u32(tq[nq], tk4[i])) + 1]);
+          if (USE_T && T2) t = fmaf(st[mk][nq][i], -kLog2e, absdiff_u32(tq[nq], tk4[i]) >= thr ? tcv_hi : tcv);
+          else if (USE_T) t = fmaf(st[mk][nq][i], -kLog2e, TCONST ? tcv : t2tab[ffbh_u32(absdiff_u32(tq[nq], tk4[i])) + 1]);
           else t = st[mk][nq][i] * -kLog2e;
           p[i] = t * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
           bool vis = hirel[nq] > mk * 16 + i;
@@ -316,8 +319,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     for (int nq = 0; nq < 2; ++nq) hirel[nq] = hi_r[nq] - (c0 + lg * 4);
 
     // rab_t: one constant for the block when all its pairs share a bucket.
-    bool tconst = true;
-    float tcv = 0.f;
+    bool tconst = true, two = false;
+    float tcv = 0.f, tcv_hi = 0.f;
+    unsigned thr = 0u;
     if (USE_T) {
       const unsigned kmin = __builtin_amdgcn_readfirstlane(tkst[b * 2]);
       const unsigned kmax = __builtin_amdgcn_readfirstlane(tkst[b * 2 + 1]);
@@ -335,6 +339,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       const int blo = bucket_u32(dlo, a.n_tb), bhi = bucket_u32(dhi, a.n_tb);
       tconst = blo == bhi;
       tcv = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t2tab[ffbh_u32(dlo) + 1])));
+      // Two buckets: |dt| >= 2^bhi is bucket bhi, the rest blo (bhi may be
+      // the clamped last bucket; blo is then below the clamp).
+      two = bhi == blo + 1;
+      if (two) {
+        thr = 1u << bhi;
+        tcv_hi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t2tab[32 - bhi])));
+      }
     }
 
     const unsigned *tkb = tkey + b * (USE_T ? BN : 0);
@@ -347,7 +358,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
           goto tile_done;
         }
       }
-      if (USE_T && !tconst) {
+      if (USE_T && !tconst && two) {
+        if (full) fwd_epilogue<true, USE_T, false, false, true>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg, tfr, 0, thr, tcv_hi);
+        else fwd_epilogue<false, USE_T, false, false, true>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg, tfr, 0, thr, tcv_hi);
+      } else if (USE_T && !tconst) {
         if (full) fwd_epilogue<true, USE_T, false>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
         else fwd_epilogue<false, USE_T, false>(st, pa, hirel, tq_r, tkb, t2tab, tcv, lg);
       } else {
