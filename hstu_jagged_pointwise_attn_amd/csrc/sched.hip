@@ -156,29 +156,110 @@ __device__ int block_exclusive_scan(int v, int *s_wsum, int *total) {
   return excl;
 }
 
-// Bitonic sort of n2 (a power of two, at most kSchedThreads) keys, one per
-// thread: stages with partners in the same wave exchange through lane
-// shuffles, the others through LDS. Every thread of the block calls it.
-__device__ void sort_small(unsigned *keys, int n2) {
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_u32(unsigned x) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// The value of lane (lane ^ J), J < 64. J = 1, 2: quad permutes; J = 8: a
+// rotation by 8 within the row of 16; J = 4: one of the rotations by 4 and
+// by 12, whichever reaches lane ^ 4 (fwd4, found once from the lane ids);
+// J = 16, 32: a lane permute through the LDS crossbar. All lanes active.
+template <int J>
+__device__ __forceinline__ unsigned lane_xor(unsigned x, bool fwd4) {
+  if constexpr (J == 1) return dpp_u32<0xB1>(x);  // quad_perm 1,0,3,2
+  else if constexpr (J == 2) return dpp_u32<0x4E>(x);  // quad_perm 2,3,0,1
+  else if constexpr (J == 4) {
+    const unsigned a = dpp_u32<0x124>(x), b = dpp_u32<0x12C>(x);  // row_ror 4, 12
+    return fwd4 ? a : b;
+  } else if constexpr (J == 8) return dpp_u32<0x128>(x);  // row_ror 8
+  else return (unsigned)__shfl_xor((int)x, J, 64);
+}
+
+// One compare-exchange stage of distance J < 64 on the E keys of a thread
+// (index tid + e * kSchedThreads), partners in the same wave.
+template <int J, int E>
+__device__ __forceinline__ void wave_stage(unsigned (&x)[E], int k, bool fwd4) {
   const int tid = threadIdx.x;
-  unsigned x = tid < n2 ? keys[tid] : 0xffffffffu;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid + e * kSchedThreads;
+    const unsigned y = lane_xor<J>(x[e], fwd4);
+    const bool up = (i & k) == 0, lower = (i & J) == 0;
+    x[e] = (lower == up) ? min(x[e], y) : max(x[e], y);
+  }
+}
+
+// Bitonic sort of n2 keys (a power of two, at most E * kSchedThreads), E per
+// thread at indices tid + e * kSchedThreads, kept in registers. Per merge
+// size k, the stages run from distance k/2 down to 1: partners in the same
+// thread (distance >= kSchedThreads), through two LDS buffers used in turn
+// with one barrier each (64 .. kSchedThreads/2), then within the wave as
+// straight-line code (32 .. 1), so that a stage costs a few vector
+// instructions and no scalar branching. keys holds the input and receives
+// the output; tmp is the second buffer. Every thread of the block calls it.
+template <int E>
+__device__ void sort_keys(unsigned *keys, unsigned *tmp, int n2) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const bool fwd4 = dpp_u32<0x124>((unsigned)lane) == (unsigned)(lane ^ 4);
+  unsigned x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid + e * kSchedThreads;
+    x[e] = i < n2 ? keys[i] : 0xffffffffu;
+  }
+  int pb = 0;
   for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      unsigned y;
-      if (j >= 64) {
-        __syncthreads();
-        if (tid < n2) keys[tid] = x;
-        __syncthreads();
-        y = tid < n2 ? keys[tid ^ j] : 0xffffffffu;
-      } else {
-        y = (unsigned)__shfl_xor((int)x, j, 64);
+    int j = k >> 1;
+    if constexpr (E > 1) {
+      for (; j >= kSchedThreads; j >>= 1) {
+        const int d = j / kSchedThreads;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+#pragma unroll
+          for (int f = e + 1; f < E; ++f) {
+            if (f != (e | d) || (e & d)) continue;
+            const bool up = ((tid + e * kSchedThreads) & k) == 0;
+            const unsigned lo = min(x[e], x[f]), hi = max(x[e], x[f]);
+            x[e] = up ? lo : hi;
+            x[f] = up ? hi : lo;
+          }
+        }
       }
-      const bool up = (tid & k) == 0, lower = (tid & j) == 0;
-      x = (lower == up) ? min(x, y) : max(x, y);
+    }
+    for (; j >= 64; j >>= 1) {
+      unsigned *bb = pb ? tmp : keys;
+      pb ^= 1;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = tid + e * kSchedThreads;
+        if (i < n2) bb[i] = x[e];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = tid + e * kSchedThreads;
+        const unsigned y = i < n2 ? bb[i ^ j] : 0xffffffffu;
+        const bool up = (i & k) == 0, lower = (i & j) == 0;
+        x[e] = (lower == up) ? min(x[e], y) : max(x[e], y);
+      }
+    }
+    switch (j) {
+      case 32: wave_stage<32>(x, k, fwd4); [[fallthrough]];
+      case 16: wave_stage<16>(x, k, fwd4); [[fallthrough]];
+      case 8: wave_stage<8>(x, k, fwd4); [[fallthrough]];
+      case 4: wave_stage<4>(x, k, fwd4); [[fallthrough]];
+      case 2: wave_stage<2>(x, k, fwd4); [[fallthrough]];
+      case 1: wave_stage<1>(x, k, fwd4); break;
+      default: break;
     }
   }
   __syncthreads();
-  if (tid < n2) keys[tid] = x;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid + e * kSchedThreads;
+    if (i < n2) keys[i] = x[e];
+  }
   __syncthreads();
 }
 
@@ -186,6 +267,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
   constexpr int kRecCache = kSchedThreads;  // records kept in LDS for short lists
   __shared__ int s_qoff[kMaxSeqs + 1];
   __shared__ unsigned s_keys[kSortCap];
+  __shared__ unsigned s_tmp[kSortCap];
   __shared__ QTile s_rec[kRecCache];
   __shared__ int s_wsum[kSchedThreads / 64];
   __shared__ int s_bits, s_first;
@@ -272,26 +354,11 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
   }
   if (!sorted) return;
 
-  if (n2 <= kSchedThreads) {
-    sort_small(s_keys, n2);
-  } else {
-    for (int k = 2; k <= n2; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < n2; i += kSchedThreads) {
-          int ixj = i ^ j;
-          if (ixj > i) {
-            unsigned x = s_keys[i], y = s_keys[ixj];
-            bool up = (i & k) == 0;
-            if ((x > y) == up) {
-              s_keys[i] = y;
-              s_keys[ixj] = x;
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
-  }
+  static_assert(kSortCap <= 8 * kSchedThreads, "at most 8 keys per thread");
+  if (n2 <= kSchedThreads) sort_keys<1>(s_keys, s_tmp, n2);
+  else if (n2 <= 2 * kSchedThreads) sort_keys<2>(s_keys, s_tmp, n2);
+  else if (n2 <= 4 * kSchedThreads) sort_keys<4>(s_keys, s_tmp, n2);
+  else sort_keys<8>(s_keys, s_tmp, n2);
 
   for (int r = tid; r < NQ; r += kSchedThreads) {
     int g = (int)(s_keys[r] & 0x3ffffu);

@@ -111,9 +111,23 @@ def _got_tiles(tiles):
     return [(int(t[0]), int(t[1]), int(t[2]), int(t[3]) & 0xFFFF, int(t[3]) >> 16) for t in tiles]
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "causal_rab_bf16", "mtgr_small", "train", "mtgr", "long"])
+def _many_tiles(n_seqs, seed):
+    """Many short sequences: the longest-first order of a few thousand query
+    tiles (several sort keys per thread in the scheduler's sort)."""
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(1, 400, size=n_seqs)
+    return synth.custom(f"many_tiles_{n_seqs}", lengths, H=1, d=32, wid=seed, std=0.3, n_max=400)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "causal_rab_bf16", "mtgr_small", "train", "mtgr", "long",
+                                  "many_tiles_900", "many_tiles_1500", "many_tiles_3500"])
 def test_schedule_bit_exact(name):
-    p = synth.WORKLOADS[name]() if name in synth.WORKLOADS else {q.name: q for q in _small_problems()}[name]
+    if name.startswith("many_tiles_"):
+        n = int(name.rsplit("_", 1)[1])
+        p = _many_tiles(n, 170 + n % 97)
+    else:
+        p = synth.WORKLOADS[name]() if name in synth.WORKLOADS else {q.name: q for q in _small_problems()}[name]
+    print("schedule", name, "B", p.B, flush=True)
     ns = device.upload(p)
     BM, BN = api.tile_shape(ns.problem)
     qoff, tiles = api.schedule_export(ns.problem)
