@@ -221,3 +221,14 @@ def test_stack_entry_points_reject_bad_arguments(L):
     assert lib.hstu_graph_launch(None, None) == L.HSTU_ERR_INVALID_ARG
     assert lib.hstu_graph_destroy(None) == L.HSTU_ERR_INVALID_ARG
     del g
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with a message before
+    touching a device or importing the library."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], cwd=ROOT,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
