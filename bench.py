@@ -72,6 +72,27 @@ def visible_pairs(lengths, prefix=None, cand=None):
     return tot
 
 
+def algorithmic_bytes(wl, src, kind):
+    """HBM bytes each kernel must move at least once per launch: every
+    operand read once and every result written once (timestamps 8 B and
+    norm statistics 2 x 4 B per token)."""
+    import numpy as np
+    e = 4 if str(src.dtype).endswith("float32") else 2
+    D = src.H * src.d
+    if wl == "mfalcon":
+        Tc, Th = int(src.cand_offsets[-1]), int(src.hist_offsets[-1])
+        ts = 8 * (Tc + Th) if getattr(src, "cand_ts", None) is not None else 0
+        return {"attn_fwd": 3 * Tc * D * e + 2 * Th * D * e + ts + Tc * D * e,
+                "norm_fwd": 3 * Tc * D * e + 8 * Tc}
+    T = int(src.T)
+    ts = 8 * T if src.ts is not None else 0
+    out = {"attn_fwd": 4 * T * D * e + ts, "norm_fwd": 3 * T * D * e + 8 * T}
+    if kind == "fwdbwd":
+        out.update({"norm_bwd": 5 * T * D * e + 8 * T, "attn_bwd_dq": 5 * T * D * e + ts,
+                    "attn_bwd_dkdv": 6 * T * D * e + ts})
+    return out
+
+
 # Sources each timed kernel is built from (a traffic figure is valid only
 # while these are unchanged).
 KERNEL_SOURCES = {
@@ -151,25 +172,69 @@ def cpu_baseline(p, flops_per_pair, kind, budget_s):
                 oracle_bwd(sub)
             return time.perf_counter() - t0
 
-    def take(target):
-        n, acc = 0, 0
-        while n < len(order) and (acc < target or n == 0):
-            acc += unit_pairs[n]
-            n += 1
-        return n, acc
-
-    n0, pairs0 = take(min(sum(unit_pairs), 2e7))
-    t0 = run(order[:n0])
-    rate = pairs0 / max(t0, 1e-6)
-    n1, pairs1 = take(rate * budget_s)
+    # Calibrate the oracle's rate on the smallest unit, then take units in the
+    # seeded order, skipping any that would overrun the budget (the smallest if none fits).
+    small = min(range(len(order)), key=lambda i: (unit_pairs[i], i))
+    t0 = run([order[small]])
+    rate = unit_pairs[small] / max(t0, 1e-6)
+    chosen, pairs1 = [], 0
+    for i in range(len(order)):
+        if pairs1 + unit_pairs[i] <= rate * budget_s:
+            chosen.append(i)
+            pairs1 += unit_pairs[i]
+    if not chosen:
+        chosen, pairs1 = [small], unit_pairs[small]
+    n1 = len(chosen)
     # A batch smaller than the budget is run several times over.
     reps = max(1, min(20, int(budget_s * rate / pairs1))) if n1 == len(order) else 1
-    t1 = sum(run(order[:n1]) for _ in range(reps))
+    t1 = sum(run([order[i] for i in chosen]) for _ in range(reps))
     value = flops_per_pair * pairs1 * reps / t1 / 1e12
-    what = f"first {n1} of {len(order)} {label}" if n1 < len(order) else f"all {n1} {label}, {reps} run(s)"
-    return {"value": value, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{what} in a seeded order ({pairs1} visible pairs x heads per run); "
+    what = (f"{n1} of {len(order)} {label} (those that fit the budget, in a seeded order)" if n1 < len(order)
+            else f"all {n1} {label}, {reps} run(s), in a seeded order")
+    return {"value": value, "unit": "TFLOP/s", "cores": cores, "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"{what} ({pairs1} visible pairs x heads per run); "
                       f"{t1:.1f} s of fp64 oracle time with OpenMP on {cores} threads"}
+
+
+EVICT_MIB = 512
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def timed_steps(step, steps, evict=True):
+    """Times `steps` calls of step() on the current stream, each between its
+    own pair of HIP events. With evict, a 512 MiB buffer is written before
+    every step (outside its events), which pushes the inputs out of L2 and
+    the MALL (256 MiB), so each step starts from HBM. Returns the per-step
+    milliseconds."""
+    import torch
+    stream = torch.cuda.current_stream()
+    buf = torch.empty(EVICT_MIB << 20, dtype=torch.uint8, device="cuda") if evict else None
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        if buf is not None:
+            buf.fill_(i & 0xFF)
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
 
 
 def bench_batchprep(args):
@@ -204,12 +269,7 @@ def bench_batchprep(args):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = median(timed_steps(step, args.steps, evict=not args.no_evict))
     api.kernel_timing(True)
     for _ in range(args.steps):
         step()
@@ -279,7 +339,7 @@ def cpu_baseline_layer(lp, budget_s):
     rate = w0 / max(run(order[:n0]), 1e-6)
     n1, w1 = take(rate * budget_s)
     t1 = run(order[:n1])
-    return {"value": w1 / t1 / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": w1 / t1 / 1e12, "unit": "TFLOP/s", "cores": cores, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"first {n1} of {len(order)} sequences in a seeded order (layer forward + backward, "
                       f"{w1 / 1e12:.3f} useful TFLOP); {t1:.1f} s of fp64 oracle time with OpenMP on {cores} threads"}
 
@@ -320,12 +380,7 @@ def bench_layer(args):
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {args.steps} steps")
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = median(timed_steps(step, args.steps, evict=not args.no_evict))
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {ms:.4f} ms/step, {value:.2f} useful TFLOP/s")
     api.kernel_timing(True)
@@ -417,12 +472,7 @@ def bench_stack(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = median(timed_steps(step, args.steps, evict=not args.no_evict))
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {ms:.4f} ms/step, {value:.2f} useful TFLOP/s, {Tc / (ms * 1e-3):.3e} candidates/s")
     api.kernel_timing(True)
@@ -525,7 +575,8 @@ def cpu_baseline_stack(sp, budget_s, flops_per_user):
     t1 = run(1)
     n = max(1, min(sp.B, int(budget_s / max(t1, 1e-3))))
     t = run(n) if n > 1 else t1
-    return {"value": n * flops_per_user / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": n * flops_per_user / t / 1e12, "unit": "TFLOP/s", "cores": cores, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"first {n} of {sp.B} users (full pass over history + candidates, all layers); "
                       f"{t:.1f} s of fp64 oracle time with OpenMP on {cores} threads"}
 
@@ -535,7 +586,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="train", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="long", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-evict", action="store_true",
+                    help="do not write the 512 MiB eviction buffer between timed steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -613,24 +666,12 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    value = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] {ms:.4f} ms/step, {value:.2f} useful TFLOP/s")
-
-    # Dominant kernel: timed per launch with HIP events on its launch stream.
+    # Timed region: each step between its own HIP events, L2/MALL evicted
+    # before each step; library kernels timed per launch on their stream.
+    log(f"[bench] timing {args.steps} steps ({'no eviction' if args.no_evict else f'{EVICT_MIB} MiB eviction write'}"
+        " between steps)")
     api.kernel_timing(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
+    step_ms = timed_steps(step, args.steps, evict=not args.no_evict)
     per = {}
     for kid, kname in ((_lib.HSTU_KERNEL_SCHED, "sched"), (_lib.HSTU_KERNEL_ATTN_FWD, "attn_fwd"),
                        (_lib.HSTU_KERNEL_NORM_FWD, "norm_fwd"), (_lib.HSTU_KERNEL_NORM_BWD, "norm_bwd"),
@@ -640,7 +681,15 @@ def main():
         if n:
             per[kname] = tms / n
     api.kernel_timing(False)
+    ms = median(step_ms)
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] median {ms:.4f} ms/step (min {min(step_ms):.4f}, max {max(step_ms):.4f}), "
+        f"{value:.2f} useful TFLOP/s")
     log("[bench] per-launch ms: " + ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
+    # Secondary: warm caches, steps back to back (mean over one event pair).
+    warm = timed_steps(lambda: [step() for _ in range(args.steps)], 1, evict=False)[0] / args.steps
+    log(f"[bench] warm-cache back-to-back {warm:.4f} ms/step")
+
     # Dominant kernel: the longest one; each attention kernel carries 4*d
     # useful FLOPs per visible pair and head (forward: Q.K and A.V; backward
     # query pass: dA and dQ; key pass: dV and dK).
@@ -650,10 +699,16 @@ def main():
     dom_flops = 4.0 * src.d * pairs
     peak = PEAK_F32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms else None
+    # Algorithmic HBM bytes per launch (each operand read once, each result
+    # written once) and the rate they imply, per kernel.
+    algo = algorithmic_bytes(wl, src, kind)
+    hbm = {k: {"algorithmic_bytes": b, "GB_per_s": b / (per[k] * 1e-3) / 1e9,
+               "frac_of_8TBs": b / (per[k] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+           for k, b in algo.items() if k in per}
     roofline = {"bound": "mfma" if dtype == "bf16" else "alu", "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s", "frac": (achieved / peak) if achieved else None,
                 "traffic": traffic_from_profiles(wl, dom_name), "kernel": dom_name,
-                "kernel_ms": dom_ms, "per_kernel_ms": per}
+                "kernel_ms": dom_ms, "per_kernel_ms": per, "hbm_algorithmic": hbm}
 
     if args.copy_probe_mb > 0:
         n = args.copy_probe_mb << 20
@@ -677,7 +732,12 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded generators; no dataset)",
         "config": {"workload": WORKLOAD_TEXT[wl], "name": wl, "step": kind, **shape,
-                   "useful_tflop_per_step": flops / 1e12, "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS},
+                   "useful_tflop_per_step": flops / 1e12, "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+                   "timing": ("median of per-step HIP event pairs, " +
+                              ("no eviction" if args.no_evict else f"{EVICT_MIB} MiB written before each step")),
+                   "step_ms_min_max": [min(step_ms), max(step_ms)],
+                   "warm_back_to_back_ms_per_step": warm,
+                   "warm_back_to_back_tflops": flops / (warm * 1e-3) / 1e12},
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -164,6 +164,54 @@ def attn_bwd(p, Q, K, V, U, O, mean, rstd, dY, *, dQ=None, dK=None, dV=None, dU=
                            d_beta=d_beta, ws=ws)
 
 
+class HSTUAttnFn(torch.autograd.Function):
+    """hstu_attn_fwd / hstu_attn_bwd as one autograd node.
+
+    apply(p, Q, K, V, U, rab_p, rab_t, gamma, beta) -> Y [T, H*d]. `p` is the
+    problem built by problem(); rab_p, rab_t, gamma and beta must be the very
+    tensors `p` was built with (or None), so that their gradients land on
+    them. The forward keeps O, mean and rstd for the backward; the backward
+    calls hstu_attn_bwd once with the incoming dY (made contiguous) and hands
+    back dQ, dK, dV, dU and the table / affine gradients. Timestamps, offsets
+    and segment lengths take no gradient."""
+
+    @staticmethod
+    def forward(ctx, p, Q, K, V, U, rab_p=None, rab_t=None, gamma=None, beta=None):
+        for t, name, field in ((rab_p, "rab_p", p.rab_p), (rab_t, "rab_t", p.rab_t), (gamma, "gamma", p.gamma),
+                               (beta, "beta", p.beta)):
+            if (t.data_ptr() if t is not None else None) != field:
+                raise ValueError(f"{name} is not the tensor the problem was built with")
+        out = attn_fwd(p, Q, K, V, U)
+        ctx.p = p
+        ctx.save_for_backward(Q, K, V, U, out.O, out.mean, out.rstd)
+        ctx.want_affine = gamma is not None or beta is not None
+        ctx.affine_shapes = (None if gamma is None else gamma.shape, None if beta is None else beta.shape)
+        return out.Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        Q, K, V, U, O, mean, rstd = ctx.saved_tensors
+        g = attn_bwd(ctx.p, Q, K, V, U, O, mean, rstd, dY.contiguous(), want_affine=ctx.want_affine)
+        gs, bs = ctx.affine_shapes
+        return (None, g.dQ, g.dK, g.dV, g.dU, g.d_rab_p, g.d_rab_t,
+                g.d_gamma.view(gs) if g.d_gamma is not None else None,
+                g.d_beta.view(bs) if g.d_beta is not None else None)
+
+
+def hstu_attention(offsets, Q, K, V, U, *, max_len, n_max, prefix_len=None, cand_len=None, timestamps=None,
+                   rab_p=None, rab_t=None, norm=HSTU_NORM_LN, eps=1e-5, token_group=None, n_groups=1, gamma=None,
+                   beta=None, time_filter=False):
+    """Y = Norm(A V) * U of a jagged batch through HSTUAttnFn (differentiable
+    in Q, K, V, U, rab_p, rab_t, gamma, beta). Q/K/V/U: [T, H, d] device
+    tensors of one dtype; the other arguments as for problem()."""
+    T, H, d = Q.shape
+    p = problem(offsets, H=H, d=d, dtype=Q.dtype, total_tokens=T, max_len=max_len, n_max=n_max,
+                prefix_len=prefix_len, cand_len=cand_len, timestamps=timestamps, rab_p=rab_p, rab_t=rab_t,
+                norm=norm, eps=eps, token_group=token_group, n_groups=n_groups, gamma=gamma, beta=beta,
+                time_filter=time_filter)
+    return HSTUAttnFn.apply(p, Q, K, V, U, rab_p, rab_t, gamma, beta)
+
+
 def mfalcon_score(cand_p, hist_offsets, hist_tokens, hist_max_len, K_cache, V_cache, Qc, Kc, Vc, Uc, *,
                   hist_ts=None, microbatch=0, Yc=None, Oc=None, mean=None, rstd=None, ws=None, stream=None):
     """hstu_mfalcon_score. cand_p describes the candidates (offsets over Tc

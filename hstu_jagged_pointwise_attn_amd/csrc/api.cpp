@@ -624,6 +624,7 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
   b.H = p->H;
   b.d = p->d;
   b.hdr = qa.hdr;
+  b.status = qa.hdr + kHdrStatus;
   b.desc = qa.desc;
   b.tiles = qa.tiles;
   long long units = L.max_tiles * p->H;

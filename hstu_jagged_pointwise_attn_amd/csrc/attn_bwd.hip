@@ -550,7 +550,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       *(u32x4 *)(dQ + (long long)(sd.q_base + row0 + row) * ld + h * D + col) =
           *(const u32x4 *)(os + row * ST + col);
   }
-  if (USE_T && tid == 0 && s_bad) atomicOr(&a.hdr[kHdrStatus], HSTU_DEV_BAD_TIMESTAMPS);
+  if (USE_T && tid == 0 && s_bad) atomicOr(a.status, HSTU_DEV_BAD_TIMESTAMPS);
 }
 
 // ---------------------------------------------------------------------------
@@ -602,8 +602,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int kmax_valid = k0 + nkeys - 1;
   const int rmin_tile = kmax_valid < sd.P ? 0 : kmax_valid;      // rows >= it see every key
   const long long t_ref = USE_T ? a.ts[sd.kv_base + k0] : 0;
+  __shared__ int s_bad;
+  if (tid == 0) s_bad = 0;
+  // Times are kept as u = t - t_ref + 2^31; a row or key 2^31 s or more
+  // away from t_ref would wrap, so it raises the status bit.
+  bool bad_t = false;
   unsigned tk = 0u;
-  if (USE_T) tk = (unsigned)(a.ts[sd.kv_base + key] - t_ref + 2147483648LL);
+  if (USE_T) {
+    const long long dk = a.ts[sd.kv_base + key] - t_ref;
+    bad_t = dk < -2147483648LL || dk > 2147483647LL;
+    tk = (unsigned)(dk + 2147483648LL);
+  }
   unsigned kmin = 0, kmax = 0;
   if (USE_T) {
     kmin = __builtin_amdgcn_readfirstlane(wave_min_u32(tk));
@@ -655,7 +664,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     }
     if (USE_P && tid < WIN) rabw[buf * WIN + tid] = pf.r;
     if (USE_T && tid < BM) {
-      const unsigned u = (unsigned)(pf.t - t_ref + 2147483648LL);
+      const long long dr = pf.t - t_ref;
+      bad_t |= dr < -2147483648LL || dr > 2147483647LL;
+      const unsigned u = (unsigned)(dr + 2147483648LL);
       trow[buf * BM + tid] = u;
       const unsigned mn = wave_min_u32(u), mx = wave_max_u32(u);
       if (tid == 0) {
@@ -789,6 +800,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     __syncthreads();
   }
 
+  if (USE_T && bad_t) atomicOr(&s_bad, 1);
   // Stage dK and dV (C layout: key 4 lg + i, column 16 nd + lr) through LDS;
   // dV summed -log2(e) SiLU(.) dO, which -ln(2) / N_max restores.
   const float vscale = a.inv_nmax * -kLn2;
@@ -812,6 +824,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       *(u32x4 *)(dV + g) = *(const u32x4 *)(sv + row * ST + col);
     }
   }
+  if (USE_T && tid == 0 && s_bad) atomicOr(a.status, HSTU_DEV_BAD_TIMESTAMPS);
 }
 
 // ---------------------------------------------------------------------------

@@ -143,6 +143,7 @@ struct BwdArgs {
   int H, d;
   int tfilt;                       // candidates see causal-segment keys only if strictly earlier
   int *hdr;                        // header of the schedule this kernel runs
+  int *status;                     // the call's status word (HSTU_DEV_* bits)
   const SeqDesc *desc;
   const QTile *tiles;
   int units;                       // grid bound: records * H

@@ -84,8 +84,11 @@ enum {
   HSTU_DEV_BAD_SEGMENTS = 2,  /* prefix_len/cand_len negative or P + C > L */
   HSTU_DEV_BAD_GROUP = 4,     /* a token group id >= n_groups (that token uses gamma = 1, beta = 0) */
   HSTU_DEV_TOO_LONG = 8,      /* a sequence longer than max_len */
-  HSTU_DEV_BAD_TIMESTAMPS = 16 /* timestamps of one sequence span 2^31 s or more (rab_t terms of
-                                  that sequence are then undefined) */
+  HSTU_DEV_BAD_TIMESTAMPS = 16 /* a kernel met a timestamp 2^31 s or more away from the reference
+                                  time of its tile (the tile's first row or key); this cannot
+                                  happen when every sequence spans less than 2^31 s. A sequence
+                                  with a larger span may or may not raise it; its rab_t terms and
+                                  timestamp-filter decisions are then undefined */
 };
 
 /*
@@ -229,7 +232,7 @@ hstu_status_t hstu_tile_shape(const hstu_problem_t *p, int32_t op, int32_t *BM, 
  *                   PARTIAL, rows [row0, row0 + nrows) are local query rows
  *                   of sequence b (candidate indices for M-FALCON).
  *                   Execution order is longest first (nk descending, ties in
- *                   canonical order) when there are at most 16384 query
+ *                   canonical order) when there are at most 8192 query
  *                   tiles, canonical otherwise.
  *   count           (host) number of query tiles (records beyond cap are not
  *                   copied)

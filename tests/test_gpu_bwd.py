@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from hstu_jagged_pointwise_attn_amd import api, device, synth
-from tests.common import oracle_bwd, rel_l2, tol
+from tests.common import oracle_bwd, oracle_fwd, rel_l2, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -55,20 +55,34 @@ def _run(p, ns=None):
 
 def mass_rel(got, ref, mass):
     """||got - ref|| / ||mass||: the error of a sum of many cancelling terms
-    measured against the sum of their magnitudes (mass >= |ref| entrywise,
-    so this never exceeds the plain relative error)."""
+    measured against the sum of their magnitudes (a diagnostic printed next
+    to the plain relative error)."""
     got = np.asarray(got, np.float64).reshape(-1)
     den = np.linalg.norm(np.asarray(mass, np.float64).reshape(-1))
     return np.linalg.norm(got - np.asarray(ref).reshape(-1)) / den if den else np.linalg.norm(got - ref)
 
 
+def kappa(ref, mass):
+    """Cancellation factor ||sum |dS| per entry|| / ||d rab||: how much larger
+    the magnitudes summed into a rab gradient are than the gradient itself."""
+    r = np.linalg.norm(np.asarray(ref, np.float64))
+    return np.linalg.norm(np.asarray(mass, np.float64)) / r if r else np.inf
+
+
+# (problem, gradient) pairs whose plain relative error cannot reach the bf16
+# bound with bf16 operands: the gradient is a sum over ~60k pairs that cancels
+# by a factor above 1000, so the 2^-9 relative rounding of dO (the dP
+# product's bf16 operand) and of the forward's attention weights (the A.V
+# product's bf16 operand) each exceed 1e-2 of it on their own (a CPU
+# emulation of those two roundings alone gives 1.0e-2 and 5.8e-3). For these
+# the test asserts the mass-relative error at the bf16 bound and that the
+# cancellation factor really is above 1000; the plain error is printed.
+ILL_CONDITIONED = {("bf16_mtgr_gln", "drab_t"): 1000.0}
+
+
 def _compare(p, g, ref, rows=None, what=("dQ", "dK", "dV", "dU"), extra=True):
-    """Relative L2 error per gradient. The rab gradients are sums of dS over
-    up to all L^2 visible pairs of the batch; the bf16 forward perturbs each
-    term by about 2^-9 relative (the saved O carries the rounding of the bf16
-    attention weights, and LayerNorm's backward passes it on to dO), so for
-    them the attainable bound is relative to the mass sum |dS| per entry,
-    reported as "<name>~"; their plain relative error is reported too."""
+    """Plain relative L2 error per gradient (the rab gradients also print
+    their mass-relative error, "<name>~", and cancellation factor)."""
     T, D = p.T, p.H * p.d
     errs = {}
     for name in what:
@@ -84,9 +98,24 @@ def _compare(p, g, ref, rows=None, what=("dQ", "dK", "dV", "dU"), extra=True):
         for name, gname in (("drab_p", "d_rab_p"), ("drab_t", "d_rab_t")):
             if ref[name] is not None and getattr(g, gname) is not None:
                 got = getattr(g, gname).cpu().numpy()
-                errs[name + "~"] = mass_rel(got, ref[name], ref[name + "_abs"])
-                errs["(plain) " + name] = rel_l2(got, ref[name])
+                errs[name] = rel_l2(got, ref[name])
+                errs["(diag) " + name + "~"] = mass_rel(got, ref[name], ref[name + "_abs"])
+                errs["(diag) " + name + " kappa"] = kappa(ref[name], ref[name + "_abs"])
     return errs
+
+
+def check_errs(p, errs):
+    """Every gradient within the dtype's bound in plain relative L2, except
+    the listed ill-conditioned rab gradients (see ILL_CONDITIONED)."""
+    for k, v in errs.items():
+        if k.startswith("(diag)"):
+            continue
+        bound = ILL_CONDITIONED.get((p.name, k))
+        if bound is not None:
+            assert errs["(diag) " + k + " kappa"] >= bound, (k, errs["(diag) " + k + " kappa"])
+            assert errs["(diag) " + k + "~"] <= tol(p), (k, errs["(diag) " + k + "~"])
+            continue
+        assert v <= tol(p), (k, v)
 
 
 @pytest.mark.parametrize("p", _problems(), ids=lambda p: p.name)
@@ -97,9 +126,7 @@ def test_bwd_matches_oracle_small(p):
     ref = oracle_bwd(p)
     errs = _compare(p, g, ref)
     _say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
-    for k, v in errs.items():
-        if not k.startswith("(plain)"):
-            assert v <= tol(p), (k, v)
+    check_errs(p, errs)
 
 
 def _subsample_seqs(p):
@@ -154,3 +181,36 @@ def test_bwd_gradient_identity_on_gpu():
             a1 = (Q[s:e, h] * dQ[s:e, h]).sum()
             a2 = (K[s:e, h] * dK[s:e, h]).sum()
             assert a1 == pytest.approx(a2, rel=1e-4, abs=1e-9)
+
+
+def test_autograd_function_matches_oracle():
+    """api.hstu_attention (HSTUAttnFn: hstu_attn_fwd in the forward,
+    hstu_attn_bwd in the backward) under torch.autograd: Y and the gradients
+    of Q, K, V, U, both rab tables and the Group LayerNorm affine against the
+    oracle."""
+    L = np.array([150, 40, 133, 7])
+    P = np.array([100, 0, 60, 3]); C = np.array([30, 40, 33, 2])
+    grp = np.concatenate([np.minimum(np.arange(l) * 3 // l, 2) for l in L])
+    for dtype in (torch.float32, torch.bfloat16):
+        p = synth.custom(f"autograd_{dtype}", L, H=2, d=64, dtype=dtype, wid=58, std=0.4, n_max=16,
+                         norm=synth.NORM_GLN, prefix_len=P, cand_len=C, group=grp, n_groups=3, gamma_std=0.3,
+                         beta_std=0.3, n_pos=200, n_tb=24, rab_std=0.3, with_dy=True)
+        ns = device.upload(p)
+        leaves = {k: getattr(ns, k).clone().requires_grad_(True) for k in ("Q", "K", "V", "U")}
+        tabs = {k: getattr(ns, k).clone().requires_grad_(True) for k in ("rab_p", "rab_t", "gamma", "beta")}
+        Y = api.hstu_attention(ns.offsets, leaves["Q"], leaves["K"], leaves["V"], leaves["U"], max_len=p.max_len,
+                               n_max=p.n_max, prefix_len=ns.prefix_len, cand_len=ns.cand_len, timestamps=ns.ts,
+                               norm=p.norm, eps=p.eps, token_group=ns.group, n_groups=p.n_groups, **tabs)
+        Y.backward(ns.dY)
+        torch.cuda.synchronize()
+        ref = oracle_bwd(p)
+        fref = oracle_fwd(p)
+        T, D = p.T, p.H * p.d
+        errs = {"Y": rel_l2(Y.detach(), fref["Y"])}
+        for name in ("Q", "K", "V", "U"):
+            errs["d" + name] = rel_l2(leaves[name].grad.float().cpu().numpy().reshape(T, D), ref["d" + name])
+        for name, rname in (("rab_p", "drab_p"), ("rab_t", "drab_t"), ("gamma", "dgamma"), ("beta", "dbeta")):
+            errs[rname] = rel_l2(tabs[name].grad.cpu().numpy(), ref[rname])
+        _say(f"autograd {dtype}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        for k, v in errs.items():
+            assert v <= tol(p), (k, v)

@@ -111,18 +111,23 @@ def _got_tiles(tiles):
     return [(int(t[0]), int(t[1]), int(t[2]), int(t[3]) & 0xFFFF, int(t[3]) >> 16) for t in tiles]
 
 
-def _many_tiles(n_seqs, seed):
+def _many_tiles(n_seqs, seed, lo=1, hi=400):
     """Many short sequences: the longest-first order of a few thousand query
-    tiles (several sort keys per thread in the scheduler's sort)."""
+    tiles (several sort keys per thread in the scheduler's sort); with
+    lengths of 129..500 and 4000 sequences, more query tiles (about 11.6k)
+    than the scheduler sorts, so it keeps the canonical order."""
     rng = np.random.default_rng(seed)
-    lengths = rng.integers(1, 400, size=n_seqs)
-    return synth.custom(f"many_tiles_{n_seqs}", lengths, H=1, d=32, wid=seed, std=0.3, n_max=400)
+    lengths = rng.integers(lo, hi, size=n_seqs)
+    return synth.custom(f"many_tiles_{n_seqs}", lengths, H=1, d=32, wid=seed, std=0.3, n_max=hi)
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "causal_rab_bf16", "mtgr_small", "train", "mtgr", "long",
-                                  "many_tiles_900", "many_tiles_1500", "many_tiles_3500"])
+                                  "many_tiles_900", "many_tiles_1500", "many_tiles_3500", "over_sort_cap_4000"])
 def test_schedule_bit_exact(name):
-    if name.startswith("many_tiles_"):
+    if name.startswith("over_sort_cap_"):
+        n = int(name.rsplit("_", 1)[1])
+        p = _many_tiles(n, 171, lo=129, hi=501)
+    elif name.startswith("many_tiles_"):
         n = int(name.rsplit("_", 1)[1])
         p = _many_tiles(n, 170 + n % 97)
     else:
@@ -132,15 +137,18 @@ def test_schedule_bit_exact(name):
     BM, BN = api.tile_shape(ns.problem)
     qoff, tiles = api.schedule_export(ns.problem)
     entries = oracle.schedule(p.offsets, BM, BN, prefix_len=p.prefix_len, cand_len=p.cand_len)
+    if name.startswith("over_sort_cap_"):
+        assert len(entries) > 8192, len(entries)
     counts = np.bincount([e["b"] for e in entries], minlength=p.B)
     np.testing.assert_array_equal(qoff, np.concatenate([[0], np.cumsum(counts)]))
     assert _got_tiles(tiles) == _expected_tiles(entries)
 
 
-@pytest.mark.parametrize("microbatch", [0, 256, 100, 1])
-def test_schedule_mfalcon_bit_exact(microbatch):
-    mf = synth.mfalcon_bf16(users=3, n_hist=300, m_cand=200 if microbatch != 1 else 20, microbatch=microbatch,
-                            H=2, d=64)
+@pytest.mark.parametrize("microbatch,m_cand", [(0, 200), (256, 200), (100, 200), (1, 20), (1, 3000)])
+def test_schedule_mfalcon_bit_exact(microbatch, m_cand):
+    """(1, 3000): one candidate per microbatch, 9000 query tiles, more than
+    the scheduler sorts."""
+    mf = synth.mfalcon_bf16(users=3, n_hist=300, m_cand=m_cand, microbatch=microbatch, H=2, d=64)
     ns = device.upload_mfalcon(mf)
     BM, BN = api.tile_shape(ns.problem, api.HSTU_OP_MFALCON)
     qoff, tiles = api.schedule_export(ns.problem, api.HSTU_OP_MFALCON, ns.hist_offsets, ns.hist_tokens,

@@ -9,6 +9,7 @@ import torch
 import oracle
 from hstu_jagged_pointwise_attn_amd import api, device, synth
 from tests.common import oracle_bwd, oracle_fwd, oracle_mfalcon, rel_l2, tol
+from tests.test_gpu_bwd import _compare, check_errs
 
 pytestmark = pytest.mark.gpu
 
@@ -136,12 +137,6 @@ def test_filter_mfalcon_matches_oracle():
     assert eo <= 1e-2 and ey <= 1e-2
 
 
-def _mass_rel(got, ref, mass):
-    got = np.asarray(got, np.float64).reshape(-1)
-    den = np.linalg.norm(np.asarray(mass, np.float64).reshape(-1))
-    return np.linalg.norm(got - np.asarray(ref).reshape(-1)) / den if den else np.linalg.norm(got - ref)
-
-
 @pytest.mark.parametrize("p", _problems(), ids=lambda p: p.name)
 def test_filter_bwd_matches_oracle(p):
     _say("filter bwd", p.name)
@@ -151,14 +146,6 @@ def test_filter_bwd_matches_oracle(p):
     torch.cuda.synchronize()
     assert api.device_status(g.ws) == 0
     ref = oracle_bwd(p)
-    T, D = p.T, p.H * p.d
-    errs = {}
-    for name in ("dQ", "dK", "dV", "dU"):
-        errs[name] = rel_l2(getattr(g, name).float().cpu().numpy().reshape(T, D), ref[name])
-    # rab gradients against the mass of the sums they come from (see test_gpu_bwd)
-    for name, gname in (("drab_p", "d_rab_p"), ("drab_t", "d_rab_t")):
-        if ref[name] is not None and getattr(g, gname) is not None:
-            errs[name + "~"] = _mass_rel(getattr(g, gname).cpu().numpy(), ref[name], ref[name + "_abs"])
+    errs = _compare(p, g, ref)
     _say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
-    for k, v in errs.items():
-        assert v <= tol(p), (k, v)
+    check_errs(p, errs)
