@@ -106,6 +106,8 @@ struct Layout {
   // table: per-workgroup partials of d gamma / d beta (npart_blocks rows)
   size_t npart;
   long long npart_blocks;
+  // fp32 backward: fp64 accumulators of d rab_p and d rab_t (n_pos + n_tb)
+  size_t rab64;
   int norm_tpw;
 };
 
@@ -151,6 +153,9 @@ Layout layout(const hstu_problem_t *p, int op, int microbatch, int hist_max_len)
       L.norm_tpw = norm_affine_tpw(p->total_tokens);
       L.npart_blocks = norm_bwd_blocks(p->total_tokens, L.norm_tpw);
       L.npart = off;  off += align256(sizeof(float) * 2 * (size_t)(G * p->H * p->d) * (size_t)L.npart_blocks);
+    }
+    if (p->dtype == HSTU_F32) {
+      L.rab64 = off;  off += align256(sizeof(double) * (size_t)(std::max(p->n_pos, 0) + std::max(p->n_tb, 0) + 1));
     }
   }
   L.total = off;
@@ -438,6 +443,10 @@ hstu_status_t weight_grad(const void *A, long long M, const void *B, long long N
 
 }  // namespace
 
+namespace hstu {
+hstu_status_t set_last_error(hstu_status_t st, const char *msg) { return fail(st, "%s", msg); }
+}  // namespace hstu
+
 extern "C" {
 
 const char *hstu_version(void) { return "0.1.0"; }
@@ -577,10 +586,14 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
   // d gamma / d beta: per-workgroup LDS partials and a reduction when the
   // tables are small (and there are tokens), else global atomics.
   const bool aff_lds = (dg || db) && L.npart_blocks > 0;
+  // fp32: d rab is summed in fp64 in the workspace and rounded once at the end
+  double *rab64 = bf16 ? nullptr : at<double>(ws, L.rab64);
   {
     Timed t_(HSTU_KERNEL_AUX, st);
     if (p->rab_p) HIP_TRY(launch_fill_f32(d_rab_p, p->n_pos, 0.f, st), "fill");
     if (p->rab_t && d_rab_t) HIP_TRY(launch_fill_f32(d_rab_t, p->n_tb, 0.f, st), "fill");
+    if (rab64 && (p->rab_p || (p->rab_t && d_rab_t)))
+      HIP_TRY(launch_fill_f32((float *)rab64, 2ll * (p->n_pos + p->n_tb), 0.f, st), "fill");
     if (dg && !aff_lds) HIP_TRY(launch_fill_f32(dg, (long long)G * D, 0.f, st), "fill");
     if (db && !aff_lds) HIP_TRY(launch_fill_f32(db, (long long)G * D, 0.f, st), "fill");
   }
@@ -618,6 +631,8 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
   b.tfilt = (tf && use_t) ? 1 : 0;
   b.drab_p = d_rab_p;
   b.drab_t = d_rab_t;
+  b.drab_p64 = rab64;
+  b.drab_t64 = rab64 ? rab64 + p->n_pos : nullptr;
   b.n_pos = p->n_pos;
   b.n_tb = p->n_tb;
   b.inv_nmax = 1.0f / (float)p->n_max;
@@ -634,6 +649,12 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
   {
     Timed t_(HSTU_KERNEL_ATTN_BWD_DQ, st);
     HIP_TRY(bf16 ? launch_attn_bwd_dq_bf16(b, st) : launch_attn_bwd_dq_f32(b, st), "dq launch");
+  }
+  if (rab64 && (p->rab_p || b.rab_t)) {
+    Timed t_(HSTU_KERNEL_AUX, st);
+    HIP_TRY(launch_rab64_finalize(p->rab_p ? rab64 : nullptr, p->n_pos, b.rab_t ? rab64 + p->n_pos : nullptr, p->n_tb,
+                                  b.inv_nmax, d_rab_p, d_rab_t, st),
+            "d rab finalize launch");
   }
   b.hdr = ka.hdr;
   b.desc = ka.desc;

@@ -902,8 +902,8 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < DP; ++c) dq[c] = fmaf(ds, Ks[jl][part * DP + c], dq[c]);
         if (part == 0) {
-          if (use_p) atomicAdd(a.drab_p + pidx, ds * a.inv_nmax);
-          if (use_t && has_rt) atomicAdd(a.drab_t + tidx, ds * a.inv_nmax);
+          if (use_p) atomicAdd(a.drab_p64 + pidx, (double)ds);
+          if (use_t && has_rt) atomicAdd(a.drab_t64 + tidx, (double)ds);
         }
       }
     }
@@ -931,8 +931,8 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a) {
       dV[srow + c] = s * sg * g[c] * a.inv_nmax;
     }
     if (part == 0) {
-      if (use_p) atomicAdd(a.drab_p, ds * a.inv_nmax);
-      if (use_t && has_rt) atomicAdd(a.drab_t, ds * a.inv_nmax);
+      if (use_p) atomicAdd(a.drab_p64, (double)ds);
+      if (use_t && has_rt) atomicAdd(a.drab_t64, (double)ds);
     }
   }
   if (ok) {
@@ -940,6 +940,13 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < DP; ++c) dQ[roff + c] = dq[c] * a.inv_nmax;
   }
+}
+
+__global__ __launch_bounds__(256) void rab64_finalize_kernel(const double *acc_p, int n_pos, const double *acc_t,
+                                                             int n_tb, float inv_nmax, float *drab_p, float *drab_t) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (acc_p && i < n_pos) drab_p[i] = (float)(acc_p[i] * (double)inv_nmax);
+  if (acc_t && i < n_tb) drab_t[i] = (float)(acc_t[i] * (double)inv_nmax);
 }
 
 template <int D>
@@ -1076,6 +1083,15 @@ hipError_t launch_attn_bwd_dq_f32(const BwdArgs &a, hipStream_t s) {
     case 128: hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, dim3(a.units), dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_rab64_finalize(const double *acc_p, int n_pos, const double *acc_t, int n_tb, float inv_nmax,
+                                 float *drab_p, float *drab_t, hipStream_t s) {
+  const int n = max(acc_p ? n_pos : 0, acc_t ? n_tb : 0);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rab64_finalize_kernel, dim3((n + 255) / 256), dim3(256), 0, s, acc_p, n_pos, acc_t, n_tb,
+                     inv_nmax, drab_p, drab_t);
   return hipGetLastError();
 }
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/hstu.h"
+
 namespace hstu {
 
 // Per-sequence frame of the attention core. A "frame" is the sequence as the
@@ -138,6 +140,7 @@ struct BwdArgs {
   const int64_t *ts;               // timestamps (rab_t or the filter) or NULL
   const float *rab_p, *rab_t;      // tables or NULL
   float *drab_p, *drab_t;          // fp32 accumulators (zeroed by the caller)
+  double *drab_p64, *drab_t64;     // fp32 path: fp64 accumulators of the unscaled sums (zeroed by the caller)
   int n_pos, n_tb;
   float inv_nmax;
   int H, d;
@@ -155,8 +158,15 @@ hipError_t launch_attn_bwd_dq_bf16(const BwdArgs &a, hipStream_t s);
 hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs &a, hipStream_t s);
 hipError_t launch_attn_bwd_dq_f32(const BwdArgs &a, hipStream_t s);
 hipError_t launch_attn_bwd_dkdv_f32(const BwdArgs &a, hipStream_t s);
+// d rab_p[i] = acc_p[i] * inv_nmax and d rab_t[i] = acc_t[i] * inv_nmax,
+// rounded once from fp64 (either table may be NULL).
+hipError_t launch_rab64_finalize(const double *acc_p, int n_pos, const double *acc_t, int n_tb, float inv_nmax,
+                                 float *drab_p, float *drab_t, hipStream_t s);
 
 hipError_t launch_fill_f32(float *p, long long n, float v, hipStream_t s);
+
+// Records `msg` as this thread's hstu_last_error text and returns st.
+hstu_status_t set_last_error(hstu_status_t st, const char *msg);
 
 // Batch preparation (Stochastic Length, row gather, work-balanced bins).
 hipError_t launch_stochastic_length(const int *offsets, int B, long long T, int max_len, int cap,
