@@ -73,6 +73,8 @@ SIGNATURES = {
     "hstu_tile_shape": ([ctypes.POINTER(Problem), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                          ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
     "hstu_attn_fwd": ([ctypes.POINTER(Problem)] + [_vp] * 9 + [ctypes.c_size_t, _vp], ctypes.c_int),
+    "hstu_attn_fwd_static": ([ctypes.POINTER(Problem)] + [_vp] * 9, ctypes.c_int),
+    "hstu_static_scratch_bytes": ([], ctypes.c_size_t),
     "hstu_attn_bwd": ([ctypes.POINTER(Problem)] + [_vp] * 17 + [ctypes.c_size_t, _vp], ctypes.c_int),
     "hstu_mfalcon_score": ([ctypes.POINTER(Problem), _vp, ctypes.c_int64, ctypes.c_int32] + [_vp] * 7
                            + [ctypes.c_int32] + [_vp] * 5 + [ctypes.c_size_t, _vp], ctypes.c_int),

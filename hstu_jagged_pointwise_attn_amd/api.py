@@ -130,6 +130,34 @@ def attn_fwd(p, Q, K, V, U, *, Y=None, O=None, mean=None, rstd=None, ws=None, st
     return SimpleNamespace(Y=Y, O=O, mean=mean, rstd=rstd, ws=ws)
 
 
+def attn_fwd_static(p, Q, K, V, U, *, Y=None, O=None, mean=None, rstd=None, stream=None):
+    """hstu_attn_fwd_static: hstu_attn_fwd with the library's static device
+    scratch instead of a workspace (no allocation inside the library). The
+    outputs are allocated here unless given. Returns a namespace with Y, O,
+    mean and rstd."""
+    T, D = p.total_tokens, p.H * p.d
+    dev, dt = Q.device, Q.dtype
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (U, "U")):
+        _need(t, n, dt, dev, T * D)
+    if _DTYPES.get(dt) != p.dtype:
+        raise TypeError("tensor dtype differs from the problem's dtype")
+    Y = torch.empty(T, D, dtype=dt, device=dev) if Y is None else Y
+    O = torch.empty(T, D, dtype=dt, device=dev) if O is None else O
+    mean = torch.empty(T, dtype=torch.float32, device=dev) if mean is None else mean
+    rstd = torch.empty(T, dtype=torch.float32, device=dev) if rstd is None else rstd
+    for t, n in ((Y, "Y"), (O, "O")):
+        _need(t, n, dt, dev, T * D)
+    _need(mean, "mean", torch.float32, dev, T)
+    _need(rstd, "rstd", torch.float32, dev, T)
+    L.check(L.lib().hstu_attn_fwd_static(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(U), _ptr(Y), _ptr(O),
+                                         _ptr(mean), _ptr(rstd), _stream(stream)))
+    return SimpleNamespace(Y=Y, O=O, mean=mean, rstd=rstd)
+
+
+def static_scratch_bytes() -> int:
+    return int(L.lib().hstu_static_scratch_bytes())
+
+
 def attn_bwd(p, Q, K, V, U, O, mean, rstd, dY, *, dQ=None, dK=None, dV=None, dU=None, d_rab_p=None,
              d_rab_t=None, d_gamma=None, d_beta=None, want_affine=True, ws=None, stream=None):
     """hstu_attn_bwd. Returns a namespace with dQ, dK, dV, dU ([T, H, d]),

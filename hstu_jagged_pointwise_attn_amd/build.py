@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhstu.so")
 SOURCES = ["sched.hip", "attn_fwd.hip", "attn_bwd.hip", "norm.hip", "batching.hip", "layer.hip", "gemm.cpp",
-           "api.cpp"]
+           "api.cpp", "static_ws.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",

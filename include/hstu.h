@@ -171,6 +171,26 @@ hstu_status_t hstu_attn_fwd(const hstu_problem_t *p, const void *Q, const void *
                             size_t ws_bytes, void *stream);
 
 /*
+ * hstu_attn_fwd without a workspace, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation). Arguments and results as for hstu_attn_fwd; the
+ * scratch it needs (the tile schedule: at most hstu_static_scratch_bytes(),
+ * 4 MiB, which covers up to 8192 sequences and tens of millions of tokens)
+ * lives in a static device array of the library, one per GPU, held until the
+ * process ends. It calls no allocation routine. The array of the current
+ * device is shared by every call on that device and keeps the last call's
+ * contents (each call's scheduler rewrites all it reads): calls that overlap
+ * on one GPU, e.g. on two streams, race. Returns HSTU_ERR_WORKSPACE, before
+ * any GPU work, when hstu_workspace_size(p, HSTU_OP_FWD, ...) exceeds the
+ * array. The stream must belong to the current device.
+ */
+hstu_status_t hstu_attn_fwd_static(const hstu_problem_t *p, const void *Q, const void *K, const void *V,
+                                   const void *U, void *Y, void *O, float *mean, float *rstd, void *stream);
+
+/* Bytes of the static scratch array of hstu_attn_fwd_static (host only). */
+size_t hstu_static_scratch_bytes(void);
+
+/*
  * Backward of hstu_attn_fwd given dY [T, H*d]. O, mean and rstd are the
  * forward's outputs for the same inputs. Writes dQ, dK, dV, dU (overwritten,
  * [T, H, d]), d_rab_p [n_pos] and d_rab_t [n_tb] (overwritten; required when

@@ -232,3 +232,16 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_static_forward_rejects_oversized_problem(L):
+    """hstu_attn_fwd_static refuses, before any GPU work, a problem whose
+    schedule does not fit the static scratch."""
+    lib = L.lib()
+    cap = lib.hstu_static_scratch_bytes()
+    assert cap == 4 << 20
+    p = _problem(L, B=8192, total_tokens=100_000_000, max_len=65536)
+    dummy = ctypes.c_void_p(0x1000)
+    st = lib.hstu_attn_fwd_static(ctypes.byref(p), *([dummy] * 8), None)
+    assert st == L.HSTU_ERR_WORKSPACE
+    assert b"static scratch" in lib.hstu_last_error()
