@@ -629,6 +629,7 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
   b.rab_p = p->rab_p;
   b.rab_t = use_rt ? p->rab_t : nullptr;
   b.tfilt = (tf && use_t) ? 1 : 0;
+  b.no_cand = p->cand_len == nullptr ? 1 : 0;
   b.drab_p = d_rab_p;
   b.drab_t = d_rab_t;
   b.drab_p64 = rab64;

@@ -58,8 +58,9 @@ struct PairPrefetch {
 // tiles. Diagonals that no later key tile can touch are flushed to global
 // memory after every tile.
 // ---------------------------------------------------------------------------
-template <int D, bool USE_P, bool USE_T, bool TF>
+template <int D, bool USE_P, bool USE_T, bool TF, bool DIAG_DPP>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  static_assert(!DIAG_DPP || USE_P, "register diagonal sums are for rab_p");
   static_assert(!TF || USE_T, "the timestamp filter needs the timestamps");
   constexpr int BM = kFwdBM, BN = 32, NWV = 4;
   constexpr int KS = D / 32, ND = D / 16;
@@ -78,8 +79,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned tkey[USE_T ? 2 * BN : 4];
   __shared__ unsigned tkst[4];
   __shared__ float t2tab[33];
-  __shared__ float ring[USE_P ? RING : 1];
-  __shared__ float skew[USE_P ? NWV * 32 * SKW : 1];
+  // Diagonal rings, each updated by plain read-add-write (LDS float atomics
+  // are slow): with DIAG_DPP one per (wave, lane group) (no two lanes of a
+  // wave share an address; rings 20 words apart put a wave's 64 lanes in 64
+  // banks), otherwise one per wave for the skewed block's column sums.
+  constexpr int RSTR = RING + 20;
+  constexpr int NRING = DIAG_DPP ? NWV * 4 : NWV;
+  __shared__ float ring[USE_P ? NRING * RSTR : 1];
+  __shared__ float skew[USE_P && !DIAG_DPP ? NWV * 32 * SKW : 1];
   __shared__ float hts[USE_T ? 33 : 1];   // per-element path: by ffbh(|dt|) + 1
   __shared__ float htb[USE_T ? 32 : 1];   // constant blocks: by bucket
   __shared__ float self_acc;
@@ -121,8 +128,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     if (tid < 32) htb[tid] = 0.f;
   }
   if (USE_P) {
-    for (int c = tid; c < RING; c += NT) ring[c] = 0.f;
-    for (int c = tid; c < NWV * 32 * SKW; c += NT) skew[c] = 0.f;
+    for (int c = tid; c < NRING * RSTR; c += NT) ring[c] = 0.f;
+    if (!DIAG_DPP)
+      for (int c = tid; c < NWV * 32 * SKW; c += NT) skew[c] = 0.f;
   }
   __syncthreads();
 
@@ -256,6 +264,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   };
 
   float *skw = skew + w * 32 * SKW;
+  // DIAG_DPP (launches without candidates, so every row sits at its own
+  // position): the diagonal sums of a wave's 32 x 32 dS block of d rab_p are
+  // formed in registers. In the S^T layout lane (lg, lr) holds keys
+  // 16 mk + 4 lg + i of row 16 nq + lr, so element i sits on diagonal
+  // base + 16 (nq - mk) + lr - 4 lg - i. Shifting element i of every lane down
+  // by i lanes within its row of 16 (DPP row_shl) lines all four up on
+  // diagonal base + 16 (nq - mk) + lr - 4 lg; the elements that would leave
+  // the row land, shifted up by 16 - i (row_shr), on the diagonal 16 lower.
+  // dacc[s] holds diagonal base + 16 - 16 s + lr - 4 lg; the four are added
+  // into the ring of this wave and lane group. With candidates (positions
+  // repeat) the skewed LDS block is used instead.
+  constexpr bool wave_dpp = DIAG_DPP;
+  // rab_t sums of constant / two-bucket tiles, carried across key tiles while
+  // the bucket stays: per-lane partial sums of buckets tcur and tcur + 1
+  // (tcur < 0: none yet; -2 so that bucket 0 does not match tcur + 1).
+  int tcur = -2;
+  float tacc_lo = 0.f, tacc_hi = 0.f;
+  auto tflush = [&]() __attribute__((always_inline)) {
+    if (tcur >= 0) {
+      const float lo = wave_sum_f32(tacc_lo), hi = wave_sum_f32(tacc_hi);
+      if (lane == 0) {
+        if (lo != 0.f) atomicAdd(&htb[tcur], lo);
+        if (hi != 0.f) atomicAdd(&htb[tcur + 1], hi);
+      }
+    }
+    tacc_lo = tacc_hi = 0.f;
+  };
   if (nk > 0) {
     load(0);
     store(0);
@@ -273,7 +308,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
     bool tconst = true, two = false;
     float tcv = 0.f, tcv_hi = 0.f;
-    int tcidx = 0, tcidx_hi = 0;
+    int tcidx = 0;
     unsigned thr = 0u;
     if (USE_T) {
       const unsigned kmin = __builtin_amdgcn_readfirstlane(tkst[b * 2]);
@@ -299,7 +334,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       if (two) {
         thr = 1u << bhi;
         tcv_hi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t2tab[32 - bhi])));
-        tcidx_hi = bhi;
       }
     }
 
@@ -318,6 +352,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       const int prel = sd.P - (c0 + lg * 4);
       float tsum = 0.f, tsum_hi = 0.f, run_s = 0.f;
       int run_b = -1;
+      float dacc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int nq = 0; nq < 2; ++nq) {
         u32x4 wds;
@@ -351,7 +386,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
             if (TFV) vis = vis && (!tfr[nq] || prel > mk * 16 + i || tk4[i] < tq[nq]);
             if (!FULL) ds = vis ? ds : 0.f;
             dsv[i] = ds;
-            if (USE_P) skw[(nq * 16 + lr) * SKW + mk * 16 + lg * 4 + i + 31 - sh_r[nq]] = ds;
+            if (USE_P && !wave_dpp) skw[(nq * 16 + lr) * SKW + mk * 16 + lg * 4 + i + 31 - sh_r[nq]] = ds;
             if (USE_T) {
               if (TC || T2) {
                 tsum += ds;
@@ -368,19 +403,41 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           }
           wds[mk * 2] = pack_bf16x2(dsv[0], dsv[1]);
           wds[mk * 2 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+          if (USE_P && wave_dpp) {
+            const int sa = 1 - nq + mk;  // offset 16 (nq - mk) -> slot
+            dacc[sa] += dsv[0] + dpp_f32<0x101>(dsv[1]) + dpp_f32<0x102>(dsv[2]) + dpp_f32<0x103>(dsv[3]);
+            dacc[sa + 1] += dpp_f32<0x11F>(dsv[1]) + dpp_f32<0x11E>(dsv[2]) + dpp_f32<0x11D>(dsv[3]);
+          }
         }
         dsa[nq] = __builtin_bit_cast(bf16x8, wds);
       }
+      if (USE_P && wave_dpp) {
+        const int dbase = pos_w0 - c0 + lr - 4 * lg + 16;
+        float *rg = ring + (w * 4 + lg) * RSTR;
+        float old[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) old[k] = rg[(dbase - 16 * k) & (RING - 1)];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) rg[(dbase - 16 * k) & (RING - 1)] = old[k] + dacc[k];
+      }
       if (USE_T && TC) {
-        const float t = wave_sum_f32(tsum);
-        if (lane == 0) atomicAdd(&htb[tcidx], t);
+        if (tcidx == tcur) {
+          tacc_lo += tsum;
+        } else if (tcidx == tcur + 1) {
+          tacc_hi += tsum;
+        } else {
+          tflush();
+          tcur = tcidx;
+          tacc_lo = tsum;
+        }
       }
       if (USE_T && T2) {
-        const float t = wave_sum_f32(tsum), th = wave_sum_f32(tsum_hi);
-        if (lane == 0) {
-          atomicAdd(&htb[tcidx], t - th);
-          atomicAdd(&htb[tcidx_hi], th);
+        if (tcidx != tcur) {
+          tflush();
+          tcur = tcidx;
         }
+        tacc_lo += tsum - tsum_hi;
+        tacc_hi += tsum_hi;
       }
       if (USE_T && !TC && !T2 && run_b >= 0) atomicAdd(&hts[run_b], run_s);
     };
@@ -403,7 +460,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         else epilogue(bc<false>(), bc<true>(), bc<false>(), bc<false>());
       }
     }
-    if (USE_P) {
+    if (USE_P && !wave_dpp) {
       // column sums of the skewed block = this wave's diagonal sums
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -413,7 +470,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int rr = 0; rr < 32; ++rr) c1 += skw[rr * SKW + lane];
         const int tbase = pos_w0 - c0 + 31;  // diagonal of column c is tbase - c
-        atomicAdd(&ring[(tbase - lane) & (RING - 1)], c1);
+        float *slot = &ring[w * RSTR + ((tbase - lane) & (RING - 1))];
+        *slot += c1;
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -440,18 +498,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     if (USE_P && tid < BN) {
       const int t = (pos_max - c0) - tid;
       float *slot = &ring[t & (RING - 1)];
-      const float v = *slot;
+      float v = 0.f;
+#pragma unroll
+      for (int q = 0; q < NRING; ++q) {
+        v += slot[q * RSTR];
+        slot[q * RSTR] = 0.f;
+      }
       if (v != 0.f) atomicAdd(a.drab_p + pos_bucket(t, a.n_pos), v * a.inv_nmax);
-      *slot = 0.f;
     }
     if (kt + 1 < nk) gemms(b ^ 1);
   }
   if (USE_P && nk > 0 && tid < WIN - BN) {
     // the rest of the last window: diagonals [pos_max - c_last - 159, pos_max - c_last - 32]
     const int t = (pos_max - (nk - 1) * BN) - BN - tid;
-    const float v = ring[t & (RING - 1)];
+    const float *slot = &ring[t & (RING - 1)];
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < NRING; ++q) v += slot[q * RSTR];
     if (v != 0.f) atomicAdd(a.drab_p + pos_bucket(t, a.n_pos), v * a.inv_nmax);
   }
+
+  if (USE_T) tflush();
 
   // A candidate's pair with itself (|pos| and |dt| are 0).
   const bool any_cand = fil >= sd.E;
@@ -1052,7 +1119,27 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a) {
     return hipGetLastError();                                                                   \
   }
 
-HSTU_BWD_BF16_LAUNCH(bwd_dq_kernel, 256)
+template <int D>
+hipError_t launch_bwd_dq_kernel_d(const BwdArgs &a, hipStream_t s) {
+  const bool p = a.rab_p != nullptr, t = a.ts != nullptr;
+  const dim3 g(a.units), b(256);
+  if (a.tfilt) {
+    if (p) hipLaunchKernelGGL((bwd_dq_kernel<D, true, true, true, false>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<D, false, true, true, false>), g, b, 0, s, a);
+  } else if (p && a.no_cand) {
+    if (t) hipLaunchKernelGGL((bwd_dq_kernel<D, true, true, false, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<D, true, false, false, true>), g, b, 0, s, a);
+  } else if (p && t) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true, true, false, false>), g, b, 0, s, a);
+  } else if (p) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true, false, false, false>), g, b, 0, s, a);
+  } else if (t) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false, true, false, false>), g, b, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false, false, false, false>), g, b, 0, s, a);
+  }
+  return hipGetLastError();
+}
 HSTU_BWD_BF16_LAUNCH(bwd_dkdv_kernel, 256)
 
 hipError_t launch_attn_bwd_dq_bf16(const BwdArgs &a, hipStream_t s) {

@@ -145,6 +145,7 @@ struct BwdArgs {
   float inv_nmax;
   int H, d;
   int tfilt;                       // candidates see causal-segment keys only if strictly earlier
+  int no_cand;                     // no sequence has candidates (cand_len is NULL)
   int *hdr;                        // header of the schedule this kernel runs
   int *status;                     // the call's status word (HSTU_DEV_* bits)
   const SeqDesc *desc;
