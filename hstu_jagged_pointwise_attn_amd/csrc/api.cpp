@@ -577,8 +577,7 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
   ka.tiles = at<QTile>(ws, L.ktiles);
   {
     Timed t_(HSTU_KERNEL_SCHED, st);
-    HIP_TRY(launch_sched(qa, st), "scheduler launch");
-    HIP_TRY(launch_sched(ka, st), "key scheduler launch");
+    HIP_TRY(launch_sched_pair(qa, ka, st), "scheduler launch");
   }
   const int G = p->norm == HSTU_NORM_GLN ? p->n_groups : 1;
   float *dg = (p->gamma && p->norm != HSTU_NORM_NONE) ? d_gamma : nullptr;

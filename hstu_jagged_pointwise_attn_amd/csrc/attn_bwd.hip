@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int NCHUNK = BN * CH;
   constexpr int NCH = (NCHUNK + NT - 1) / NT;
   constexpr int WIN = BM + BN;         // 159 window entries used
-  constexpr int RING = 512;
+  constexpr int RING = 256;              // > the 159 diagonals live at once
   constexpr int SKW = 64;              // skewed row: 32 keys + 31 shifts (+1 pad)
   static_assert(BM == 128 && NCH >= 1, "4 waves x 32 rows");
   static_assert(BM * ST <= 4 * BN * ST, "dQ staging reuses the K/V buffers");

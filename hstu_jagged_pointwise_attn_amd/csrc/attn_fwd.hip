@@ -460,6 +460,12 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   __shared__ float Ks[BN][D];
   __shared__ float Vs[BN][D];
   __shared__ long long tsk[BN];
+  // rab_p window of a key tile (entry x: rab_p[|pos_max - c0 - x|]) and the
+  // rab_t table by bucket (|dt| < 2^63, so buckets stop at 62), in LDS so
+  // that the key loop does no dependent global loads.
+  constexpr int PWIN = kF32BM + BN;
+  __shared__ float rabw[PWIN];
+  __shared__ float rabt[64];
 
   const int H = a.H;
   const int unit = blockIdx.x;
@@ -486,6 +492,9 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
     o[c] = 0.f;
   }
   const int kv_limit = frame_hi(sd.q_frame0 + row0 + nrows - 1, sd.P, sd.E);
+  const int fil = sd.q_frame0 + row0 + nrows - 1;
+  const int pos_max = fil < sd.E ? fil : sd.E;
+  if (use_t && has_rt && tid < 64) rabt[tid] = a.rab_t[min(tid, a.n_tb - 1)];
 
   for (int kt = 0; kt < nk; ++kt) {
     const int c0 = kt * BN;
@@ -498,17 +507,23 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
       Vs[row][col] = in ? V[g] : 0.f;
     }
     if (tid < BN) tsk[tid] = (use_t && c0 + tid < kv_limit) ? a.ts_kv[sd.kv_base + c0 + tid] : 0;
+    if (use_p && tid < PWIN) rabw[tid] = a.rab_p[pos_bucket(pos_max - c0 - tid, a.n_pos)];
     __syncthreads();
     const int jend = min(BN, kv_limit - c0);
+    // The four lanes of a row hold a quarter of q each; their partial dot
+    // products are summed with two quad DPP moves (no LDS round trip).
+#pragma unroll 4
     for (int jl = 0; jl < jend; ++jl) {
       const int j = c0 + jl;
       float s = 0.f;
 #pragma unroll
       for (int c = 0; c < DP; ++c) s = fmaf(q[c], Ks[jl][part * DP + c], s);
-      s += __shfl_xor(s, 1, 64);
-      s += __shfl_xor(s, 2, 64);
-      if (use_p) s += a.rab_p[pos_bucket(pos - j, a.n_pos)];
-      if (use_t && has_rt) s += a.rab_t[time_bucket(tq - tsk[jl], a.n_tb)];
+      s += dpp_f32<0xB1>(s);
+      s += dpp_f32<0x4E>(s);
+      // pos - j = pos_max - c0 - x with x = pos_max - pos + jl in [0, 126]
+      // (rows past the tile end read x = jl; their pairs are masked)
+      if (use_p) s += rabw[(ok ? pos_max - pos : 0) + jl];
+      if (use_t && has_rt) s += rabt[time_bucket(tq - tsk[jl], 64)];
       const bool vis = j < hi && (!tfr || j < sd.P || tsk[jl] < tq);
       const float p = vis ? s / (1.0f + expf(-s)) : 0.f;
 #pragma unroll

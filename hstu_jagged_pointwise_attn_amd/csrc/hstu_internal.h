@@ -63,6 +63,8 @@ struct SchedArgs {
 };
 
 hipError_t launch_sched(const SchedArgs &a, hipStream_t s);
+// Builds two independent schedules in one launch (one workgroup each).
+hipError_t launch_sched_pair(const SchedArgs &a, const SchedArgs &b, hipStream_t s);
 
 // Forward attention kernels. Arrays are token-major with row stride H*d.
 struct FwdArgs {

@@ -263,7 +263,7 @@ __device__ void sort_keys(unsigned *keys, unsigned *tmp, int n2) {
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
+__device__ __forceinline__ void sched_body(const SchedArgs &a) {
   constexpr int kRecCache = kSchedThreads;  // records kept in LDS for short lists
   __shared__ int s_qoff[kMaxSeqs + 1];
   __shared__ unsigned s_keys[kSortCap];
@@ -377,10 +377,23 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) { sched_body(a); }
+
+// Two independent schedules in one launch (workgroup 0 builds a, 1 builds b).
+__global__ __launch_bounds__(kSchedThreads) void sched_pair_kernel(SchedArgs a, SchedArgs b) {
+  if (blockIdx.x == 0) sched_body(a);
+  else sched_body(b);
+}
+
 }  // namespace
 
 hipError_t launch_sched(const SchedArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sched_pair(const SchedArgs &a, const SchedArgs &b, hipStream_t s) {
+  hipLaunchKernelGGL(sched_pair_kernel, dim3(2), dim3(kSchedThreads), 0, s, a, b);
   return hipGetLastError();
 }
 
