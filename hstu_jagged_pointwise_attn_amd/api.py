@@ -295,6 +295,13 @@ def kernel_timing(enable: bool) -> None:
     L.check(L.lib().hstu_kernel_timing(1 if enable else 0))
 
 
+def set_inline_schedule(enable: bool) -> bool:
+    """hstu_set_inline_schedule: whether small forwards build their tiles
+    inside the attention kernel (default) instead of launching the scheduler.
+    Returns the previous setting."""
+    return bool(L.lib().hstu_set_inline_schedule(1 if enable else 0))
+
+
 def kernel_timing_read(kernel: int):
     """hstu_kernel_timing_read: (total milliseconds, launches) of one kernel id."""
     ms, n = ctypes.c_double(0), ctypes.c_int64(0)

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -264,11 +266,25 @@ hstu_status_t check_mfalcon(const hstu_problem_t *cand, const int32_t *hist_offs
   return HSTU_OK;
 }
 
+// Whether small forwards build their tiles inside the attention kernel
+// (hstu_set_inline_schedule).
+std::atomic<int> g_inline_sched{1};
+
+// Per-call value that marks an inline-schedule forward's timestamp flag in
+// the workspace header; seeded from the clock so that a fresh workspace's
+// stale contents match it only by a 2^-32 chance.
+unsigned next_epoch() {
+  static std::atomic<unsigned> e{(unsigned)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u};
+  return e.fetch_add(1u);
+}
+
+// inl: when not NULL, the attention workgroups build their own tiles from it
+// (no scheduler launch before this call).
 hstu_status_t run_forward(const hstu_problem_t *p, int op, const Layout &L, void *ws,
                           hipStream_t st, const void *Q, const void *K, const void *V,
                           const void *Kself, const void *Vself, const void *U,
                           const int64_t *ts_q, const int64_t *ts_kv, void *Y, void *O,
-                          float *mean, float *rstd) {
+                          float *mean, float *rstd, const SchedArgs *inl = nullptr) {
   Tiles t = tiles_for(p, op);
   FwdArgs f;
   std::memset(&f, 0, sizeof f);
@@ -293,6 +309,12 @@ hstu_status_t run_forward(const hstu_problem_t *p, int op, const Layout &L, void
   if (units >= (1ll << 31)) return fail(HSTU_ERR_UNSUPPORTED, "too many work units");
   f.units = (int)units;
   (void)t;
+  const unsigned epoch = next_epoch();
+  if (inl) {
+    f.inline_sched = 1;
+    f.epoch = epoch;
+    f.sched = *inl;
+  }
   {
     Timed t_(HSTU_KERNEL_ATTN_FWD, st);
     HIP_TRY(p->dtype == HSTU_BF16 ? launch_attn_fwd_bf16(f, st) : launch_attn_fwd_f32(f, st),
@@ -312,6 +334,8 @@ hstu_status_t run_forward(const hstu_problem_t *p, int op, const Layout &L, void
   n.T = p->total_tokens;
   n.D = p->H * p->d;
   n.hdr = at<int>(ws, L.hdr);
+  n.merge_ts = inl && f.ts_q ? 1 : 0;
+  n.epoch = epoch;
   {
     Timed t_(HSTU_KERNEL_NORM_FWD, st);
     HIP_TRY(launch_norm_fwd(n, p->dtype == HSTU_BF16, st), "norm forward launch");
@@ -451,6 +475,8 @@ extern "C" {
 
 const char *hstu_version(void) { return "0.1.0"; }
 
+int32_t hstu_set_inline_schedule(int32_t enable) { return g_inline_sched.exchange(enable ? 1 : 0); }
+
 const char *hstu_last_error(void) { return g_err.c_str(); }
 
 hstu_status_t hstu_workspace_size(const hstu_problem_t *p, int32_t op, int32_t microbatch,
@@ -493,12 +519,16 @@ hstu_status_t hstu_attn_fwd(const hstu_problem_t *p, const void *Q, const void *
   hipStream_t st = (hipStream_t)stream;
   SchedArgs sa;
   fill_sched(sa, p, HSTU_OP_FWD, L, ws, nullptr, 0, 0, 0);
-  {
+  // Small batches skip the scheduler launch: each attention workgroup finds
+  // its own tile (one dependent launch less on a latency-bound step).
+  const bool inl = g_inline_sched.load(std::memory_order_relaxed) != 0 && p->total_tokens > 0 &&
+                   p->B > 0 && p->B <= kInlineSchedMaxSeqs && L.max_tiles * p->H <= kInlineSchedMaxUnits;
+  if (!inl) {
     Timed t_(HSTU_KERNEL_SCHED, st);
     HIP_TRY(launch_sched(sa, st), "scheduler launch");
   }
   return run_forward(p, HSTU_OP_FWD, L, ws, st, Q, K, V, K, V, U, p->timestamps, p->timestamps,
-                     Y, O, mean, rstd);
+                     Y, O, mean, rstd, inl ? &sa : nullptr);
 }
 
 hstu_status_t hstu_mfalcon_score(const hstu_problem_t *cand, const int32_t *hist_offsets,

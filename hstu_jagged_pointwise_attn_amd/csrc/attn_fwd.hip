@@ -22,6 +22,7 @@
 #include "hstu_internal.h"
 #include "../../include/hstu.h"
 #include "device_common.h"
+#include "sched_common.h"
 
 namespace hstu {
 namespace {
@@ -150,7 +151,8 @@ __device__ __forceinline__ void fwd_epilogue(const f32x4 (&st)[4][2], bf16x8 (&p
 // of a distant key tile rarely changes); then rab_t is one scalar for the
 // whole block, else it is gathered per element from a 33-entry LDS table
 // indexed by ffbh(|dt|) + 1.
-template <int D, bool USE_P, bool USE_T, bool TF>
+// INL: the workgroup builds its own tile (small batches, no scheduler launch).
+template <int D, bool USE_P, bool USE_T, bool TF, bool INL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   static_assert(!TF || USE_T, "the timestamp filter needs the timestamps");
   constexpr int BM = kFwdBM, BN = kFwdBN;
@@ -175,9 +177,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int H = a.H;
   const int unit = blockIdx.x;
   const int r = unit / H, h = unit % H;
-  if (r >= a.hdr[kHdrNQ]) return;
-  const QTile tile = a.tiles[r];
-  const SeqDesc sd = a.desc[tile.b];
+  QTile tile;
+  SeqDesc sd;
+  if constexpr (INL) {
+    // the K buffers are free until the first tile is staged
+    if (!sched_dev::inline_tile<256>(a.sched, r, unit == 0, (int *)Ks, &tile, &sd)) return;
+  } else {
+    if (r >= a.hdr[kHdrNQ]) return;
+    tile = a.tiles[r];
+    sd = a.desc[tile.b];
+  }
   const int nk = tile.nk, nf = tile.nf_nrows & 0xffff, nrows = tile.nf_nrows >> 16;
   const int row0 = tile.row0;
   const long long ld = (long long)H * D;
@@ -449,11 +458,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       *(uint4 *)(O + (long long)(sd.q_base + row0 + row) * ld + h * D + col) =
           *(const uint4 *)(os + row * OST + col);
   }
-  if (USE_T && tid == 0 && s_bad) atomicOr(&a.hdr[kHdrStatus], HSTU_DEV_BAD_TIMESTAMPS);
+  if (USE_T && tid == 0 && s_bad) {
+    if constexpr (INL) a.hdr[kHdrInlineTs] = (int)a.epoch;
+    else atomicOr(&a.hdr[kHdrStatus], HSTU_DEV_BAD_TIMESTAMPS);
+  }
 }
 
 // fp32: 256 threads = 64 rows x 4 column slices of D/4; keys staged in LDS.
-template <int D>
+template <int D, bool INL>
 __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   constexpr int BN = kF32BN, DP = D / 4;
   static_assert(kF32BM == 64, "64 rows x 4 slices");
@@ -470,9 +482,16 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   const int H = a.H;
   const int unit = blockIdx.x;
   const int r = unit / H, h = unit % H;
-  if (r >= a.hdr[kHdrNQ]) return;
-  const QTile tile = a.tiles[r];
-  const SeqDesc sd = a.desc[tile.b];
+  QTile tile;
+  SeqDesc sd;
+  if constexpr (INL) {
+    static_assert(sizeof(Ks) >= (256 + 4 + 3) * sizeof(int), "scan space in the K tile");
+    if (!sched_dev::inline_tile<256>(a.sched, r, unit == 0, (int *)&Ks[0][0], &tile, &sd)) return;
+  } else {
+    if (r >= a.hdr[kHdrNQ]) return;
+    tile = a.tiles[r];
+    sd = a.desc[tile.b];
+  }
   const int nk = tile.nk, nrows = tile.nf_nrows >> 16, row0 = tile.row0;
   const long long ld = (long long)H * D;
   const int tid = threadIdx.x, lrow = tid >> 2, part = tid & 3;
@@ -556,23 +575,28 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
 
 }  // namespace
 
-template <int D>
-hipError_t launch_bf16_d(const FwdArgs &a, hipStream_t s) {
+template <int D, bool INL>
+hipError_t launch_bf16_di(const FwdArgs &a, hipStream_t s) {
   const bool p = a.rab_p != nullptr, t = a.ts_q != nullptr;
   const dim3 g(a.units), b(256);
   if (a.tfilt) {
-    if (p) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, true, true>), g, b, 0, s, a);
+    if (p) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true, true, INL>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, true, true, INL>), g, b, 0, s, a);
   } else if (p && t) {
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true, false>), g, b, 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true, false, INL>), g, b, 0, s, a);
   } else if (p) {
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false, false>), g, b, 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false, false, INL>), g, b, 0, s, a);
   } else if (t) {
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, true, false>), g, b, 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, true, false, INL>), g, b, 0, s, a);
   } else {
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, false>), g, b, 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, false, INL>), g, b, 0, s, a);
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bf16_d(const FwdArgs &a, hipStream_t s) {
+  return a.inline_sched ? launch_bf16_di<D, true>(a, s) : launch_bf16_di<D, false>(a, s);
 }
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs &a, hipStream_t s) {
@@ -585,15 +609,21 @@ hipError_t launch_attn_fwd_bf16(const FwdArgs &a, hipStream_t s) {
   }
 }
 
+template <int D>
+hipError_t launch_f32_d(const FwdArgs &a, hipStream_t s) {
+  if (a.inline_sched) hipLaunchKernelGGL((attn_fwd_f32_kernel<D, true>), dim3(a.units), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((attn_fwd_f32_kernel<D, false>), dim3(a.units), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_fwd_f32(const FwdArgs &a, hipStream_t s) {
   if (a.units <= 0) return hipSuccess;
   switch (a.d) {
-    case 32: hipLaunchKernelGGL(attn_fwd_f32_kernel<32>, dim3(a.units), dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, dim3(a.units), dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, dim3(a.units), dim3(256), 0, s, a); break;
+    case 32: return launch_f32_d<32>(a, s);
+    case 64: return launch_f32_d<64>(a, s);
+    case 128: return launch_f32_d<128>(a, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace hstu

@@ -35,6 +35,11 @@ struct QTile {
 constexpr int kHdrStatus = 0;    // OR of HSTU_DEV_* bits
 constexpr int kHdrFirstBad = 1;  // smallest offending sequence index
 constexpr int kHdrNQ = 2;        // number of query tiles
+// Timestamp flag of a forward whose workgroups built their own tiles: the
+// attention kernel stores the call's epoch there when it meets a timestamp
+// out of range, and the norm kernel that follows moves that into
+// kHdrStatus and overwrites the word (so no flag outlives its call).
+constexpr int kHdrInlineTs = 3;
 constexpr int kHdrWords = 64;    // 256 bytes
 
 constexpr int kSchedThreads = 1024;
@@ -43,6 +48,13 @@ constexpr int kMaxSeqs = 8192;   // sequences per call (query-tile offsets live 
 constexpr int kMaxKeyTiles = 16383;
 
 enum SchedMode { kSchedAttn = 0, kSchedMFalcon = 1, kSchedKeys = 2 };
+
+// A forward of at most this many sequences and work units (query tiles x
+// heads, as bounded on the host) skips the scheduler launch: every attention
+// workgroup finds its own tile (sched_dev::inline_tile). At this size all
+// units run at once or nearly, so the longest-first order has nothing to win.
+constexpr int kInlineSchedMaxSeqs = 256;
+constexpr long long kInlineSchedMaxUnits = 1024;
 
 struct SchedArgs {
   int mode;
@@ -81,6 +93,12 @@ struct FwdArgs {
   const SeqDesc *desc;
   const QTile *tiles;
   int units;                      // grid size bound: max query tiles * H
+  // Small batches: each workgroup builds its own tile from `sched`
+  // (kSchedAttn) instead of reading desc / tiles, and a timestamp out of
+  // range is flagged by storing `epoch` into hdr[kHdrInlineTs].
+  int inline_sched;
+  unsigned epoch;
+  SchedArgs sched;
 };
 
 // bf16 inputs, MFMA, tile 128 x 64
@@ -105,6 +123,10 @@ struct NormArgs {
   long long T;
   int D;
   int *hdr;             // status word (group id violations)
+  // After an attention forward with inline_sched: fold hdr[kHdrInlineTs] ==
+  // epoch into the status word, then overwrite it.
+  int merge_ts;
+  unsigned epoch;
 };
 hipError_t launch_norm_fwd(const NormArgs &a, bool bf16, hipStream_t s);
 

@@ -88,6 +88,10 @@ template <bool BF16, int MAXCH>
 __global__ __launch_bounds__(256) void norm_fwd_kernel(NormArgs a) {
   using V = Vec<BF16>;
   constexpr int N = V::N;
+  if (a.merge_ts && blockIdx.x == 0 && threadIdx.x == 0) {
+    if ((unsigned)a.hdr[kHdrInlineTs] == a.epoch) atomicOr(&a.hdr[kHdrStatus], HSTU_DEV_BAD_TIMESTAMPS);
+    a.hdr[kHdrInlineTs] = (int)~a.epoch;
+  }
   const long long t = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
   const int lane = threadIdx.x & 63;

@@ -27,106 +27,12 @@
 // (k0 < P ? 0 : k0) to the end of the sequence.
 #include "hstu_internal.h"
 #include "../../include/hstu.h"
+#include "sched_common.h"
 
 namespace hstu {
 namespace {
 
-__device__ __forceinline__ int frame_hi(int i, int P, int E) {
-  return i < P ? P : (i < E ? i + 1 : E);
-}
-
-// Validated frame of sequence b (see SeqDesc). Offending sequences come back
-// with valid = 0 and qcount = 0, and their status bits in *bits.
-__device__ SeqDesc seq_info(const SchedArgs &a, int b, int *bits) {
-  SeqDesc s{};
-  *bits = 0;
-  if (a.mode != kSchedMFalcon) {
-    long long beg = a.offsets[b], end = a.offsets[b + 1];
-    int P = a.prefix ? a.prefix[b] : 0;
-    int C = a.cand ? a.cand[b] : 0;
-    long long L = end - beg;
-    if (beg < 0 || end < beg || end > a.Tq) *bits |= HSTU_DEV_BAD_OFFSETS;
-    else if (L > a.max_len) *bits |= HSTU_DEV_TOO_LONG;
-    else if (P < 0 || C < 0 || (long long)P + C > L) *bits |= HSTU_DEV_BAD_SEGMENTS;
-    if (*bits) return s;
-    s.q_base = (int)beg;
-    s.kv_base = (int)beg;
-    s.E = (int)L - C;
-    s.P = P;
-    s.self_base = (int)beg + s.E;
-    s.q_frame0 = 0;
-    s.qcount = (int)L;
-    s.valid = 1;
-  } else {
-    long long hb = a.hist_offsets[b], he = a.hist_offsets[b + 1];
-    long long cb = a.cand_offsets[b], ce = a.cand_offsets[b + 1];
-    if (hb < 0 || he < hb || he > a.Tkv || cb < 0 || ce < cb || ce > a.Tq)
-      *bits |= HSTU_DEV_BAD_OFFSETS;
-    else if (he - hb > a.hist_max_len || ce - cb > a.max_len)
-      *bits |= HSTU_DEV_TOO_LONG;
-    if (*bits) return s;
-    int n = (int)(he - hb);
-    s.q_base = (int)cb;
-    s.kv_base = (int)hb;
-    s.self_base = (int)cb;
-    s.q_frame0 = n;
-    s.P = 0;
-    s.E = n;
-    s.qcount = (int)(ce - cb);
-    s.valid = 1;
-  }
-  return s;
-}
-
-__device__ __forceinline__ int div_up(int x, int y) { return (x + y - 1) / y; }
-
-// Number of work records (query tiles, or key tiles in key-major mode) of a sequence.
-__device__ int qtile_count(const SchedArgs &a, const SeqDesc &s) {
-  const int q = s.qcount;
-  if (q <= 0) return 0;
-  if (a.mode == kSchedKeys) return div_up(s.E, a.BN);
-  if (a.mode == kSchedAttn || a.microbatch <= 0 || a.microbatch >= q) return div_up(q, a.BM);
-  int bm = a.microbatch, tpm = div_up(bm, a.BM);
-  return (q / bm) * tpm + div_up(q % bm, a.BM);
-}
-
-// Record of the t-th query tile (canonical order) of sequence s.
-__device__ QTile make_tile(const SchedArgs &a, const SeqDesc &s, int b, int t) {
-  int row0, nrows;
-  if (a.mode == kSchedKeys) {
-    const int k0 = t * a.BN;
-    const int nkeys = min(a.BN, s.E - k0);
-    const int qt_lo = (k0 < s.P ? 0 : k0) / a.BM;
-    const int qt_hi = div_up(s.qcount, a.BM);
-    QTile r;
-    r.b = b;
-    r.row0 = k0;
-    r.nk = qt_hi - qt_lo;
-    r.nf_nrows = qt_lo | (nkeys << 16);
-    return r;
-  }
-  if (a.mode == kSchedAttn || a.microbatch <= 0 || a.microbatch >= s.qcount) {
-    row0 = t * a.BM;
-    nrows = min(a.BM, s.qcount - row0);
-  } else {
-    int bm = a.microbatch, tpm = div_up(bm, a.BM);
-    int mb = t / tpm, ti = t % tpm;
-    row0 = mb * bm + ti * a.BM;
-    int end = min(s.qcount, (mb + 1) * bm);
-    nrows = min(a.BM, end - row0);
-  }
-  int i0 = s.q_frame0 + row0, i1 = i0 + nrows - 1;
-  int nk = div_up(frame_hi(i1, s.P, s.E), a.BN);
-  int nf = frame_hi(i0, s.P, s.E) / a.BN;
-  // Under the timestamp filter a candidate row is sure to see only the prefix.
-  if (a.time_filter && i1 >= s.E) nf = min(nf, s.P / a.BN);
-  QTile r;
-  r.b = b;
-  r.row0 = row0;
-  r.nk = nk;
-  r.nf_nrows = nf | (nrows << 16);
-  return r;
-}
+using namespace sched_dev;
 
 // Exclusive scan of one value per thread across the workgroup.
 __device__ int block_exclusive_scan(int v, int *s_wsum, int *total) {

@@ -298,6 +298,17 @@ hstu_status_t hstu_kernel_timing(int32_t enable);
 hstu_status_t hstu_kernel_timing_read(int32_t kernel, double *total_ms, int64_t *launches);
 
 /*
+ * Small forwards (at most 256 sequences and 1024 work units of query tiles
+ * x heads) normally skip the scheduler launch: every attention workgroup
+ * validates the offsets, scans the query-tile counts and finds its own tile,
+ * taking the tiles in canonical order instead of longest-first (all units
+ * run at once at that size). Outputs and status bits are the same either
+ * way. enable = 0 makes every forward launch the scheduler, 1 restores the
+ * default. Process-wide, host only; returns the previous setting.
+ */
+int32_t hstu_set_inline_schedule(int32_t enable);
+
+/*
  * Stochastic Length (HSTU blog, section 3.4: training sequences are sampled
  * down to a length budget, 4096 -> about 776 at alpha = 1.6). Device side,
  * no host round trip. For every sequence b of the input batch (offsets [B+1],
