@@ -96,7 +96,7 @@ def algorithmic_bytes(wl, src, kind):
 # Sources each timed kernel is built from (a traffic figure is valid only
 # while these are unchanged).
 KERNEL_SOURCES = {
-    "attn_fwd": ["attn_fwd.hip", "device_common.h", "hstu_internal.h"],
+    "attn_fwd": ["attn_fwd.hip", "device_common.h", "hstu_internal.h", "sched_common.h"],
     "attn_bwd_dq": ["attn_bwd.hip", "device_common.h", "hstu_internal.h"],
     "attn_bwd_dkdv": ["attn_bwd.hip", "device_common.h", "hstu_internal.h"],
     "norm_fwd": ["norm.hip", "hstu_internal.h"],

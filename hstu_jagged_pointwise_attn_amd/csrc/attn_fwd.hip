@@ -465,10 +465,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
 }
 
 // fp32: 256 threads = 64 rows x 4 column slices of D/4; keys staged in LDS.
+// Key groups of the fp32 kernel: the keys of a tile are dealt round-robin to
+// KSPLIT groups of 256 threads, whose partial outputs are summed in LDS at the
+// end, so that a thread's dependent chain is 64 / KSPLIT keys long.
+template <int D>
+constexpr int f32_ksplit() { return D <= 64 ? 4 : 2; }
+
 template <int D, bool INL>
-__global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256 * f32_ksplit<D>()) void attn_fwd_f32_kernel(FwdArgs a) {
   constexpr int BN = kF32BN, DP = D / 4;
-  static_assert(kF32BM == 64, "64 rows x 4 slices");
+  constexpr int KSPLIT = f32_ksplit<D>(), NT = 256 * KSPLIT;
+  static_assert(kF32BM == 64, "64 rows x 4 slices per key group");
   __shared__ float Ks[BN][D];
   __shared__ float Vs[BN][D];
   __shared__ long long tsk[BN];
@@ -478,6 +485,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   constexpr int PWIN = kF32BM + BN;
   __shared__ float rabw[PWIN];
   __shared__ float rabt[64];
+  __shared__ float red[(KSPLIT - 1) * kF32BM * D];  // partial outputs of key groups 1..
 
   const int H = a.H;
   const int unit = blockIdx.x;
@@ -485,8 +493,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   QTile tile;
   SeqDesc sd;
   if constexpr (INL) {
-    static_assert(sizeof(Ks) >= (256 + 4 + 3) * sizeof(int), "scan space in the K tile");
-    if (!sched_dev::inline_tile<256>(a.sched, r, unit == 0, (int *)&Ks[0][0], &tile, &sd)) return;
+    static_assert(sizeof(Ks) >= (NT + NT / 64 + 3) * sizeof(int), "scan space in the K tile");
+    if (!sched_dev::inline_tile<NT>(a.sched, r, unit == 0, (int *)&Ks[0][0], &tile, &sd)) return;
   } else {
     if (r >= a.hdr[kHdrNQ]) return;
     tile = a.tiles[r];
@@ -494,7 +502,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   }
   const int nk = tile.nk, nrows = tile.nf_nrows >> 16, row0 = tile.row0;
   const long long ld = (long long)H * D;
-  const int tid = threadIdx.x, lrow = tid >> 2, part = tid & 3;
+  const int tid = threadIdx.x, kgrp = tid >> 8, lrow = (tid & 255) >> 2, part = tid & 3;
   const float *Q = (const float *)a.Q, *K = (const float *)a.K, *V = (const float *)a.V;
   const bool use_p = a.rab_p != nullptr, use_t = a.ts_q != nullptr, has_rt = a.rab_t != nullptr;
 
@@ -518,7 +526,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   for (int kt = 0; kt < nk; ++kt) {
     const int c0 = kt * BN;
     __syncthreads();
-    for (int c = tid; c < BN * D; c += 256) {
+    for (int c = tid; c < BN * D; c += NT) {
       const int row = c / D, col = c % D;
       const bool in = c0 + row < kv_limit;
       const long long g = (long long)(sd.kv_base + c0 + row) * ld + h * D + col;
@@ -532,7 +540,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
     // The four lanes of a row hold a quarter of q each; their partial dot
     // products are summed with two quad DPP moves (no LDS round trip).
 #pragma unroll 4
-    for (int jl = 0; jl < jend; ++jl) {
+    for (int jl = kgrp; jl < jend; jl += KSPLIT) {
       const int j = c0 + jl;
       float s = 0.f;
 #pragma unroll
@@ -549,6 +557,18 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
       for (int c = 0; c < DP; ++c) o[c] = fmaf(p, Vs[jl][part * DP + c], o[c]);
     }
   }
+
+  // Sum the key groups' partial outputs (group 0 keeps the total).
+  if (kgrp > 0) {
+#pragma unroll
+    for (int c = 0; c < DP; ++c) red[((kgrp - 1) * kF32BM + lrow) * D + part * DP + c] = o[c];
+  }
+  __syncthreads();
+  if (kgrp > 0) return;
+#pragma unroll
+  for (int g = 0; g < KSPLIT - 1; ++g)
+#pragma unroll
+    for (int c = 0; c < DP; ++c) o[c] += red[(g * kF32BM + lrow) * D + part * DP + c];
 
   if (ok && fi >= sd.E) {
     const float *Ksf = (const float *)a.Kself, *Vsf = (const float *)a.Vself;
@@ -611,8 +631,9 @@ hipError_t launch_attn_fwd_bf16(const FwdArgs &a, hipStream_t s) {
 
 template <int D>
 hipError_t launch_f32_d(const FwdArgs &a, hipStream_t s) {
-  if (a.inline_sched) hipLaunchKernelGGL((attn_fwd_f32_kernel<D, true>), dim3(a.units), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((attn_fwd_f32_kernel<D, false>), dim3(a.units), dim3(256), 0, s, a);
+  const dim3 g(a.units), b(256 * f32_ksplit<D>());
+  if (a.inline_sched) hipLaunchKernelGGL((attn_fwd_f32_kernel<D, true>), g, b, 0, s, a);
+  else hipLaunchKernelGGL((attn_fwd_f32_kernel<D, false>), g, b, 0, s, a);
   return hipGetLastError();
 }
 
