@@ -685,6 +685,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     kmin = __builtin_amdgcn_readfirstlane(wave_min_u32(tk));
     kmax = __builtin_amdgcn_readfirstlane(wave_max_u32(tk));
   }
+  // The t2tab entries in a register (lane c holds entry c): a step's
+  // constant rab_t term is a lane read, with no LDS round trip.
+  float t2v = 0.f;
+  if (USE_T && has_rt && lane < 33) {
+    const int bkt = lane == 0 ? 0 : 32 - lane;
+    t2v = -kLog2e * a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1];
+  }
   bf16x8 kf[KS], vf[KS];
   {
     const long long off = (long long)(sd.kv_base + key) * ld + h * D + lg * 8;
@@ -797,7 +804,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       }
       const int blo = bucket_u32(dlo, a.n_tb), bhi = bucket_u32(dhi, a.n_tb);
       tconst = blo == bhi;
-      tcv = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t2tab[ffbh_u32(dlo) + 1])));
+      // t2tab index ffbh(dlo) + 1, in scalar registers
+      tcv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t2v), dlo ? __builtin_clz(dlo) + 1 : 0));
     }
     // Under the timestamp filter, candidate rows of this step see the tile's
     // causal keys by time: such a step is partial and takes the gathered path.
@@ -806,45 +814,62 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const bool full = fr0 >= rmin_tile && !tf_step;
     const int rrel = rmin - (fr0 + lg * 4);  // element (mr, i) visible iff 16 mr + i >= rrel
     bf16x8 pa[2], da[2];
+    // FULL (every pair visible) and TC (one rab_t value for the step) are
+    // compile-time in each copy of the epilogue, so that the per-element
+    // bucket reads of the other steps are straight-line code (issued
+    // together, one wait) rather than a branch and a wait per element.
+    auto epilogue = [&](auto fullc, auto tconstc) __attribute__((always_inline)) {
+      constexpr bool FULL = decltype(fullc)::value, TC = decltype(tconstc)::value;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      u32x4 wp, wd;
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 wp, wd;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int mr = kk * 2 + h2;
-        u32x4 tr4 = {0u, 0u, 0u, 0u};
-        if (USE_T && !tconst) tr4 = *(const u32x4 *)(trow + b * BM + mr * 16 + lg * 4);
-        float pv[4], dv4[4];
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int mr = kk * 2 + h2;
+          u32x4 tr4 = {0u, 0u, 0u, 0u};
+          if (USE_T && !TC) tr4 = *(const u32x4 *)(trow + b * BM + mr * 16 + lg * 4);
+          float pv[4], dv4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // t = -log2(e) x with x = S + rab_t (t2tab and tcv hold
-          // -log2(e) rab_t); p = t sig(x) = -log2(e) SiLU(x), which the dV
-          // scale undoes, and SiLU'(x) = sig + p (-ln 2) (1 - sig).
-          float t;
-          if (USE_T) t = fmaf(s[mr][i], -kLog2e, tconst ? tcv : t2tab[ffbh_u32(absdiff_u32(tr4[i], tk)) + 1]);
-          else t = s[mr][i] * -kLog2e;
-          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
-          float p = t * sg;
-          float d = dp[mr][i] * fmaf(p, fmaf(sg, kLn2, -kLn2), sg);
-          bool vis = mr * 16 + i >= rrel;
-          if (TF && tf_step) {
-            const int row = fr0 + lg * 4 + mr * 16 + i;
-            vis = vis && (row < sd.E || key < sd.P || tk < tr4[i]);
+          for (int i = 0; i < 4; ++i) {
+            // t = -log2(e) x with x = S + rab_t (t2tab and tcv hold
+            // -log2(e) rab_t); p = t sig(x) = -log2(e) SiLU(x), which the dV
+            // scale undoes, and SiLU'(x) = sig + p (-ln 2) (1 - sig).
+            float t;
+            if (USE_T) t = fmaf(s[mr][i], -kLog2e, TC ? tcv : t2tab[ffbh_u32(absdiff_u32(tr4[i], tk)) + 1]);
+            else t = s[mr][i] * -kLog2e;
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+            float p = t * sg;
+            float d = dp[mr][i] * fmaf(p, fmaf(sg, kLn2, -kLn2), sg);
+            if (!FULL) {
+              bool vis = mr * 16 + i >= rrel;
+              if (TF && !TC && tf_step) {
+                const int row = fr0 + lg * 4 + mr * 16 + i;
+                vis = vis && (row < sd.E || key < sd.P || tk < tr4[i]);
+              }
+              if (!vis) {
+                p = 0.f;
+                d = 0.f;
+              }
+            }
+            pv[i] = p;
+            dv4[i] = d;
           }
-          if (!full && !vis) {
-            p = 0.f;
-            d = 0.f;
-          }
-          pv[i] = p;
-          dv4[i] = d;
+          wp[h2 * 2] = pack_bf16x2(pv[0], pv[1]);
+          wp[h2 * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
+          wd[h2 * 2] = pack_bf16x2(dv4[0], dv4[1]);
+          wd[h2 * 2 + 1] = pack_bf16x2(dv4[2], dv4[3]);
         }
-        wp[h2 * 2] = pack_bf16x2(pv[0], pv[1]);
-        wp[h2 * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
-        wd[h2 * 2] = pack_bf16x2(dv4[0], dv4[1]);
-        wd[h2 * 2 + 1] = pack_bf16x2(dv4[2], dv4[3]);
+        pa[kk] = __builtin_bit_cast(bf16x8, wp);
+        da[kk] = __builtin_bit_cast(bf16x8, wd);
       }
-      pa[kk] = __builtin_bit_cast(bf16x8, wp);
-      da[kk] = __builtin_bit_cast(bf16x8, wd);
+    };
+    // (a timestamp-filter step is never FULL and never TC)
+    if (!USE_T || tconst) {
+      if (full) epilogue(bc<true>(), bc<true>());
+      else epilogue(bc<false>(), bc<true>());
+    } else {
+      if (full) epilogue(bc<true>(), bc<false>());
+      else epilogue(bc<false>(), bc<false>());
     }
     // dV += P^T dO and dK += dS^T Q with dO and Q read transposed.
 #pragma unroll

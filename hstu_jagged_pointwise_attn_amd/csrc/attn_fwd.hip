@@ -243,6 +243,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     qmin = __builtin_amdgcn_readfirstlane(wave_min_u32(min(tq_r[0], tq_r[1])));
     qmax = __builtin_amdgcn_readfirstlane(wave_max_u32(max(tq_r[0], tq_r[1])));
   }
+  // The t2tab entries in a register too (lane c holds entry c).
+  float t2v = 0.f;
+  if (USE_T && has_rt && lane < 33) {
+    const int bkt = lane == 0 ? 0 : 32 - lane;
+    t2v = -kLog2e * a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1];
+  }
   // Keys [0, wave_hi) are the ones this wave's rows see: a key tile at or
   // beyond it (the upper half of a diagonal block, or a wave past the last
   // row) is skipped by this wave; its pairs are all masked.
@@ -347,13 +353,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       }
       const int blo = bucket_u32(dlo, a.n_tb), bhi = bucket_u32(dhi, a.n_tb);
       tconst = blo == bhi;
-      tcv = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t2tab[ffbh_u32(dlo) + 1])));
+      // t2tab entry ffbh(dlo) + 1 as a lane read (scalar index, no LDS round trip)
+      tcv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t2v), dlo ? __builtin_clz(dlo) + 1 : 0));
       // Two buckets: |dt| >= 2^bhi is bucket bhi, the rest blo (bhi may be
       // the clamped last bucket; blo is then below the clamp).
       two = bhi == blo + 1;
       if (two) {
         thr = 1u << bhi;
-        tcv_hi = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t2tab[32 - bhi])));
+        tcv_hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t2v), 32 - bhi));
       }
     }
 
@@ -539,8 +546,13 @@ __global__ __launch_bounds__(256 * f32_ksplit<D>()) void attn_fwd_f32_kernel(Fwd
     const int jend = min(BN, kv_limit - c0);
     // The four lanes of a row hold a quarter of q each; their partial dot
     // products are summed with two quad DPP moves (no LDS round trip).
+    // A fixed trip count (the body holds DPP moves, which keep a loop with
+    // a run-time count from being unrolled); keys past jend are skipped by a
+    // branch that is uniform in the wave.
 #pragma unroll 4
-    for (int jl = kgrp; jl < jend; jl += KSPLIT) {
+    for (int jj = 0; jj < BN / KSPLIT; ++jj) {
+      const int jl = kgrp + jj * KSPLIT;
+      if (jl >= jend) continue;
       const int j = c0 + jl;
       float s = 0.f;
 #pragma unroll
