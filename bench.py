@@ -588,6 +588,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay secondary measurement")
+    ap.add_argument("--tile-order", choices=["longest", "sequence"], default="longest",
+                    help="work-list order of the scheduler (hstu_set_tile_order)")
     ap.add_argument("--no-evict", action="store_true",
                     help="do not write the 512 MiB eviction buffer between timed steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle baseline")
@@ -610,6 +612,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    api.set_tile_order(api.HSTU_TILE_ORDER_BY_SEQUENCE if args.tile_order == "sequence"
+                       else api.HSTU_TILE_ORDER_LONGEST)
     wl = args.workload
     if wl == "batchprep":
         return bench_batchprep(args)
@@ -764,6 +768,7 @@ def main():
         "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded generators; no dataset)",
         "config": {"workload": WORKLOAD_TEXT[wl], "name": wl, "step": kind, **shape,
                    "useful_tflop_per_step": flops / 1e12, "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+                   "tile_order": args.tile_order,
                    "timing": ("median of per-step HIP event pairs, " +
                               ("no eviction" if args.no_evict else f"{EVICT_MIB} MiB written before each step")),
                    "step_ms_min_max": [min(step_ms), max(step_ms)],

@@ -84,6 +84,7 @@ SIGNATURES = {
     "hstu_get_device_status": ([_vp, _vp, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
     "hstu_kernel_timing": ([ctypes.c_int32], ctypes.c_int),
     "hstu_set_inline_schedule": ([ctypes.c_int32], ctypes.c_int32),
+    "hstu_set_tile_order": ([ctypes.c_int32], ctypes.c_int32),
     "hstu_kernel_timing_read": ([ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
                                  ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
     "hstu_stochastic_length": ([_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp, _vp,

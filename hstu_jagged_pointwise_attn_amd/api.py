@@ -302,6 +302,19 @@ def set_inline_schedule(enable: bool) -> bool:
     return bool(L.lib().hstu_set_inline_schedule(1 if enable else 0))
 
 
+HSTU_TILE_ORDER_LONGEST = 0
+HSTU_TILE_ORDER_BY_SEQUENCE = 1
+
+
+def set_tile_order(order: int) -> int:
+    """hstu_set_tile_order: the scheduler's work-list order (longest record
+    first, or by sequence). Returns the previous order."""
+    prev = int(L.lib().hstu_set_tile_order(int(order)))
+    if prev < 0:
+        raise ValueError(f"unknown tile order {order}")
+    return prev
+
+
 def kernel_timing_read(kernel: int):
     """hstu_kernel_timing_read: (total milliseconds, launches) of one kernel id."""
     ms, n = ctypes.c_double(0), ctypes.c_int64(0)

@@ -43,6 +43,12 @@ hstu_status_t hip_fail(hipError_t e, const char *what) {
     if (e_ != hipSuccess) return hip_fail(e_, what); \
   } while (0)
 
+// Whether small forwards build their tiles inside the attention kernel
+// (hstu_set_inline_schedule).
+std::atomic<int> g_inline_sched{1};
+// Work-list order of the scheduler kernel (hstu_set_tile_order).
+std::atomic<int> g_tile_order{kOrderLongest};
+
 // Optional per-launch event timing (hstu_kernel_timing).
 struct TimingRecord {
   int kernel;
@@ -241,6 +247,7 @@ void fill_sched(SchedArgs &s, const hstu_problem_t *p, int op, const Layout &L, 
   s.BN = t.BN;
   s.microbatch = microbatch;
   s.time_filter = (p->mask_flags & HSTU_MASK_CAND_TIME_FILTER) ? 1 : 0;
+  s.order = g_tile_order.load(std::memory_order_relaxed);
   s.max_tiles = (int)L.max_tiles;
   s.hdr = at<int>(ws, L.hdr);
   s.desc = at<SeqDesc>(ws, L.desc);
@@ -266,9 +273,6 @@ hstu_status_t check_mfalcon(const hstu_problem_t *cand, const int32_t *hist_offs
   return HSTU_OK;
 }
 
-// Whether small forwards build their tiles inside the attention kernel
-// (hstu_set_inline_schedule).
-std::atomic<int> g_inline_sched{1};
 
 // Per-call value that marks an inline-schedule forward's timestamp flag in
 // the workspace header; seeded from the clock so that a fresh workspace's
@@ -476,6 +480,17 @@ extern "C" {
 const char *hstu_version(void) { return "0.1.0"; }
 
 int32_t hstu_set_inline_schedule(int32_t enable) { return g_inline_sched.exchange(enable ? 1 : 0); }
+
+int32_t hstu_set_tile_order(int32_t order) {
+  if (order != HSTU_TILE_ORDER_LONGEST && order != HSTU_TILE_ORDER_BY_SEQUENCE) {
+    fail(HSTU_ERR_INVALID_ARG, "tile order %d", order);
+    return -1;
+  }
+  return g_tile_order.exchange(order == HSTU_TILE_ORDER_BY_SEQUENCE ? kOrderBySequence : kOrderLongest) ==
+                 kOrderBySequence
+             ? HSTU_TILE_ORDER_BY_SEQUENCE
+             : HSTU_TILE_ORDER_LONGEST;
+}
 
 const char *hstu_last_error(void) { return g_err.c_str(); }
 

@@ -495,8 +495,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }
     __syncthreads();
     // Diagonals above the next tile's window are complete: flush them.
-    if (USE_P && tid < BN) {
-      const int t = (pos_max - c0) - tid;
+    // (by the last wave: wave 0 stages the key times)
+    if (USE_P && tid >= NT - BN) {
+      const int t = (pos_max - c0) - (tid - (NT - BN));
       float *slot = &ring[t & (RING - 1)];
       float v = 0.f;
 #pragma unroll
@@ -726,7 +727,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       const int p0 = fr0 < sd.E ? fr0 : sd.E;
       pf.r = a.rab_p[pos_bucket(p0 - (k0 + BN - 1) + tid, a.n_pos)];
     }
-    if (USE_T && tid < BM) pf.t = a.ts[sd.q_base + min(fr0 + tid, L - 1)];
+    // row times by the last wave (waves 0-1 stage the rab_p window)
+    if (USE_T && tid >= 256 - BM) pf.t = a.ts[sd.q_base + min(fr0 + tid - (256 - BM), L - 1)];
   };
   auto store = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -737,13 +739,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       *(u32x4 *)(Os + buf * BM * ST + row * ST + col) = pf.b[c];
     }
     if (USE_P && tid < WIN) rabw[buf * WIN + tid] = pf.r;
-    if (USE_T && tid < BM) {
+    if (USE_T && tid >= 256 - BM) {  // exactly the last wave
+      const int j = tid - (256 - BM);
       const long long dr = pf.t - t_ref;
       bad_t |= dr < -2147483648LL || dr > 2147483647LL;
       const unsigned u = (unsigned)(dr + 2147483648LL);
-      trow[buf * BM + tid] = u;
+      trow[buf * BM + j] = u;
       const unsigned mn = wave_min_u32(u), mx = wave_max_u32(u);
-      if (tid == 0) {
+      if (j == 0) {
         trst[buf * 2] = mn;
         trst[buf * 2 + 1] = mx;
       }

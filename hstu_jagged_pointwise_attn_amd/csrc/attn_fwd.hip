@@ -61,7 +61,8 @@ __device__ __forceinline__ void fwd_load_tile(TilePrefetch<NCH> &pf, const FwdTi
     pf.v[i] = *(const u32x4 *)(c.V + g);
   }
   if (USE_P && c.tid < WIN) pf.r = c.rab_p[pos_bucket(c.pos_max - c0 - c.tid, c.n_pos)];
-  if (USE_T && c.tid < BN) pf.t = c.ts_kv[c.kv_base + min(c0 + c.tid, c.kv_limit - 1)];
+  // key times by the last wave (waves 0-2 stage the rab_p window)
+  if (USE_T && c.tid >= 256 - BN) pf.t = c.ts_kv[c.kv_base + min(c0 + c.tid - (256 - BN), c.kv_limit - 1)];
 }
 
 template <int D, int BN, bool USE_P, bool USE_T, int NCH>
@@ -77,13 +78,14 @@ __device__ __forceinline__ void fwd_store_tile(const TilePrefetch<NCH> &pf, int 
     *(u32x4 *)(Vb + row * VST + col) = pf.v[c];
   }
   if (USE_P && tid < WIN) rw[tid] = pf.r;
-  if (USE_T && tid < BN) {  // exactly wave 0
+  if (USE_T && tid >= 256 - BN) {  // exactly the last wave
+    const int j = tid - (256 - BN);
     const long long dk = pf.t - t_ref;
     bad_t |= dk < -2147483648LL || dk > 2147483647LL;
     const unsigned u = (unsigned)(dk + 2147483648LL);
-    tk[tid] = u;
+    tk[j] = u;
     const unsigned mn = wave_min_u32(u), mx = wave_max_u32(u);
-    if (tid == 0) {
+    if (j == 0) {
       tst[0] = mn;
       tst[1] = mx;
     }

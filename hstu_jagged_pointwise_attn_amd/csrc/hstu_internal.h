@@ -49,6 +49,13 @@ constexpr int kMaxKeyTiles = 16383;
 
 enum SchedMode { kSchedAttn = 0, kSchedMFalcon = 1, kSchedKeys = 2 };
 
+// Work-list orders (hstu_set_tile_order): longest record first, or whole
+// sequences longest first with each sequence's records together (its
+// longest first), which keeps a sequence's K/V (Q/dO for the key-major
+// pass) in one L2 while its records run. M-FALCON lists are always
+// longest first.
+enum TileOrder { kOrderLongest = 0, kOrderBySequence = 1 };
+
 // A forward of at most this many sequences and work units (query tiles x
 // heads, as bounded on the host) skips the scheduler launch: every attention
 // workgroup finds its own tile (sched_dev::inline_tile). At this size all
@@ -67,6 +74,7 @@ struct SchedArgs {
   int max_len, hist_max_len;
   int BM, BN, microbatch;
   int time_filter; // candidates see causal keys by timestamp: their causal tiles are never full
+  int order;       // kOrderLongest or kOrderBySequence (attention and key-major modes)
   int max_tiles;   // capacity of `tiles`; a larger count marks the offsets bad and runs nothing
   int *hdr;
   SeqDesc *desc;

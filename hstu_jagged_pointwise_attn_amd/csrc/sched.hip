@@ -169,6 +169,33 @@ __device__ void sort_keys(unsigned *keys, unsigned *tmp, int n2) {
   __syncthreads();
 }
 
+// Sort key of record g (ascending = run first). Longest first: (record
+// length descending, g). By sequence: (sequence length descending, then the
+// sequence's records longest first: g descending for query tiles, whose
+// length grows with the row, g ascending for key tiles, whose length shrinks
+// with the key). Lengths are in key (or query) tiles, below kMaxKeyTiles;
+// g < 2^18 (kSortCap).
+__device__ __forceinline__ unsigned sort_key(const SchedArgs &a, const SeqDesc &s, const QTile &r, int g) {
+  if (a.order != kOrderBySequence || a.mode == kSchedMFalcon)
+    return ((unsigned)(kMaxKeyTiles - r.nk) << 18) | (unsigned)g;
+  int len;
+  unsigned low;
+  if (a.mode == kSchedKeys) {
+    len = (s.qcount + a.BM - 1) / a.BM;  // the first key tile sees every query tile
+    low = (unsigned)g;
+  } else {
+    len = (frame_hi(s.q_frame0 + s.qcount - 1, s.P, s.E) + a.BN - 1) / a.BN;  // the last query tile's
+    low = 0x3ffffu - (unsigned)g;
+  }
+  len = min(len, kMaxKeyTiles);
+  return ((unsigned)(kMaxKeyTiles - len) << 18) | low;
+}
+
+__device__ __forceinline__ int key_index(const SchedArgs &a, unsigned key) {
+  const int low = (int)(key & 0x3ffffu);
+  return (a.order == kOrderBySequence && a.mode == kSchedAttn) ? 0x3ffff - low : low;
+}
+
 __device__ __forceinline__ void sched_body(const SchedArgs &a) {
   constexpr int kRecCache = kSchedThreads;  // records kept in LDS for short lists
   __shared__ int s_qoff[kMaxSeqs + 1];
@@ -244,7 +271,7 @@ __device__ __forceinline__ void sched_body(const SchedArgs &a) {
     SeqDesc s = seq_info(a, lo, &bits);
     QTile r = make_tile(a, s, lo, g - s_qoff[lo]);
     if (cached) s_rec[g] = r;
-    if (sorted) s_keys[g] = ((unsigned)(kMaxKeyTiles - r.nk) << 18) | (unsigned)g;
+    if (sorted) s_keys[g] = sort_key(a, s, r, g);
     else a.tiles[g] = r;
   }
   __syncthreads();
@@ -267,7 +294,7 @@ __device__ __forceinline__ void sched_body(const SchedArgs &a) {
   else sort_keys<8>(s_keys, s_tmp, n2);
 
   for (int r = tid; r < NQ; r += kSchedThreads) {
-    int g = (int)(s_keys[r] & 0x3ffffu);
+    const int g = key_index(a, s_keys[r]);
     if (cached) {
       a.tiles[r] = s_rec[g];
       continue;

@@ -309,6 +309,27 @@ hstu_status_t hstu_kernel_timing_read(int32_t kernel, double *total_ms, int64_t 
 int32_t hstu_set_inline_schedule(int32_t enable);
 
 /*
+ * Order of the scheduler's work lists (the forward's and the backward's
+ * query tiles and the backward's key tiles; M-FALCON lists are always
+ * longest first):
+ *   HSTU_TILE_ORDER_LONGEST      longest record first (the default), which
+ *                                balances the chip best;
+ *   HSTU_TILE_ORDER_BY_SEQUENCE  whole sequences, longest first, each
+ *                                sequence's records together and longest
+ *                                first, so that its K/V (Q/dO for the key
+ *                                pass) stays in one L2 while they run: far
+ *                                fewer L2 refills, for a few percent more
+ *                                time when the GPU has the memory system to
+ *                                itself.
+ * Outputs do not depend on the order (d rab and the affine gradients up to
+ * the order of their atomic sums). Process-wide, host only; returns the
+ * previous order, or -1 (HSTU_ERR_INVALID_ARG in hstu_last_error) for an
+ * unknown one.
+ */
+enum { HSTU_TILE_ORDER_LONGEST = 0, HSTU_TILE_ORDER_BY_SEQUENCE = 1 };
+int32_t hstu_set_tile_order(int32_t order);
+
+/*
  * Stochastic Length (HSTU blog, section 3.4: training sequences are sampled
  * down to a length budget, 4096 -> about 776 at alpha = 1.6). Device side,
  * no host round trip. For every sequence b of the input batch (offsets [B+1],

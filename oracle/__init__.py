@@ -2,9 +2,9 @@
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package. It wraps ``oracle.c`` (plain fp64 loops,
-OpenMP over (sequence, head)) through ctypes and adds two small pieces of pure
-Python: the tile schedule built from the brute-force tile classifier and the
-longest-first (LPT) ordering of query tiles.
+OpenMP over (sequence, head)) through ctypes and adds small pieces of pure
+Python: the tile schedule built from the brute-force tile classifier, and the
+two orders of the query tiles (longest first, and by sequence).
 
 Everything here takes numpy arrays; floating-point inputs are converted to
 float64 (bf16 and fp32 values are represented exactly). Nothing here imports
@@ -248,6 +248,18 @@ def lpt_order(entries):
     """Longest-processing-time order: by number of present key tiles,
     descending; ties keep the canonical order."""
     return sorted(range(len(entries)), key=lambda g: (-int(np.count_nonzero(entries[g]["kinds"])), g))
+
+
+def sequence_order(entries):
+    """The by-sequence order of a query-tile schedule: whole sequences by
+    their longest tile (present key tiles), descending; within a sequence its
+    tiles longest first; sequences of equal length later-index first (the
+    tile index breaks every tie, descending)."""
+    nk = [int(np.count_nonzero(e["kinds"])) for e in entries]
+    seq_len = {}
+    for g, e in enumerate(entries):
+        seq_len[e["b"]] = max(seq_len.get(e["b"], 0), nk[g])
+    return sorted(range(len(entries)), key=lambda g: (-seq_len[entries[g]["b"]], -g))
 
 
 def stochastic_length(offsets, keys, cap):

@@ -245,3 +245,13 @@ def test_static_forward_rejects_oversized_problem(L):
     st = lib.hstu_attn_fwd_static(ctypes.byref(p), *([dummy] * 8), None)
     assert st == L.HSTU_ERR_WORKSPACE
     assert b"static scratch" in lib.hstu_last_error()
+
+
+def test_tile_order_switch(L):
+    """hstu_set_tile_order (host only): returns the previous order and
+    rejects unknown ones without changing the setting."""
+    f = L.lib().hstu_set_tile_order
+    assert f(1) == 0
+    assert f(7) == -1
+    assert f(0) == 1
+    assert f(0) == 0

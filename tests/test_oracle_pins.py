@@ -445,6 +445,24 @@ def test_lpt_order_is_stable_longest_first(oracle_mod):
             assert a < b
 
 
+def test_sequence_order_groups_sequences_longest_first(oracle_mod):
+    # lengths in key tiles of 64: 3, 1, 3, 5 (the last sequence's last tile
+    # sees 5 key tiles), plus an empty sequence
+    ent = oracle_mod.schedule([0, 130, 150, 150, 330, 600], 64, 64)
+    order = oracle_mod.sequence_order(ent)
+    assert sorted(order) == list(range(len(ent)))
+    seqs = [ent[g]["b"] for g in order]
+    # each sequence's tiles are contiguous
+    runs = [b for i, b in enumerate(seqs) if i == 0 or seqs[i - 1] != b]
+    assert len(runs) == len(set(runs))
+    # hand-computed: sequence 4 (5 key tiles) first, then 3 and 0 (3 each;
+    # the later index first), then 1; within a sequence the longest tile first
+    assert runs == [4, 3, 0, 1]
+    for b in runs:
+        rows = [ent[g]["row0"] for g in order if ent[g]["b"] == b]
+        assert rows == sorted(rows, reverse=True)
+
+
 # ------------------------------------------------------------------ inputs
 
 def test_stochastic_length_cap_matches_page():
