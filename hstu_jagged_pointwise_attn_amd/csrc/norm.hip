@@ -45,6 +45,14 @@ struct Vec<true> {
       x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
     }
   }
+  __device__ static void unpack(const uint4 &v, float *x) {
+    const u32 *w = (const u32 *)&v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(w[e] << 16);
+      x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
   __device__ static void store(void *p, long long off, const float *x) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     uint4 v;
@@ -65,6 +73,10 @@ struct Vec<false> {
   __device__ static void load(const void *p, long long off, float *x) {
     const float4 v = *(const float4 *)((const float *)p + off);
     x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  }
+  __device__ static void unpack(const uint4 &v, float *x) {
+    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
   }
   __device__ static void store(void *p, long long off, const float *x) {
     *(float4 *)((float *)p + off) = float4{x[0], x[1], x[2], x[3]};
@@ -227,17 +239,72 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
       }
     }
   };
+  // The next token's rows (16-byte chunks) and statistics are requested
+  // before the current one is computed, so a wave keeps one token in flight
+  // (rows of up to 16 chunks per lane; wider rows would spill).
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr bool PREFETCH = MAXCH <= 2;
+  constexpr int RC = PREFETCH ? MAXCH : 1;
+  uint4 rx[RC], rdy[RC], ru[RC];
+  float nmean = 0.f, nrstd = 1.f;
+  int ngrp = 0;
+  auto fetch = [&](long long t) __attribute__((always_inline)) {
+    const long long row = t * D;
+#pragma unroll
+    for (int k = 0; k < RC; ++k) {
+      const int ch = lane + 64 * k;
+      if (ch < nch) {
+        const long long off = (row + ch * N) * ESZ;
+        rx[k] = *(const uint4 *)((const char *)a.X + off);
+        rdy[k] = *(const uint4 *)((const char *)a.dY + off);
+        ru[k] = *(const uint4 *)((const char *)a.U + off);
+      }
+    }
+    if (a.mode != HSTU_NORM_NONE) {
+      nmean = a.mean[t];
+      nrstd = a.rstd[t];
+      if (a.mode == HSTU_NORM_GLN) ngrp = a.group[t];
+    }
+  };
+  if constexpr (PREFETCH) {
+    if (t0 < t1) fetch(t0);
+  }
   for (long long t = t0; t < t1; ++t) {
     const long long row = t * D;
     float x[MAXCH][N], dy[MAXCH][N], u[MAXCH][N];
+    float mean = 1.f, rstd = 1.f;
+    int grp_t = 0;
+    if constexpr (PREFETCH) {
 #pragma unroll
-    for (int k = 0; k < MAXCH; ++k) {
-      const int ch = lane + 64 * k;
-      if (ch < nch) {
-        V::load(a.X, row + ch * N, x[k]);
-        V::load(a.dY, row + ch * N, dy[k]);
-        V::load(a.U, row + ch * N, u[k]);
+      for (int k = 0; k < RC; ++k) {
+        const int ch = lane + 64 * k;
+        if (ch < nch) {
+          V::unpack(rx[k], x[k]);
+          V::unpack(rdy[k], dy[k]);
+          V::unpack(ru[k], u[k]);
+        }
       }
+      mean = nmean;
+      rstd = nrstd;
+      grp_t = ngrp;
+    } else {
+#pragma unroll
+      for (int k = 0; k < MAXCH; ++k) {
+        const int ch = lane + 64 * k;
+        if (ch < nch) {
+          V::load(a.X, row + ch * N, x[k]);
+          V::load(a.dY, row + ch * N, dy[k]);
+          V::load(a.U, row + ch * N, u[k]);
+        }
+      }
+      if (a.mode != HSTU_NORM_NONE) {
+        mean = a.mean[t];
+        rstd = a.rstd[t];
+        if (a.mode == HSTU_NORM_GLN) grp_t = a.group[t];
+      }
+    }
+    if constexpr (PREFETCH) {
+      if (t + 1 < t1) fetch(t + 1);
     }
     if (a.mode == HSTU_NORM_NONE) {
 #pragma unroll
@@ -256,10 +323,9 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
       }
       continue;
     }
-    const float mean = a.mean[t], rstd = a.rstd[t];
     int g = 0;
     if (a.mode == HSTU_NORM_GLN) {
-      g = a.group[t];
+      g = grp_t;
       if (g >= a.n_groups) g = -1;
     }
     const float *gm = (g >= 0 && a.gamma) ? a.gamma + (long long)g * D : nullptr;
