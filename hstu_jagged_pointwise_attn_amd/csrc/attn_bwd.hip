@@ -11,9 +11,9 @@
 // Two passes, no atomics on dQ/dK/dV:
 //  * query-major (dq kernel): the forward's loop with dO next to Q in
 //    registers; per key tile S^T = bias + K Q^T and dP^T = V dO^T, then
-//    dS and dQ += dS K (K read transposed from LDS). It also accumulates
-//    d rab in LDS (rab_p by signed diagonal pos_i - j, reduced per wave
-//    through a skewed LDS block and kept in a ring that slides with the key
+//    dS and dQ += dS K (K read transposed from LDS). It also sums d rab
+//    (rab_p by signed diagonal pos_i - j, reduced per wave in registers or
+//    through a skewed LDS block and kept in rings that slide with the key
 //    tiles; rab_t by bucket) and handles a candidate's pair with itself,
 //    including the candidate rows of dK and dV, which no other row sees.
 //  * key-major (dkdv kernel): per tile of 64 non-candidate keys, K and V in
@@ -49,14 +49,16 @@ struct PairPrefetch {
 // dQ kernel (query-major): the forward's 128-row query tiles, 4 waves x 32
 // rows (Q and dO of a lane's two rows stay in registers), key tiles of 32.
 //
-// d rab_p: each wave writes its 32 x 32 block of dS into a private LDS area
-// with row r shifted left by its position offset s_r (so column c holds the
-// diagonal pos_i - j = pos_w0 - c0 + 31 - c); one column sum per lane then
-// gives the wave's diagonal sums, which go into a per-workgroup ring indexed
-// by the signed diagonal. Cells outside a row's 32 written columns stay zero
-// for the whole query tile, because the shifts do not change between key
-// tiles. Diagonals that no later key tile can touch are flushed to global
-// memory after every tile.
+// d rab_p: without candidates (every row at its own position) a wave's
+// 32 x 32 block of dS is reduced to diagonal sums in registers by DPP row
+// shifts (DIAG_DPP, below). With candidates (positions repeat) each wave
+// writes the block into a private LDS area with row r shifted left by its
+// position offset s_r (so column c holds the diagonal
+// pos_i - j = pos_w0 - c0 + 31 - c), and one column sum per lane gives the
+// diagonal sums; cells outside a row's 32 written columns stay zero for the
+// whole query tile, because the shifts do not change between key tiles.
+// The sums go into rings indexed by the signed diagonal; diagonals that no
+// later key tile can touch are flushed to global memory after every tile.
 // ---------------------------------------------------------------------------
 template <int D, bool USE_P, bool USE_T, bool TF, bool DIAG_DPP>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
