@@ -178,6 +178,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     qmin = __builtin_amdgcn_readfirstlane(wave_min_u32(min(tq[0], tq[1])));
     qmax = __builtin_amdgcn_readfirstlane(wave_max_u32(max(tq[0], tq[1])));
   }
+  // Keys [0, wave_hi) are the ones this wave's rows see: a key tile at or
+  // beyond it (the upper part of the diagonal block, or a wave past the last
+  // row) has only masked pairs for this wave, which skips its work on it
+  // (the tiles come in increasing order, so once skipped always skipped).
+  const int wave_hi = __builtin_amdgcn_readfirstlane(
+      (int)wave_max_u32((unsigned)max(hi_r[0], hi_r[1])));
   // Whether some row of this wave is a candidate under the timestamp filter.
   const bool wave_tf = TF && __builtin_amdgcn_readfirstlane(
       (int)wave_max_u32((tfr[0] || tfr[1]) ? 1u : 0u)) != 0;
@@ -298,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     store(0);
     if (nk > 1) load(1);
     __syncthreads();
-    gemms(0);
+    if (wave_hi > 0) gemms(0);
   }
   for (int kt = 0; kt < nk; ++kt) {
     const int b = kt & 1;
@@ -443,9 +449,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       }
       if (USE_T && !TC && !T2 && run_b >= 0) atomicAdd(&hts[run_b], run_s);
     };
-    bool done = false;
+    bool done = c0 >= wave_hi;  // nothing this wave sees
     if constexpr (TF) {
-      if (wave_tf && !full) {
+      if (!done && wave_tf && !full) {
         epilogue(bc<false>(), bc<false>(), bc<true>(), bc<false>());
         done = true;
       }
@@ -462,7 +468,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         else epilogue(bc<false>(), bc<true>(), bc<false>(), bc<false>());
       }
     }
-    if (USE_P && !wave_dpp) {
+    if (USE_P && !wave_dpp && c0 < wave_hi) {
       // column sums of the skewed block = this wave's diagonal sums
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -478,7 +484,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       __builtin_amdgcn_wave_barrier();
     }
     // dQ += dS K with K read transposed from its row-major tile.
-    {
+    if (c0 < wave_hi) {
       const u16 *kbuf = Ks + b * BN * ST;
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) {
@@ -509,7 +515,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       }
       if (v != 0.f) atomicAdd(a.drab_p + pos_bucket(t, a.n_pos), v * a.inv_nmax);
     }
-    if (kt + 1 < nk) gemms(b ^ 1);
+    if (kt + 1 < nk && c0 + BN < wave_hi) gemms(b ^ 1);
   }
   if (USE_P && nk > 0 && tid < WIN - BN) {
     // the rest of the last window: diagonals [pos_max - c_last - 159, pos_max - c_last - 32]
