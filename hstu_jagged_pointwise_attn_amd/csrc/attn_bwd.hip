@@ -782,10 +782,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       // bias of element (mr, i): rabw[min(A + 16 mr + i, Bc)]
       const int tlo = (fr0 < sd.E ? fr0 : sd.E) - (k0 + BN - 1);
       const int A = fr0 + lg * 4 - key - tlo, Bc = sd.E - key - tlo;
+      if (fr0 + BM <= sd.E) {
+        // every row of the step sits at its own position: no clamp, so the
+        // sixteen reads share one address and take immediate offsets
+        const float *rw = rabw + b * WIN + A;
 #pragma unroll
-      for (int mr = 0; mr < 4; ++mr)
+        for (int mr = 0; mr < 4; ++mr)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[mr][i] = rabw[b * WIN + min(A + mr * 16 + i, Bc)];
+          for (int i = 0; i < 4; ++i) s[mr][i] = rw[mr * 16 + i];
+      } else {
+#pragma unroll
+        for (int mr = 0; mr < 4; ++mr)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[mr][i] = rabw[b * WIN + min(A + mr * 16 + i, Bc)];
+      }
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
