@@ -714,21 +714,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   PairPrefetch<NCH> pf;
   pf.r = 0.f;
   pf.t = 0;
-  // rows [fr0, fr0 + 64) of the frame; rows past the end load as zeros.
+  // Byte offset of this thread's chunk c inside a step's rows: the same in
+  // every step (the buffer base moves instead).
+  unsigned coff[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int chunk = tid + c * 256;
+    coff[c] = (unsigned)(((chunk / CH) * ld + h * D + (chunk % CH) * 8) * 2);
+  }
+  // rows [fr0, fr0 + 64) of the frame; rows past the end load as zeros
+  // (they fall outside the buffer, which ends at the sequence's last row).
   auto load = [&](int qt) __attribute__((always_inline)) {
     const int fr0 = qt * BM;
+    const long long rb = (long long)(sd.q_base + fr0) * ld;
+    const long long nb = (long long)(L - fr0) * ld * 2;
+    const __amdgpu_buffer_rsrc_t qr = buf_view(Q + rb, nb), gr = buf_view(dO + rb, nb);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int chunk = tid + c * 256;
-      const int row = chunk / CH, col = (chunk % CH) * 8;
-      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-      if (fr0 + row < L) {
-        const long long g = (long long)(sd.q_base + fr0 + row) * ld + h * D + col;
-        x = *(const u32x4 *)(Q + g);
-        y = *(const u32x4 *)(dO + g);
-      }
-      pf.a[c] = x;
-      pf.b[c] = y;
+      pf.a[c] = buf_load16(qr, coff[c]);
+      pf.b[c] = buf_load16(gr, coff[c]);
     }
     if (USE_P && tid < WIN) {
       // window of t = pos(row) - key: t_lo = pos(fr0) - (k0 + 63)

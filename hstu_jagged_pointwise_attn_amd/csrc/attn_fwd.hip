@@ -36,6 +36,7 @@ struct TilePrefetch {
   u32x4 k[NCH], v[NCH];
   float r;
   long long t;
+  unsigned off[NCH];  // byte offset of this thread's chunks inside a tile (fixed)
 };
 
 // Per-workgroup constants of the key loop.
@@ -51,14 +52,14 @@ template <int D, int BN, bool USE_P, bool USE_T, int NCH>
 __device__ __forceinline__ void fwd_load_tile(TilePrefetch<NCH> &pf, const FwdTileCtx &c, int t) {
   constexpr int CH = D / 8, WIN = kFwdBM + BN;
   const int c0 = t * BN;
+  // keys past kv_limit (seen by no row here) fall outside the buffers and load as zeros
+  const long long rb = (long long)(c.kv_base + c0) * c.ld;
+  const long long nb = (long long)(c.kv_limit - c0) * c.ld * 2;
+  const __amdgpu_buffer_rsrc_t kr = buf_view(c.K + rb, nb), vr = buf_view(c.V + rb, nb);
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int chunk = c.tid + i * 256;
-    const int row = chunk / CH, col = (chunk % CH) * 8;
-    const int key = min(c0 + row, c.kv_limit - 1);
-    const long long g = (long long)(c.kv_base + key) * c.ld + c.hd + col;
-    pf.k[i] = *(const u32x4 *)(c.K + g);
-    pf.v[i] = *(const u32x4 *)(c.V + g);
+    pf.k[i] = buf_load16(kr, pf.off[i]);
+    pf.v[i] = buf_load16(vr, pf.off[i]);
   }
   if (USE_P && c.tid < WIN) pf.r = c.rab_p[pos_bucket(c.pos_max - c0 - c.tid, c.n_pos)];
   // key times by the last wave (waves 0-2 stage the rab_p window)
@@ -264,6 +265,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   TilePrefetch<NCH> pf;
   pf.r = 0.f;
   pf.t = 0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int chunk = tid + i * 256;
+    pf.off[i] = (unsigned)(((chunk / (D / 8)) * ld + h * D + (chunk % (D / 8)) * 8) * 2);
+  }
   FwdTileCtx cx;
   cx.K = K; cx.V = V; cx.rab_p = a.rab_p; cx.ts_kv = a.ts_kv; cx.ld = ld;
   cx.kv_base = sd.kv_base; cx.kv_limit = kv_limit; cx.hd = h * D; cx.pos_max = pos_max;

@@ -106,6 +106,22 @@ __device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(u32, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// A raw buffer resource over [p, p + bytes) (bytes clamped to [0, 2^32 - 1];
+// word 3 is the gfx9 raw-dword format). A load whose 32-bit byte offset runs
+// past the end returns zeros without touching memory, so a tile's rows past
+// the end of a sequence need no branch, no zero fill and no clamped index, and
+// the per-lane offsets inside a tile stay fixed while the base moves.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_view(const void *p, long long bytes) {
+  const long long n = bytes < 0 ? 0 : (bytes > 0xffffffffLL ? 0xffffffffLL : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)(unsigned)n, 0x00020000);
+}
+
+// 16 bytes at byte offset off (all of it in the vector offset, which is the
+// part the range check sees).
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 
 }  // namespace dev
 }  // namespace hstu
