@@ -896,16 +896,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       if (full) epilogue(bc<true>(), bc<false>());
       else epilogue(bc<false>(), bc<false>());
     }
-    // dV += P^T dO and dK += dS^T Q with dO and Q read transposed.
+    // dV += P^T dO and dK += dS^T Q with dO and Q read transposed; the
+    // fragment reads run GD steps ahead of their MFMAs in a ring.
+    {
+      constexpr int NI = 2 * ND, GD = 2;
+      const int base = (lg * 4 + (lr >> 2)) * ST + (lr & 3) * 4;
+      s16x4 ro0[GD], ro1[GD], rq0[GD], rq1[GD];
+      auto rd = [&](int i) __attribute__((always_inline)) {
+        const int off = base + (i / ND) * 32 * ST + (i % ND) * 16;
+        ro0[i % GD] = lds_read_tr16(ob + off);
+        ro1[i % GD] = lds_read_tr16(ob + off + 16 * ST);
+        rq0[i % GD] = lds_read_tr16(qb + off);
+        rq1[i % GD] = lds_read_tr16(qb + off + 16 * ST);
+      };
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+      for (int i = 0; i < GD; ++i) rd(i);
 #pragma unroll
-      for (int nd = 0; nd < ND; ++nd) {
-        const int off = (kk * 32 + lg * 4 + (lr >> 2)) * ST + nd * 16 + (lr & 3) * 4;
-        const s16x4 o0 = lds_read_tr16(ob + off), o1 = lds_read_tr16(ob + off + 16 * ST);
-        const s16x4 q0 = lds_read_tr16(qb + off), q1 = lds_read_tr16(qb + off + 16 * ST);
+      for (int i = 0; i < NI; ++i) {
+        const s16x4 o0 = ro0[i % GD], o1 = ro1[i % GD], q0 = rq0[i % GD], q1 = rq1[i % GD];
         const bf16x8 ot = __builtin_bit_cast(bf16x8, s16x8{o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]});
         const bf16x8 qt = __builtin_bit_cast(bf16x8, s16x8{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]});
+        if (i + GD < NI) rd(i + GD);
+        const int kk = i / ND, nd = i % ND;
         dv[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[kk], ot, dv[nd], 0, 0, 0);
         dk[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[kk], qt, dk[nd], 0, 0, 0);
       }

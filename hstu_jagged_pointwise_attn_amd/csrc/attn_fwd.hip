@@ -308,17 +308,43 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  // O += P V with V read transposed from its row-major LDS tile.
+  // O += P V with V read transposed from its row-major LDS tile. The 2 x ND
+  // fragment reads run PVD steps ahead of their MFMAs in a ring, so that no
+  // step waits for a whole batch of reads to drain (not with the timestamp
+  // filter, whose extra state leaves no registers for it).
   auto pv = [&](int buf) __attribute__((always_inline)) {
-    const u16 *vb = Vs + buf * BN * VST;
+    const u16 *vb = Vs + buf * BN * VST + (lg * 4 + (lr >> 2)) * VST + (lr & 3) * 4;
+    if constexpr (TF) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-      for (int nd = 0; nd < ND; ++nd) {
-        const u16 *p0 = vb + (kk * 32 + lg * 4 + (lr >> 2)) * VST + nd * 16 + (lr & 3) * 4;
-        const s16x4 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * VST);
+        for (int nd = 0; nd < ND; ++nd) {
+          const u16 *p0 = vb + kk * 32 * VST + nd * 16;
+          const s16x4 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * VST);
+          const bf16x8 vbf = __builtin_bit_cast(
+              bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+          for (int nq = 0; nq < 2; ++nq)
+            acc[nq][nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[nq][kk], vbf, acc[nq][nd], 0, 0, 0);
+        }
+      }
+    } else {
+      constexpr int NI = 2 * ND, PVD = 4;
+      s16x4 rlo[PVD], rhi[PVD];
+      auto rd = [&](int i) __attribute__((always_inline)) {
+        const u16 *p0 = vb + (i / ND) * 32 * VST + (i % ND) * 16;
+        rlo[i % PVD] = lds_read_tr16(p0);
+        rhi[i % PVD] = lds_read_tr16(p0 + 16 * VST);
+      };
+#pragma unroll
+      for (int i = 0; i < PVD; ++i) rd(i);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const s16x4 lo = rlo[i % PVD], hi = rhi[i % PVD];
         const bf16x8 vbf = __builtin_bit_cast(
             bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        if (i + PVD < NI) rd(i + PVD);
+        const int kk = i / ND, nd = i % ND;
 #pragma unroll
         for (int nq = 0; nq < 2; ++nq)
           acc[nq][nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[nq][kk], vbf, acc[nq][nd], 0, 0, 0);
