@@ -397,7 +397,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
             if (USE_P && !wave_dpp) skw[(nq * 16 + lr) * SKW + mk * 16 + lg * 4 + i + 31 - sh_r[nq]] = ds;
             if (USE_T) {
               if (TC || T2) {
-                tsum += ds;
+                if (!(USE_P && wave_dpp)) tsum += ds;  // else from the diagonal sums below
                 if (T2) tsum_hi += hi ? ds : 0.f;
               } else {
                 if (tix != run_b) {
@@ -420,6 +420,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         dsa[nq] = __builtin_bit_cast(bf16x8, wds);
       }
       if (USE_P && wave_dpp) {
+        // every dS of the block sits in exactly one lane's four diagonal sums,
+        // so their total is the block's sum for a one- or two-bucket rab_t
+        if (USE_T && (TC || T2)) tsum = (dacc[0] + dacc[1]) + (dacc[2] + dacc[3]);
         const int dbase = pos_w0 - c0 + lr - 4 * lg + 16;
         float *rg = ring + (w * 4 + lg) * RSTR;
         float old[4];
@@ -483,15 +486,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_wave_barrier();
     }
-    // dQ += dS K with K read transposed from its row-major tile.
+    // dQ += dS K with K read transposed from its row-major tile; the
+    // fragment reads run QD steps ahead of their MFMAs in a ring.
     if (c0 < wave_hi) {
-      const u16 *kbuf = Ks + b * BN * ST;
+      const u16 *kbuf = Ks + b * BN * ST + (lg * 4 + (lr >> 2)) * ST + (lr & 3) * 4;
+      constexpr int QD = ND < 4 ? ND : 4;
+      s16x4 rlo[QD], rhi[QD];
+      auto rd = [&](int nd) __attribute__((always_inline)) {
+        rlo[nd % QD] = lds_read_tr16(kbuf + nd * 16);
+        rhi[nd % QD] = lds_read_tr16(kbuf + nd * 16 + 16 * ST);
+      };
+#pragma unroll
+      for (int nd = 0; nd < QD; ++nd) rd(nd);
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) {
-        const u16 *p0 = kbuf + (lg * 4 + (lr >> 2)) * ST + nd * 16 + (lr & 3) * 4;
-        const s16x4 lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 16 * ST);
+        const s16x4 lo = rlo[nd % QD], hi = rhi[nd % QD];
         const bf16x8 kb = __builtin_bit_cast(
             bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        if (nd + QD < ND) rd(nd + QD);
 #pragma unroll
         for (int nq = 0; nq < 2; ++nq)
           acc[nq][nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[nq], kb, acc[nq][nd], 0, 0, 0);
