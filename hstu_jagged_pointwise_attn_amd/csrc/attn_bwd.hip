@@ -360,7 +360,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       const int prel = sd.P - (c0 + lg * 4);
       float tsum = 0.f, tsum_hi = 0.f, run_s = 0.f;
       int run_b = -1;
-      float dacc[4] = {0.f, 0.f, 0.f, 0.f};
+      float dacc[4] = {-0.f, -0.f, -0.f, -0.f};  // -0: the first add is exact and folds away
 #pragma unroll
       for (int nq = 0; nq < 2; ++nq) {
         u32x4 wds;

@@ -85,11 +85,14 @@ __device__ __forceinline__ unsigned wave_ext_u32(unsigned v) {
 __device__ __forceinline__ unsigned wave_min_u32(unsigned v) { return wave_ext_u32<false>(v); }
 __device__ __forceinline__ unsigned wave_max_u32(unsigned v) { return wave_ext_u32<true>(v); }
 
-// Wave-wide fp32 sum by the same DPP pattern (every lane active).
+// A DPP lane move of an fp32 value; a lane whose source lies outside its row
+// (row shifts) reads 0 (bound_ctrl), so no zeroed destination is needed.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
+
+// Wave-wide fp32 sum by the same DPP pattern (every lane active).
 __device__ __forceinline__ float wave_sum_f32(float v) {
   v += dpp_f32<0xB1>(v);
   v += dpp_f32<0x4E>(v);
