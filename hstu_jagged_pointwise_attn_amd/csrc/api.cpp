@@ -59,10 +59,10 @@ bool g_timing_on = false;
 std::vector<TimingRecord> g_timing;
 
 void timing_clear_locked() {
-  for (auto &r : g_timing) {
-    hipEventSynchronize(r.stop);
-    hipEventDestroy(r.start);
-    hipEventDestroy(r.stop);
+  for (auto &r : g_timing) {  // clean-up: a failure here leaves nothing to undo
+    (void)hipEventSynchronize(r.stop);
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
   }
   g_timing.clear();
 }
@@ -77,17 +77,23 @@ struct Timed {
     if (!g_timing_on) return;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
-    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
-      a = b = nullptr;
-      return;
-    }
-    hipEventRecord(a, st);
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess ||
+        hipEventRecord(a, st) != hipSuccess)
+      drop();
   }
   ~Timed() {
     if (!a) return;
-    hipEventRecord(b, st);
+    if (hipEventRecord(b, st) != hipSuccess) {  // no record of this launch
+      drop();
+      return;
+    }
     std::lock_guard<std::mutex> g(g_timing_mu);
     g_timing.push_back({kernel, a, b});
+  }
+  void drop() {
+    if (a) (void)hipEventDestroy(a);
+    if (b) (void)hipEventDestroy(b);
+    a = b = nullptr;
   }
 };
 
@@ -1086,25 +1092,25 @@ hstu_status_t hstu_stack_score_capture(const hstu_problem_t *cand, int32_t n_lay
   HIP_TRY(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "stream create");
   hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
   if (e != hipSuccess) {
-    hipStreamDestroy(cs);
+    (void)hipStreamDestroy(cs);
     return hip_fail(e, "begin capture");
   }
   s = hstu_stack_score(cand, n_layers, layers, hist_offsets, hist_tokens, hist_max_len, hist_ts, microbatch, Xc, Out,
                        ws, ws_bytes, cs);
   hipGraph_t g = nullptr;
   e = hipStreamEndCapture(cs, &g);
-  hipStreamDestroy(cs);
+  (void)hipStreamDestroy(cs);  // clean-up of a stream of our own; its error changes nothing
   if (s) {
-    if (g) hipGraphDestroy(g);
+    if (g) (void)hipGraphDestroy(g);
     return s;
   }
   if (e != hipSuccess) {
-    if (g) hipGraphDestroy(g);
+    if (g) (void)hipGraphDestroy(g);
     return hip_fail(e, "end capture");
   }
   hipGraphExec_t ex = nullptr;
   e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
-  hipGraphDestroy(g);
+  (void)hipGraphDestroy(g);
   if (e != hipSuccess) return hip_fail(e, "graph instantiate");
   *graph = ex;
   return HSTU_OK;
@@ -1156,8 +1162,8 @@ hstu_status_t hstu_kernel_timing_read(int32_t kernel, double *total_ms, int64_t 
     HIP_TRY(hipEventElapsedTime(&e, r.start, r.stop), "event elapsed time");
     ms += e;
     n++;
-    hipEventDestroy(r.start);
-    hipEventDestroy(r.stop);
+    (void)hipEventDestroy(r.start);  // read; a failed destroy leaves nothing to undo
+    (void)hipEventDestroy(r.stop);
   }
   g_timing.swap(keep);
   *total_ms = ms;

@@ -45,12 +45,12 @@ struct FwdTileCtx {
   const float *rab_p;
   const int64_t *ts_kv;
   long long ld;
-  int kv_base, kv_limit, hd, pos_max, n_pos, tid;
+  int kv_base, kv_limit, pos_max, n_pos, tid;
 };
 
 template <int D, int BN, bool USE_P, bool USE_T, int NCH>
 __device__ __forceinline__ void fwd_load_tile(TilePrefetch<NCH> &pf, const FwdTileCtx &c, int t) {
-  constexpr int CH = D / 8, WIN = kFwdBM + BN;
+  constexpr int WIN = kFwdBM + BN;
   const int c0 = t * BN;
   // keys past kv_limit (seen by no row here) fall outside the buffers and load as zeros
   const long long rb = (long long)(c.kv_base + c0) * c.ld;
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   }
   FwdTileCtx cx;
   cx.K = K; cx.V = V; cx.rab_p = a.rab_p; cx.ts_kv = a.ts_kv; cx.ld = ld;
-  cx.kv_base = sd.kv_base; cx.kv_limit = kv_limit; cx.hd = h * D; cx.pos_max = pos_max;
+  cx.kv_base = sd.kv_base; cx.kv_limit = kv_limit; cx.pos_max = pos_max;
   cx.n_pos = a.n_pos; cx.tid = tid;
   f32x4 acc[2][ND];
 #pragma unroll

@@ -204,18 +204,19 @@ int gemm_rm(const GemmRM &g, void *ws, size_t ws_bytes, hipStream_t stream) {
       float best = 1e30f;
       for (const Choice &c : cands) {
         if (run(c) != HIPBLAS_STATUS_SUCCESS) continue;  // warm-up; skip what fails
-        hipEventRecord(e0, stream);
+        bool timed = hipEventRecord(e0, stream) == hipSuccess;
         for (int r = 0; r < kTuneRuns; ++r) run(c);
-        hipEventRecord(e1, stream);
+        timed = timed && hipEventRecord(e1, stream) == hipSuccess;
         float ms = 0.f;
-        if (hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess && ms < best) {
+        if (timed && hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess &&
+            ms < best) {
           best = ms;
           ch = c;
         }
       }
     }
-    if (e0) hipEventDestroy(e0);
-    if (e1) hipEventDestroy(e1);
+    if (e0) (void)hipEventDestroy(e0);  // nothing to do if a destroy fails
+    if (e1) (void)hipEventDestroy(e1);
   }
   GEMM_TRY(run(ch));
   std::lock_guard<std::mutex> lk(g_mu);
