@@ -117,24 +117,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int pos_max = fil < sd.E ? fil : sd.E;
   const long long t_ref = USE_T ? a.ts[sd.q_base + row0] : 0;
 
-  if (tid == 0) {
-    s_bad = 0;
-    self_acc = 0.f;
-  }
+  PairPrefetch<NCH> pf;
+  pf.r = 0.f;
+  pf.t = 0;
+  auto load = [&](int t) __attribute__((always_inline)) {
+    const int c0 = t * BN;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int chunk = tid + c * NT;
+      if (NCHUNK % NT != 0 && chunk >= NCHUNK) break;
+      const int row = chunk / CH, col = (chunk % CH) * 8;
+      const int key = min(c0 + row, kv_limit - 1);
+      const long long g = (long long)(sd.kv_base + key) * ld + h * D + col;
+      pf.a[c] = *(const u32x4 *)(K + g);
+      pf.b[c] = *(const u32x4 *)(V + g);
+    }
+    if (USE_P && tid < WIN) pf.r = a.rab_p[pos_bucket(pos_max - c0 - tid, a.n_pos)];
+    if (USE_T && tid < BN) pf.t = a.ts[sd.kv_base + min(c0 + tid, kv_limit - 1)];
+  };
+  // The first key tile is requested before the query rows, so that the two
+  // loads overlap instead of waiting one after the other.
+  if (nk > 0) load(0);
   const bool has_rt = a.rab_t != nullptr;  // USE_T without a table: times for the filter only
-  if (USE_T && tid < 33) {
-    const int c = tid - 1;
-    const int bkt = c < 0 ? 0 : 31 - c;
-    t2tab[tid] = has_rt ? -kLog2e * a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1] : 0.f;
-    hts[tid] = 0.f;
-    if (tid < 32) htb[tid] = 0.f;
-  }
-  if (USE_P) {
-    for (int c = tid; c < NRING * RSTR; c += NT) ring[c] = 0.f;
-    if (!DIAG_DPP)
-      for (int c = tid; c < NWV * 32 * SKW; c += NT) skew[c] = 0.f;
-  }
-  __syncthreads();
 
   // This lane's query rows (S^T layout): local rows w*32 + nq*16 + lr.
   const int wrow0 = min(w * 32, nrows - 1);
@@ -173,6 +177,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       dof[nq][ks] = __builtin_bit_cast(bf16x8, g);
     }
   }
+  // (tables and accumulators are set up after the rows are requested: the
+  // table's wait covers those loads)
+  if (tid == 0) {
+    s_bad = 0;
+    self_acc = 0.f;
+  }
+  if (USE_T && tid < 33) {
+    const int c = tid - 1;
+    const int bkt = c < 0 ? 0 : 31 - c;
+    t2tab[tid] = has_rt ? -kLog2e * a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1] : 0.f;
+    hts[tid] = 0.f;
+    if (tid < 32) htb[tid] = 0.f;
+  }
+  if (USE_P) {
+    for (int c = tid; c < NRING * RSTR; c += NT) ring[c] = 0.f;
+    if (!DIAG_DPP)
+      for (int c = tid; c < NWV * 32 * SKW; c += NT) skew[c] = 0.f;
+  }
+  __syncthreads();
   unsigned qmin = 0, qmax = 0;
   if (USE_T) {
     qmin = __builtin_amdgcn_readfirstlane(wave_min_u32(min(tq[0], tq[1])));
@@ -188,24 +211,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const bool wave_tf = TF && __builtin_amdgcn_readfirstlane(
       (int)wave_max_u32((tfr[0] || tfr[1]) ? 1u : 0u)) != 0;
 
-  PairPrefetch<NCH> pf;
-  pf.r = 0.f;
-  pf.t = 0;
-  auto load = [&](int t) __attribute__((always_inline)) {
-    const int c0 = t * BN;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int chunk = tid + c * NT;
-      if (NCHUNK % NT != 0 && chunk >= NCHUNK) break;
-      const int row = chunk / CH, col = (chunk % CH) * 8;
-      const int key = min(c0 + row, kv_limit - 1);
-      const long long g = (long long)(sd.kv_base + key) * ld + h * D + col;
-      pf.a[c] = *(const u32x4 *)(K + g);
-      pf.b[c] = *(const u32x4 *)(V + g);
-    }
-    if (USE_P && tid < WIN) pf.r = a.rab_p[pos_bucket(pos_max - c0 - tid, a.n_pos)];
-    if (USE_T && tid < BN) pf.t = a.ts[sd.kv_base + min(c0 + tid, kv_limit - 1)];
-  };
   auto store = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -300,7 +305,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     tacc_lo = tacc_hi = 0.f;
   };
   if (nk > 0) {
-    load(0);
     store(0);
     if (nk > 1) load(1);
     __syncthreads();
@@ -675,54 +679,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const u16 *Q = (const u16 *)a.Q, *K = (const u16 *)a.K, *V = (const u16 *)a.V;
   const u16 *dO = (const u16 *)a.dO;
 
-  const bool has_rt = a.rab_t != nullptr;  // USE_T without a table: times for the filter only
-  if (USE_T && tid < 33) {
-    const int c = tid - 1;
-    const int bkt = c < 0 ? 0 : 31 - c;
-    t2tab[tid] = has_rt ? -kLog2e * a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1] : 0.f;
-  }
-
-  // This lane's key (B-operand and C-column layout): k0 + w*16 + lr.
-  const int lkey = w * 16 + lr;
-  const bool kok = lkey < nkeys;
-  const int key = k0 + (kok ? lkey : nkeys - 1);
-  const int rmin = kok ? (key < sd.P ? 0 : key) : 0x7fffffff;  // first row that sees the key
-  const int kmax_valid = k0 + nkeys - 1;
-  const int rmin_tile = kmax_valid < sd.P ? 0 : kmax_valid;      // rows >= it see every key
-  const long long t_ref = USE_T ? a.ts[sd.kv_base + k0] : 0;
-  __shared__ int s_bad;
-  if (tid == 0) s_bad = 0;
-  // Times are kept as u = t - t_ref + 2^31; a row or key 2^31 s or more
-  // away from t_ref would wrap, so it raises the status bit.
-  bool bad_t = false;
-  unsigned tk = 0u;
-  if (USE_T) {
-    const long long dk = a.ts[sd.kv_base + key] - t_ref;
-    bad_t = dk < -2147483648LL || dk > 2147483647LL;
-    tk = (unsigned)(dk + 2147483648LL);
-  }
-  unsigned kmin = 0, kmax = 0;
-  if (USE_T) {
-    kmin = __builtin_amdgcn_readfirstlane(wave_min_u32(tk));
-    kmax = __builtin_amdgcn_readfirstlane(wave_max_u32(tk));
-  }
-  // The t2tab entries in a register (lane c holds entry c): a step's
-  // constant rab_t term is a lane read, with no LDS round trip.
-  float t2v = 0.f;
-  if (USE_T && has_rt && lane < 33) {
-    const int bkt = lane == 0 ? 0 : 32 - lane;
-    t2v = -kLog2e * a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1];
-  }
-  bf16x8 kf[KS], vf[KS];
-  {
-    const long long off = (long long)(sd.kv_base + key) * ld + h * D + lg * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(K + off + ks * 32));
-      vf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(V + off + ks * 32));
-    }
-  }
-
   PairPrefetch<NCH> pf;
   pf.r = 0.f;
   pf.t = 0;
@@ -754,6 +710,57 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // row times by the last wave (waves 0-1 stage the rab_p window)
     if (USE_T && tid >= 256 - BM) pf.t = a.ts[sd.q_base + min(fr0 + tid - (256 - BM), L - 1)];
   };
+  // The first query step is requested before the keys, so that the loads
+  // overlap instead of waiting one after the other.
+  if (nq > 0) load(qt_lo);
+  const bool has_rt = a.rab_t != nullptr;  // USE_T without a table: times for the filter only
+
+  // This lane's key (B-operand and C-column layout): k0 + w*16 + lr.
+  const int lkey = w * 16 + lr;
+  const bool kok = lkey < nkeys;
+  const int key = k0 + (kok ? lkey : nkeys - 1);
+  const int rmin = kok ? (key < sd.P ? 0 : key) : 0x7fffffff;  // first row that sees the key
+  const int kmax_valid = k0 + nkeys - 1;
+  const int rmin_tile = kmax_valid < sd.P ? 0 : kmax_valid;      // rows >= it see every key
+
+  bf16x8 kf[KS], vf[KS];
+  {
+    const long long off = (long long)(sd.kv_base + key) * ld + h * D + lg * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(K + off + ks * 32));
+      vf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(V + off + ks * 32));
+    }
+  }
+  const long long t_ref = USE_T ? a.ts[sd.kv_base + k0] : 0;
+  const long long t_key = USE_T ? a.ts[sd.kv_base + key] : 0;
+  float t2raw = 0.f;
+  if (USE_T && has_rt) {
+    const int bkt = (lane == 0 || lane > 32) ? 0 : 32 - lane;
+    t2raw = a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1];
+  }
+  __shared__ int s_bad;
+  if (tid == 0) s_bad = 0;
+  // Times are kept as u = t - t_ref + 2^31; a row or key 2^31 s or more
+  // away from t_ref would wrap, so it raises the status bit.
+  bool bad_t = false;
+  unsigned tk = 0u;
+  if (USE_T) {
+    const long long dk = t_key - t_ref;
+    bad_t = dk < -2147483648LL || dk > 2147483647LL;
+    tk = (unsigned)(dk + 2147483648LL);
+  }
+  unsigned kmin = 0, kmax = 0;
+  if (USE_T) {
+    kmin = __builtin_amdgcn_readfirstlane(wave_min_u32(tk));
+    kmax = __builtin_amdgcn_readfirstlane(wave_max_u32(tk));
+  }
+  // The t2tab entries in a register (lane c holds entry c): a step's
+  // constant rab_t term is a lane read, with no LDS round trip. (The table
+  // was requested with the key rows; lanes past 32 read entry 0 and drop it.)
+  const float t2v = (USE_T && lane < 33) ? -kLog2e * t2raw : 0.f;
+  if (USE_T && tid < 33) t2tab[tid] = t2v;  // the same entries, for the per-element reads
+
   auto store = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -782,7 +789,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   for (int nd = 0; nd < ND; ++nd) dk[nd] = dv[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (nq > 0) {
-    load(qt_lo);
     store(0);
     if (nq > 1) load(qt_lo + 1);
   }

@@ -202,16 +202,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int pos_max = fil < sd.E ? fil : sd.E;
   const long long t_ref = USE_T ? a.ts_q[sd.q_base + row0] : 0;
 
+  // Global -> register prefetch of one key tile, and register -> LDS store.
+  TilePrefetch<NCH> pf;
+  pf.r = 0.f;
+  pf.t = 0;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int chunk = tid + i * 256;
+    pf.off[i] = (unsigned)(((chunk / (D / 8)) * ld + h * D + (chunk % (D / 8)) * 8) * 2);
+  }
+  FwdTileCtx cx;
+  cx.K = K; cx.V = V; cx.rab_p = a.rab_p; cx.ts_kv = a.ts_kv; cx.ld = ld;
+  cx.kv_base = sd.kv_base; cx.kv_limit = kv_limit; cx.pos_max = pos_max;
+  cx.n_pos = a.n_pos; cx.tid = tid;
+  // The first key tile is requested before the query rows, so that the two
+  // loads overlap instead of waiting one after the other.
+  if (nk > 0) fwd_load_tile<D, BN, USE_P, USE_T>(pf, cx, 0);
+
   // With USE_T the kernel has timestamps; the rab_t table may still be
   // absent when they serve only the timestamp filter (then it adds zero).
   const bool has_rt = a.rab_t != nullptr;
-  if (tid == 0) s_bad = 0;
-  if (USE_T && tid < 33) {
-    const int c = tid - 1;
-    const int bkt = c < 0 ? 0 : 31 - c;
-    t2tab[tid] = has_rt ? -kLog2e * a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1] : 0.f;
-  }
-  __syncthreads();
 
   // This lane's query rows in the S^T layout: local rows w*32 + nq*16 + lr.
   int hi_r[2], vb_r[2];
@@ -241,16 +251,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       qf[nq][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  unsigned qmin = 0, qmax = 0;
-  if (USE_T) {
-    qmin = __builtin_amdgcn_readfirstlane(wave_min_u32(min(tq_r[0], tq_r[1])));
-    qmax = __builtin_amdgcn_readfirstlane(wave_max_u32(max(tq_r[0], tq_r[1])));
-  }
-  // The t2tab entries in a register too (lane c holds entry c).
+  // The t2tab entries in a register too (lane c holds entry c); the table
+  // is read after the rows are requested, so its wait covers those loads.
   float t2v = 0.f;
   if (USE_T && has_rt && lane < 33) {
     const int bkt = lane == 0 ? 0 : 32 - lane;
     t2v = -kLog2e * a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1];
+  }
+  if (tid == 0) s_bad = 0;
+  if (USE_T && tid < 33) t2tab[tid] = t2v;  // the same entries, for the per-element reads
+  __syncthreads();
+  unsigned qmin = 0, qmax = 0;
+  if (USE_T) {
+    qmin = __builtin_amdgcn_readfirstlane(wave_min_u32(min(tq_r[0], tq_r[1])));
+    qmax = __builtin_amdgcn_readfirstlane(wave_max_u32(max(tq_r[0], tq_r[1])));
   }
   // Keys [0, wave_hi) are the ones this wave's rows see: a key tile at or
   // beyond it (the upper half of a diagonal block, or a wave past the last
@@ -261,19 +275,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const bool wave_tf = TF && __builtin_amdgcn_readfirstlane(
       (int)wave_max_u32((tfr[0] || tfr[1]) ? 1u : 0u)) != 0;
 
-  // Global -> register prefetch of one key tile, and register -> LDS store.
-  TilePrefetch<NCH> pf;
-  pf.r = 0.f;
-  pf.t = 0;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int chunk = tid + i * 256;
-    pf.off[i] = (unsigned)(((chunk / (D / 8)) * ld + h * D + (chunk % (D / 8)) * 8) * 2);
-  }
-  FwdTileCtx cx;
-  cx.K = K; cx.V = V; cx.rab_p = a.rab_p; cx.ts_kv = a.ts_kv; cx.ld = ld;
-  cx.kv_base = sd.kv_base; cx.kv_limit = kv_limit; cx.pos_max = pos_max;
-  cx.n_pos = a.n_pos; cx.tid = tid;
   f32x4 acc[2][ND];
 #pragma unroll
   for (int nq = 0; nq < 2; ++nq)
@@ -353,7 +354,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   };
 
   if (nk > 0) {
-    fwd_load_tile<D, BN, USE_P, USE_T>(pf, cx, 0);
     fwd_store_tile<D, BN, USE_P, USE_T>(pf, tid, Ks, Vs, rabw, tkey, tkst, t_ref, bad_t);
     if (nk > 1) fwd_load_tile<D, BN, USE_P, USE_T>(pf, cx, 1);
     __syncthreads();
