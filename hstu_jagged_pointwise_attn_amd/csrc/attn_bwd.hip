@@ -494,7 +494,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     // fragment reads run QD steps ahead of their MFMAs in a ring.
     if (c0 < wave_hi) {
       const u16 *kbuf = Ks + b * BN * ST + (lg * 4 + (lr >> 2)) * ST + (lr & 3) * 4;
-      constexpr int QD = ND < 4 ? ND : 4;
+      constexpr int QD = ND < 2 ? ND : 2;
       s16x4 rlo[QD], rhi[QD];
       auto rd = [&](int nd) __attribute__((always_inline)) {
         rlo[nd % QD] = lds_read_tr16(kbuf + nd * 16);
@@ -917,7 +917,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // dV += P^T dO and dK += dS^T Q with dO and Q read transposed; the
     // fragment reads run GD steps ahead of their MFMAs in a ring.
     {
-      constexpr int NI = 2 * ND, GD = 2;
+      constexpr int NI = 2 * ND, GD = 1;
       const int base = (lg * 4 + (lr >> 2)) * ST + (lr & 3) * 4;
       s16x4 ro0[GD], ro1[GD], rq0[GD], rq1[GD];
       auto rd = [&](int i) __attribute__((always_inline)) {

@@ -330,7 +330,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
         }
       }
     } else {
-      constexpr int NI = 2 * ND, PVD = 4;
+      constexpr int NI = 2 * ND, PVD = 2;
       s16x4 rlo[PVD], rhi[PVD];
       auto rd = [&](int i) __attribute__((always_inline)) {
         const u16 *p0 = vb + (i / ND) * 32 * VST + (i % ND) * 16;
