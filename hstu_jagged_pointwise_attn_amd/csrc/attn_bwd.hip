@@ -89,7 +89,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int NRING = DIAG_DPP ? NWV * 4 : NWV;
   __shared__ float ring[USE_P ? NRING * RSTR : 1];
   __shared__ float skew[USE_P && !DIAG_DPP ? NWV * 32 * SKW : 1];
-  __shared__ float hts[USE_T ? 33 : 1];   // per-element path: by ffbh(|dt|) + 1
+  // per-element path: by ffbh(|dt|) + 1, one copy per lane row (lr), so that
+  // the sixteen rows of a lane group, which usually share a bucket, add into
+  // different words instead of queueing on one (summed at the end)
+  constexpr int HSN = 16, HSS = 33;
+  __shared__ float hts[USE_T ? HSN * HSS : 1];
   __shared__ float htb[USE_T ? 32 : 1];   // constant blocks: by bucket
   __shared__ float self_acc;
   __shared__ int s_bad;
@@ -187,9 +191,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const int c = tid - 1;
     const int bkt = c < 0 ? 0 : 31 - c;
     t2tab[tid] = has_rt ? -kLog2e * a.rab_t[bkt < a.n_tb - 1 ? bkt : a.n_tb - 1] : 0.f;
-    hts[tid] = 0.f;
     if (tid < 32) htb[tid] = 0.f;
   }
+  if (USE_T)
+    for (int c = tid; c < HSN * HSS; c += NT) hts[c] = 0.f;
   if (USE_P) {
     for (int c = tid; c < NRING * RSTR; c += NT) ring[c] = 0.f;
     if (!DIAG_DPP)
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
                 if (T2) tsum_hi += hi ? ds : 0.f;
               } else {
                 if (tix != run_b) {
-                  if (run_b >= 0) atomicAdd(&hts[run_b], run_s);
+                  if (run_b >= 0) atomicAdd(&hts[lr * HSS + run_b], run_s);
                   run_b = tix;
                   run_s = 0.f;
                 }
@@ -454,7 +459,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         tacc_lo += tsum - tsum_hi;
         tacc_hi += tsum_hi;
       }
-      if (USE_T && !TC && !T2 && run_b >= 0) atomicAdd(&hts[run_b], run_s);
+      if (USE_T && !TC && !T2 && run_b >= 0) atomicAdd(&hts[lr * HSS + run_b], run_s);
     };
     bool done = c0 >= wave_hi;  // nothing this wave sees
     if constexpr (TF) {
@@ -613,7 +618,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     if (USE_T && has_rt) atomicAdd(a.drab_t, self_acc * a.inv_nmax);
   }
   if (USE_T && has_rt && tid < 33) {
-    const float v = hts[tid];
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < HSN; ++k) v += hts[k * HSS + tid];
     if (v != 0.f) {
       const int c = tid - 1;
       const int bkt = c < 0 ? 0 : 31 - c;
