@@ -93,6 +93,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   // the sixteen rows of a lane group, which usually share a bucket, add into
   // different words instead of queueing on one (summed at the end)
   constexpr int HSN = 16, HSS = 33;
+  constexpr bool HIST_AFTER = D < 128;
   __shared__ float hts[USE_T ? HSN * HSS : 1];
   __shared__ float htb[USE_T ? 32 : 1];   // constant blocks: by bucket
   __shared__ float self_acc;
@@ -369,10 +370,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       const int prel = sd.P - (c0 + lg * 4);
       float tsum = 0.f, tsum_hi = 0.f, run_s = 0.f;
       int run_b = -1;
+      auto merge = [&](int tix, float ds) __attribute__((always_inline)) {
+        if (tix != run_b) {
+          if (run_b >= 0) atomicAdd(&hts[lr * HSS + run_b], run_s);
+          run_b = tix;
+          run_s = 0.f;
+        }
+        run_s += ds;
+      };
       float dacc[4] = {-0.f, -0.f, -0.f, -0.f};  // -0: the first add is exact and folds away
 #pragma unroll
       for (int nq = 0; nq < 2; ++nq) {
         u32x4 wds;
+        // HIST_AFTER: the row's buckets and dS are kept and merged into the
+        // histogram after its scores, so no branch sits inside the score
+        // chain (d = 128 has no registers to spare for them)
+        int tixs[2][4];
+        float dsn[2][4];
 #pragma unroll
         for (int mk = 0; mk < 2; ++mk) {
           u32x4 tk4 = {0u, 0u, 0u, 0u};
@@ -408,13 +422,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
               if (TC || T2) {
                 if (!(USE_P && wave_dpp)) tsum += ds;  // else from the diagonal sums below
                 if (T2) tsum_hi += hi ? ds : 0.f;
+              } else if (HIST_AFTER) {
+                tixs[mk][i] = tix;
+                dsn[mk][i] = ds;
               } else {
-                if (tix != run_b) {
-                  if (run_b >= 0) atomicAdd(&hts[lr * HSS + run_b], run_s);
-                  run_b = tix;
-                  run_s = 0.f;
-                }
-                run_s += ds;
+                merge(tix, ds);
               }
             }
           }
@@ -427,6 +439,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           }
         }
         dsa[nq] = __builtin_bit_cast(bf16x8, wds);
+        if (USE_T && !TC && !T2 && HIST_AFTER) {
+#pragma unroll
+          for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) merge(tixs[mk][i], dsn[mk][i]);
+        }
       }
       if (USE_P && wave_dpp) {
         // every dS of the block sits in exactly one lane's four diagonal sums,
