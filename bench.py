@@ -358,6 +358,8 @@ def bench_layer(args):
     p = lp.core
     D, dm, T = p.H * p.d, lp.d_model, p.T
     log(f"[bench] layer workload {args.workload}: T={T} D={D} d_model={dm}")
+    if args.split_projection:
+        api.set_fused_projection(False)
     ns = device.upload_layer(lp)
     # the forward keeps U, V, Q, K for the backward (no recomputation from Z)
     f = device.run_layer_fwd(ns, save_act=True)
@@ -391,7 +393,8 @@ def bench_layer(args):
     names = ((_lib.HSTU_KERNEL_SCHED, "sched"), (_lib.HSTU_KERNEL_ATTN_FWD, "attn_fwd"),
              (_lib.HSTU_KERNEL_NORM_FWD, "norm_fwd"), (_lib.HSTU_KERNEL_NORM_BWD, "norm_bwd"),
              (_lib.HSTU_KERNEL_ATTN_BWD_DQ, "attn_bwd_dq"), (_lib.HSTU_KERNEL_ATTN_BWD_DKDV, "attn_bwd_dkdv"),
-             (_lib.HSTU_KERNEL_AUX, "aux"), (_lib.HSTU_KERNEL_GEMM, "gemm"), (_lib.HSTU_KERNEL_LAYER_EW, "layer_ew"))
+             (_lib.HSTU_KERNEL_AUX, "aux"), (_lib.HSTU_KERNEL_GEMM, "gemm"), (_lib.HSTU_KERNEL_LAYER_EW, "layer_ew"),
+             (_lib.HSTU_KERNEL_PROJ_SILU, "proj_silu"))
     for kid, kname in names:
         tms, n = api.kernel_timing_read(kid)
         if n:
@@ -401,8 +404,10 @@ def bench_layer(args):
     log("[bench] per-step ms: " + ", ".join(f"{k}={v:.4f}" for k, v in per_step.items()))
     # Dominant kernel by time per step: the projection GEMMs (hipBLASLt, six
     # launches per step, reported together) or one of the attention kernels.
+    # (with the fused f1, "gemm" is the other five GEMMs and "proj_silu" f1's forward)
+    f1_flops = 8.0 * T * D * dm
     kflops = {"attn_fwd": 4.0 * p.d * pairs, "attn_bwd_dq": 4.0 * p.d * pairs, "attn_bwd_dkdv": 4.0 * p.d * pairs,
-              "gemm": gemm_flops}
+              "gemm": gemm_flops - (f1_flops if "proj_silu" in per_step else 0.0), "proj_silu": f1_flops}
     dom = max((k for k in kflops if k in per_step), key=lambda k: per_step[k])
     achieved = kflops[dom] / (per_step[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -422,6 +427,8 @@ def bench_layer(args):
         "data": "synthetic (seeded generators; no dataset)",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload, "step": "layer_fwdbwd",
                    "activations": "U, V, Q, K kept from the forward",
+                   "f1": ("library GEMM + SiLU split pass" if args.split_projection
+                          else "own MFMA GEMM with the SiLU split epilogue"),
                    "batch": p.B, "tokens": T, "d_model": dm, "heads": p.H, "d": p.d,
                    "useful_tflop_per_step": flops / 1e12, "attention_tflop": attn_flops / 1e12,
                    "gemm_tflop": gemm_flops / 1e12, "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS},
@@ -594,6 +601,8 @@ def main():
                     help="do not write the 512 MiB eviction buffer between timed steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-projection", action="store_true",
+                    help="layer workloads: f1 as a library GEMM and a separate SiLU split pass")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB 3 times (calibrates the HBM "
                          "byte counters of a profiler run against a transfer of known size)")

@@ -19,7 +19,7 @@ HSTU_MASK_CAND_TIME_FILTER = 1
 HSTU_COST_TOKENS, HSTU_COST_ATTENTION = 0, 1
 (HSTU_KERNEL_SCHED, HSTU_KERNEL_ATTN_FWD, HSTU_KERNEL_NORM_FWD, HSTU_KERNEL_NORM_BWD, HSTU_KERNEL_ATTN_BWD_DQ,
  HSTU_KERNEL_AUX, HSTU_KERNEL_ATTN_BWD_DKDV, HSTU_KERNEL_STOCHASTIC_LENGTH, HSTU_KERNEL_GATHER,
- HSTU_KERNEL_BALANCE, HSTU_KERNEL_GEMM, HSTU_KERNEL_LAYER_EW) = range(12)
+ HSTU_KERNEL_BALANCE, HSTU_KERNEL_GEMM, HSTU_KERNEL_LAYER_EW, HSTU_KERNEL_PROJ_SILU) = range(13)
 HSTU_DEV_BAD_OFFSETS, HSTU_DEV_BAD_SEGMENTS, HSTU_DEV_BAD_GROUP, HSTU_DEV_TOO_LONG = 1, 2, 4, 8
 HSTU_DEV_BAD_TIMESTAMPS = 16
 
@@ -85,6 +85,7 @@ SIGNATURES = {
     "hstu_kernel_timing": ([ctypes.c_int32], ctypes.c_int),
     "hstu_set_inline_schedule": ([ctypes.c_int32], ctypes.c_int32),
     "hstu_set_tile_order": ([ctypes.c_int32], ctypes.c_int32),
+    "hstu_set_fused_projection": ([ctypes.c_int32], ctypes.c_int32),
     "hstu_kernel_timing_read": ([ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
                                  ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
     "hstu_stochastic_length": ([_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp, _vp,

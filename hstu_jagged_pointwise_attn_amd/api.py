@@ -302,6 +302,14 @@ def set_inline_schedule(enable: bool) -> bool:
     return bool(L.lib().hstu_set_inline_schedule(1 if enable else 0))
 
 
+def set_fused_projection(enable: bool) -> bool:
+    """hstu_set_fused_projection: whether the bf16 training forward runs f1
+    as the library's own GEMM with the SiLU split epilogue (default) or as a
+    library GEMM followed by a separate SiLU split pass. Returns the previous
+    setting."""
+    return bool(L.lib().hstu_set_fused_projection(1 if enable else 0))
+
+
 HSTU_TILE_ORDER_LONGEST = 0
 HSTU_TILE_ORDER_BY_SEQUENCE = 1
 

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhstu.so")
-SOURCES = ["sched.hip", "attn_fwd.hip", "attn_bwd.hip", "norm.hip", "batching.hip", "layer.hip", "gemm.cpp",
+SOURCES = ["sched.hip", "attn_fwd.hip", "attn_bwd.hip", "norm.hip", "batching.hip", "layer.hip", "proj_gemm.hip", "gemm.cpp",
            "api.cpp", "static_ws.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

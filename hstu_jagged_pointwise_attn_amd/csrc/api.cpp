@@ -48,6 +48,9 @@ hstu_status_t hip_fail(hipError_t e, const char *what) {
 std::atomic<int> g_inline_sched{1};
 // Work-list order of the scheduler kernel (hstu_set_tile_order).
 std::atomic<int> g_tile_order{kOrderLongest};
+// Whether the bf16 training forward runs f1 as the fused SiLU-split GEMM
+// (hstu_set_fused_projection).
+std::atomic<int> g_fused_proj{1};
 
 // Optional per-launch event timing (hstu_kernel_timing).
 struct TimingRecord {
@@ -487,6 +490,8 @@ const char *hstu_version(void) { return "0.1.0"; }
 
 int32_t hstu_set_inline_schedule(int32_t enable) { return g_inline_sched.exchange(enable ? 1 : 0); }
 
+int32_t hstu_set_fused_projection(int32_t enable) { return g_fused_proj.exchange(enable ? 1 : 0); }
+
 int32_t hstu_set_tile_order(int32_t order) {
   if (order != HSTU_TILE_ORDER_LONGEST && order != HSTU_TILE_ORDER_BY_SEQUENCE) {
     fail(HSTU_ERR_INVALID_ARG, "tile order %d", order);
@@ -870,7 +875,12 @@ hstu_status_t layer_forward(const hstu_problem_t *p, const hstu_layer_weights_t 
   const bool bf16 = p->dtype == HSTU_BF16;
   const GemmType et = bf16 ? kGemmBF16 : kGemmF32;
   const long long D = (long long)p->H * p->d, dm = w->d_model;
-  if (Z) {
+  if (Z && bf16 && g_fused_proj.load() && f1_silu_gemm_supported(T, (int)dm, (int)D) &&
+      f1_silu_gemm_ws_bytes((int)dm, (int)D) <= kGemmWsBytes) {
+    // one GEMM writes Z and the four SiLU blocks; W1's transpose goes to gws
+    Timed t_(HSTU_KERNEL_PROJ_SILU, st);
+    HIP_TRY(launch_f1_silu_gemm(X, T, (int)dm, w->W1, w->b1, (int)D, gws, Z, U, V, Q, K, st), "f1 SiLU GEMM launch");
+  } else if (Z) {
     if (T > 0) GEMM_RUN(gemm(false, false, T, 4 * D, dm, X, dm, w->W1, 4 * D, Z, 4 * D, et, et, w->b1), "f1 GEMM");
     Timed t_(HSTU_KERNEL_LAYER_EW, st);
     HIP_TRY(launch_silu_split(Z, T, (int)D, bf16, U, V, Q, K, st), "SiLU split launch");

@@ -1,0 +1,437 @@
+// f1 of an HSTU layer as one bf16 MFMA GEMM with the activation in its
+// epilogue (HSTU blog, section 3, layer formula: U, V, Q, K are the four
+// column blocks of phi1(f1(X)) = SiLU(X W1 + b1)).
+//
+//   Z = X W1 + b1            X [T, dm], W1 [dm, 4D], Z [T, 4D] (bf16, kept for
+//                            the backward's SiLU')
+//   U|V|Q|K = SiLU(Z)        each [T, D]; column c of Z goes to block c / D,
+//                            column c % D
+//
+// The SiLU is taken of Z as stored (rounded to bf16), which is what the
+// backward differentiates. Both outputs leave each wave as whole row segments
+// staged through LDS, so Z is written once and never read back.
+//
+// Tiling (gfx950, v_mfma_f32_16x16x32_bf16), both forms:
+//   workgroup   256 tokens x 256 columns of Z, 8 waves, one workgroup per CU
+//   wave        64 tokens x 128 columns: 8 x 4 blocks of 16 x 16 (128 fp32
+//               accumulators per lane)
+//   operands    MFMA A = rows of W1^T (columns of Z), MFMA B = rows of X, so
+//               a lane's four accumulator entries are four consecutive
+//               columns of one token: 8 bytes of bf16 per block
+//   HBM         X and W1^T tiles through raw buffer loads: rows past the end
+//               (tokens past T, columns past 4D) read as zeros by the range
+//               check, and so does a K tail, through an out-of-range offset
+//   grid        block b runs on XCD b % 8; the column tiles of one token tile
+//               run back to back on one XCD, so that XCD's L2 serves the
+//               repeated reads of the X tile
+// K loop, d_model a multiple of 128: four LDS stages of K = 32 filled by
+// buffer loads straight into LDS, three K steps in flight
+// (f1_silu_gemm_dma_kernel). Other d_model (a multiple of 8): two LDS stages
+// of K = 64 filled through registers, one step in flight
+// (f1_silu_gemm_kernel). Both sum K in the same order, so they give the same
+// bits.
+// W1 is first transposed to W1^T [4D, dm] by a small LDS-tiled kernel, so that
+// both operands are read along K.
+#include "hstu_internal.h"
+#include "device_common.h"
+
+#include <type_traits>
+
+namespace hstu {
+namespace {
+using namespace dev;
+
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+constexpr int kBN = 256;  // columns of Z per workgroup
+constexpr int kWM = 64;   // tokens per wave
+constexpr int kWN = 128;  // columns per wave
+
+struct ProjArgs {
+  const u16 *X, *W1t;
+  const float *b1;
+  long long T;
+  int dm, N4, D, NT, MT;
+  u16 *Z, *U, *V, *Q, *K;
+};
+
+// BM tokens x 256 columns per workgroup, (BM / 64) x 2 waves, K steps of BK,
+// MINB workgroups per CU; the epilogue stages EC columns per wave at a time.
+template <int BM, int BK, int MINB, int EC>
+struct ProjCfg {
+  static constexpr int kWaves = (BM / kWM) * (kBN / kWN);
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kCPR = BK / 8;                        // 16-byte chunks per row
+  static constexpr int kLS = BK + 8;                         // LDS row stride (elements)
+  static constexpr int kStage = (kBN + BM) * kLS;            // elements per stage
+  static constexpr int kRowsPerPass = kThreads / kCPR;       // rows one pass of the threads covers
+  static constexpr int kWJ = kBN / kRowsPerPass, kXJ = BM / kRowsPerPass;  // chunks per thread
+  static constexpr int kES = EC + 8;                         // staging row stride (elements)
+  static_assert(kBN % kRowsPerPass == 0 && BM % kRowsPerPass == 0, "whole passes");
+  static_assert(2 * kStage >= kWaves * kWM * kES, "epilogue staging fits in the stage buffers");
+  static_assert(kWN % EC == 0 && EC % 64 == 0, "staging width");
+  static_assert(kThreads == BM * 2, "launch bounds");
+};
+
+template <int BM, int BK, int MINB, int EC>
+__global__ __launch_bounds__(BM * 2, MINB) void f1_silu_gemm_kernel(ProjArgs a) {
+  using C = ProjCfg<BM, BK, MINB, EC>;
+  constexpr int kLS = C::kLS, kStage = C::kStage, kCPR = C::kCPR, kES = C::kES;
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * kStage];
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int mt = (local / a.NT) * 8 + xcd, nt = local % a.NT;
+  if (mt >= a.MT) return;
+  const long long m0 = (long long)mt * BM;
+  const int n0 = nt * kBN;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int dm = a.dm;
+
+  // Tiles as raw buffers: W1^T rows n0.. (at most 256), X rows m0.. (at most BM).
+  const long long mrows = a.T - m0 < BM ? a.T - m0 : BM;
+  const int nrows = a.N4 - n0 < kBN ? a.N4 - n0 : kBN;
+  const __amdgpu_buffer_rsrc_t wr = buf_view(a.W1t + (long long)n0 * dm, (long long)nrows * dm * 2);
+  const __amdgpu_buffer_rsrc_t xr = buf_view(a.X + m0 * dm, mrows * dm * 2);
+  // chunk j of this thread: row tid / kCPR + j kRowsPerPass, 16-byte chunk tid % kCPR
+  const int ch = tid % kCPR, row0 = tid / kCPR;
+  u32x4 pw[C::kWJ], px[C::kXJ];
+  auto load = [&](int k0) __attribute__((always_inline)) {
+    const bool kv = ch * 8 < dm - k0;
+    const unsigned base = (unsigned)(row0 * dm * 2 + ch * 16 + k0 * 2);
+#pragma unroll
+    for (int j = 0; j < C::kWJ; ++j)
+      pw[j] = buf_load16(wr, kv ? base + (unsigned)(j * C::kRowsPerPass * dm * 2) : 0x80000000u);
+#pragma unroll
+    for (int j = 0; j < C::kXJ; ++j)
+      px[j] = buf_load16(xr, kv ? base + (unsigned)(j * C::kRowsPerPass * dm * 2) : 0x80000000u);
+  };
+  auto store = [&](int s) __attribute__((always_inline)) {
+    u16 *ws = lds + s * kStage, *xs = ws + kBN * kLS;
+#pragma unroll
+    for (int j = 0; j < C::kWJ; ++j) *(u32x4 *)(ws + (row0 + j * C::kRowsPerPass) * kLS + ch * 8) = pw[j];
+#pragma unroll
+    for (int j = 0; j < C::kXJ; ++j) *(u32x4 *)(xs + (row0 + j * C::kRowsPerPass) * kLS + ch * 8) = px[j];
+  };
+
+  const int wn = w & 1, wm = w >> 1;  // wave's column half and token quarter
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int ni = 0; ni < 8; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) acc[ni][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (dm + BK - 1) / BK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load((kt + 1) * BK);
+    const u16 *ws = lds + (kt & 1) * kStage, *xs = ws + kBN * kLS;
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      bf16x8 xf[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        xf[mi] = *(const bf16x8 *)(xs + (wm * kWM + mi * 16 + lr) * kLS + kk * 32 + lg * 8);
+#pragma unroll
+      for (int ni = 0; ni < 8; ++ni) {
+        const bf16x8 wf = *(const bf16x8 *)(ws + (wn * kWN + ni * 16 + lr) * kLS + kk * 32 + lg * 8);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+          acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[mi], acc[ni][mi], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nk) store((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // Epilogue. Lane (lr, lg) holds, per block (ni, mi), columns
+  // n = n0 + wn 128 + ni 16 + lg 4 + i (i < 4) of token m = m0 + wm 64 + mi 16 + lr.
+  u16 *st = lds + w * (kWM * kES);  // this wave's staging area
+  const int cw = n0 + wn * kWN;     // first column of the wave
+  float bias[8][4];
+#pragma unroll
+  for (int ni = 0; ni < 8; ++ni) {
+    const int c = cw + ni * 16 + lg * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bias[ni][i] = (a.b1 && c < a.N4) ? a.b1[c + i] : 0.f;
+  }
+  const long long mw = m0 + wm * kWM;
+  constexpr int NB = EC / 16;  // column blocks per staging round
+  // Round (pass, half): pass 0 stages Z, pass 1 SiLU(Z), EC columns at a
+  // time; the wave copies each round out as whole row segments.
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int half = 0; half < kWN / EC; ++half) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int ni = half * NB + nb;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[i] = (float)(__bf16)(acc[ni][mi][i] + bias[ni][i]);
+            if (pass == 1) v[i] = silu_fast(v[i]);
+          }
+          const unsigned lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+          *(uint2 *)(st + (mi * 16 + lr) * kES + nb * 16 + lg * 4) = make_uint2(lo, hi);
+        }
+      }
+      // kWM rows x EC / 8 chunks of 16 bytes
+      constexpr int CPR = EC / 8, RPI = 64 / CPR;
+      const int cc = lane % CPR;
+      const int col = cw + half * EC + cc * 8;
+      int blk = 0, cin = col;
+      if (pass == 1) {
+        blk = col / a.D;
+        cin = col - blk * a.D;
+      }
+      u16 *dst = pass == 0 ? a.Z : blk == 0 ? a.U : blk == 1 ? a.V : blk == 2 ? a.Q : a.K;
+      const long long ldd = pass == 0 ? a.N4 : a.D;
+#pragma unroll 4
+      for (int it = 0; it < kWM / RPI; ++it) {
+        const int r = it * RPI + lane / CPR;
+        const long long m = mw + r;
+        const u32x4 v = *(const u32x4 *)(st + r * kES + cc * 8);
+        if (m < a.T && col < a.N4) *(u32x4 *)(dst + m * ldd + cin) = v;
+      }
+    }
+  }
+}
+
+// The same GEMM with the tiles loaded straight into LDS (buffer loads with
+// the LDS flag, no registers in between), so that three K steps are in flight
+// while one is computed: 256 tokens x 256 columns, 8 waves of 64 x 128, four
+// stages of K = 32 in four LDS arrays (the compiler tells the arrays apart,
+// so a read of one stage does not wait for the loads into the others). Rows
+// are 64 bytes, unpadded; chunk c of row r sits at position c ^ ((r / 4) % 4)
+// of the row, which keeps the 16-byte fragment reads of 16 consecutive rows
+// on distinct banks. A wave's load instruction fills 1 KB of LDS in lane
+// order, so each lane fetches the chunk that belongs at its position.
+template <int EC>
+__global__ __launch_bounds__(512, 1) void f1_silu_gemm_dma_kernel(ProjArgs a) {
+  constexpr int BM = 256, BK = 32, kPart = 256 * BK, kES = EC + 8;
+  static_assert(2 * 64 * kES <= 2 * kPart, "two waves' staging per stage array");
+  __shared__ __attribute__((aligned(16))) u16 s0[2 * kPart], s1[2 * kPart], s2[2 * kPart], s3[2 * kPart];
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int mt = (local / a.NT) * 8 + xcd, nt = local % a.NT;
+  if (mt >= a.MT) return;
+  const long long m0 = (long long)mt * BM;
+  const int n0 = nt * kBN;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int dm = a.dm;
+  const long long mrows = a.T - m0 < BM ? a.T - m0 : BM;
+  const int nrows = a.N4 - n0 < kBN ? a.N4 - n0 : kBN;
+  const __amdgpu_buffer_rsrc_t wr = buf_view(a.W1t + (long long)n0 * dm, (long long)nrows * dm * 2);
+  const __amdgpu_buffer_rsrc_t xr = buf_view(a.X + m0 * dm, mrows * dm * 2);
+  // Load instruction j (0, 1) of this wave fills rows (8 j + w) 16 + lane / 4;
+  // the lane's chunk: position lane % 4 holds chunk (lane % 4) ^ ((lane / 16) % 4).
+  const int lch = (lane & 3) ^ ((lane >> 4) & 3);
+  unsigned goff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) goff[j] = (unsigned)((((j * 8 + w) * 16 + (lane >> 2)) * dm) * 2 + lch * 16);
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto issue = [&](u16 *stg, int k0) __attribute__((always_inline)) {
+    const bool kv = k0 < dm;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const unsigned off = kv ? goff[j] + (unsigned)(k0 * 2) : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void *)(stg + (j * 8 + w) * 512), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)(stg + kPart + (j * 8 + w) * 512), 16, off, 0, 0, 0);
+    }
+  };
+
+  const int wn = w & 1, wm = w >> 1;
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int ni = 0; ni < 8; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) acc[ni][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // fragment of row r (r % 16 = lr), chunk lg: element r 32 + 8 (lg ^ (lr / 4))
+  const int fro = lr * BK + ((lg ^ (lr >> 2)) * 8);
+  auto compute = [&](const u16 *stg) __attribute__((always_inline)) {
+    bf16x8 xf[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) xf[mi] = *(const bf16x8 *)(stg + kPart + (wm * kWM + mi * 16) * BK + fro);
+#pragma unroll
+    for (int ni = 0; ni < 8; ++ni) {
+      const bf16x8 wf = *(const bf16x8 *)(stg + (wn * kWN + ni * 16) * BK + fro);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[mi], acc[ni][mi], 0, 0, 0);
+    }
+  };
+  // s_waitcnt with vmcnt = n (n < 16) and no wait on the other counters
+  auto wait_vm = [](auto n) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt((decltype(n)::value & 15) | (0x7 << 4) | (0xF << 8));
+  };
+  // dm is a multiple of 128 here: K steps come in whole groups of four, so
+  // the loop body has no branches (the waits below rely on the compiler
+  // seeing every load). Loads past the last K step read zeros (out-of-range
+  // offset) into stages nobody computes.
+  const int nk = dm / BK;
+  issue(s0, 0);
+  issue(s1, BK);
+  issue(s2, 2 * BK);
+  // Step kt: wait for this wave's loads of stage kt (4 per stage per wave;
+  // the two later stages stay in flight), barrier (every wave's stage kt has
+  // landed, every wave is done with stage kt - 1), compute stage kt, then
+  // refill stage kt - 1 with K step kt + 3.
+  auto step = [&](int kt, u16 *cur, u16 *nxt3) __attribute__((always_inline)) {
+    wait_vm(ic<8>());
+    // A plain s_barrier: __syncthreads() adds a workgroup release fence,
+    // which would wait for every load in flight (vmcnt(0)) and drain the
+    // pipeline. The empty asm statements keep the compiler from moving LDS
+    // accesses across it; the LDS reads of the previous step were consumed
+    // by its MFMAs before this point.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    compute(cur);
+    issue(nxt3, (kt + 3) * BK);
+  };
+  for (int kt = 0; kt < nk; kt += 4) {
+    step(kt, s0, s3);
+    step(kt + 1, s1, s0);
+    step(kt + 2, s2, s1);
+    step(kt + 3, s3, s2);
+  }
+  __syncthreads();
+
+  u16 *st = (w >> 1) == 0 ? s0 : (w >> 1) == 1 ? s1 : (w >> 1) == 2 ? s2 : s3;
+  st += (w & 1) * 64 * kES;
+  const int cw = n0 + wn * kWN;
+  float bias[8][4];
+#pragma unroll
+  for (int ni = 0; ni < 8; ++ni) {
+    const int c = cw + ni * 16 + lg * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bias[ni][i] = (a.b1 && c < a.N4) ? a.b1[c + i] : 0.f;
+  }
+  const long long mw = m0 + wm * kWM;
+  constexpr int NB = EC / 16;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int half = 0; half < kWN / EC; ++half) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int ni = half * NB + nb;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[i] = (float)(__bf16)(acc[ni][mi][i] + bias[ni][i]);
+            if (pass == 1) v[i] = silu_fast(v[i]);
+          }
+          const unsigned lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+          *(uint2 *)(st + (mi * 16 + lr) * kES + nb * 16 + lg * 4) = make_uint2(lo, hi);
+        }
+      }
+      constexpr int CPR = EC / 8, RPI = 64 / CPR;
+      const int cc = lane % CPR;
+      const int col = cw + half * EC + cc * 8;
+      int blk = 0, cin = col;
+      if (pass == 1) {
+        blk = col / a.D;
+        cin = col - blk * a.D;
+      }
+      u16 *dst = pass == 0 ? a.Z : blk == 0 ? a.U : blk == 1 ? a.V : blk == 2 ? a.Q : a.K;
+      const long long ldd = pass == 0 ? a.N4 : a.D;
+#pragma unroll 4
+      for (int it = 0; it < kWM / RPI; ++it) {
+        const int r = it * RPI + lane / CPR;
+        const long long m = mw + r;
+        const u32x4 v = *(const u32x4 *)(st + r * kES + cc * 8);
+        if (m < a.T && col < a.N4) *(u32x4 *)(dst + m * ldd + cin) = v;
+      }
+    }
+  }
+}
+
+// W1 [dm, N4] -> W1^T [N4, dm] through 64 x 64 LDS tiles.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const u16 *__restrict__ src, int rows, int cols,
+                                                             u16 *__restrict__ dst) {
+  __shared__ u16 t[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) t[i][tx] = src[(long long)r * cols + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < cols && r < rows) dst[(long long)c * rows + r] = t[tx][i];
+  }
+}
+
+template <int BM, int BK, int MINB, int EC>
+hipError_t launch_proj(const ProjArgs &a0, hipStream_t s) {
+  ProjArgs a = a0;
+  a.MT = (int)((a.T + BM - 1) / BM);
+  const long long blocks = (long long)((a.MT + 7) / 8) * 8 * a.NT;
+  f1_silu_gemm_kernel<BM, BK, MINB, EC><<<(unsigned)blocks, ProjCfg<BM, BK, MINB, EC>::kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+ProjArgs proj_args(const void *X, long long T, int dm, const float *b1, int D, const void *W1t, void *Z, void *U,
+                   void *V, void *Q, void *K) {
+  ProjArgs a;
+  a.X = (const u16 *)X;
+  a.W1t = (const u16 *)W1t;
+  a.b1 = b1;
+  a.T = T;
+  a.dm = dm;
+  a.N4 = 4 * D;
+  a.D = D;
+  a.NT = (a.N4 + kBN - 1) / kBN;
+  a.MT = 0;
+  a.Z = (u16 *)Z;
+  a.U = (u16 *)U;
+  a.V = (u16 *)V;
+  a.Q = (u16 *)Q;
+  a.K = (u16 *)K;
+  return a;
+}
+
+template <int EC>
+hipError_t launch_proj_dma(const ProjArgs &a0, hipStream_t s) {
+  ProjArgs a = a0;
+  a.MT = (int)((a.T + 255) / 256);
+  const long long blocks = (long long)((a.MT + 7) / 8) * 8 * a.NT;
+  f1_silu_gemm_dma_kernel<EC><<<(unsigned)blocks, 512, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const void *W1, int dm, int N4, void *W1t, hipStream_t s) {
+  dim3 tg((N4 + 63) / 64, (dm + 63) / 64);
+  transpose_bf16_kernel<<<tg, 256, 0, s>>>((const u16 *)W1, dm, N4, (u16 *)W1t);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool f1_silu_gemm_supported(long long T, int dm, int D) {
+  return T >= 0 && dm >= 8 && dm % 8 == 0 && D % 8 == 0 && (long long)dm * 256 * 2 < 0x80000000LL &&
+         (T + 255) / 256 < (1LL << 24) / 8;
+}
+
+size_t f1_silu_gemm_ws_bytes(int dm, int D) { return (size_t)dm * 4 * D * 2; }
+
+hipError_t launch_f1_silu_gemm(const void *X, long long T, int dm, const void *W1, const float *b1, int D,
+                               void *W1t, void *Z, void *U, void *V, void *Q, void *K, hipStream_t s) {
+  hipError_t e = launch_transpose(W1, dm, 4 * D, W1t, s);
+  if (e != hipSuccess || T == 0) return e;
+  const ProjArgs a = proj_args(X, T, dm, b1, D, W1t, Z, U, V, Q, K);
+  // K in whole groups of four 32-wide steps: the direct-to-LDS pipeline;
+  // otherwise the register-staged kernel (any dm % 8 == 0)
+  return dm % 128 == 0 ? launch_proj_dma<64>(a, s) : launch_proj<256, 64, 1, 128>(a, s);
+}
+
+}  // namespace hstu

@@ -292,7 +292,8 @@ enum {
   HSTU_KERNEL_BALANCE = 9,        /* hstu_balance_bins */
   HSTU_KERNEL_GEMM = 10,          /* the layer's projection GEMMs (hipBLASLt) */
   HSTU_KERNEL_LAYER_EW = 11,      /* the layer's SiLU / SiLU' / bias-gradient passes */
-  HSTU_KERNEL_COUNT = 12          /* (launches recorded into a graph are not timed) */
+  HSTU_KERNEL_PROJ_SILU = 12,     /* f1 as one MFMA GEMM with the SiLU split epilogue (and W1's transpose) */
+  HSTU_KERNEL_COUNT = 13          /* (launches recorded into a graph are not timed) */
 };
 hstu_status_t hstu_kernel_timing(int32_t enable);
 hstu_status_t hstu_kernel_timing_read(int32_t kernel, double *total_ms, int64_t *launches);
@@ -328,6 +329,20 @@ int32_t hstu_set_inline_schedule(int32_t enable);
  */
 enum { HSTU_TILE_ORDER_LONGEST = 0, HSTU_TILE_ORDER_BY_SEQUENCE = 1 };
 int32_t hstu_set_tile_order(int32_t order);
+
+/*
+ * f1 of the bf16 training forward (hstu_layer_fwd with Z given; HSTU blog,
+ * section 3, layer formula). By default it runs as one MFMA GEMM of the
+ * library's own whose epilogue adds b1, writes Z and writes SiLU(Z) straight
+ * into the U, V, Q, K blocks, after a small kernel that transposes W1 into
+ * the layer workspace's GEMM area (d_model % 8 == 0, H * d % 8 == 0, and
+ * 4 * H * d * d_model * 2 bytes within that 64 MiB area; other shapes, and
+ * fp32, take the second form). enable = 0 selects the second form: a library
+ * GEMM writing Z, then a separate SiLU split pass. Both forms round Z to bf16
+ * and take the SiLU of the rounded value; they differ only in the GEMM's
+ * summation order. Process-wide, host only; returns the previous setting.
+ */
+int32_t hstu_set_fused_projection(int32_t enable);
 
 /*
  * Stochastic Length (HSTU blog, section 3.4: training sequences are sampled

@@ -114,6 +114,53 @@ def test_layer_inference_form_without_z(lp):
         assert e_ref <= tol(lp.core) and e_z <= tol(lp.core), name
 
 
+def _fused_cases():
+    out = [lp for lp in _layers() if lp.core.dtype == torch.bfloat16 and lp.d_model % 8 == 0]
+    # d_model 72: a K tail of 8 columns; 3 heads x 32: column blocks that
+    # straddle the 256-column tiles and a partial column tile (4D = 384);
+    # 300 tokens: a partial token tile
+    p = synth.custom("L_bf16_ktail", [180, 120], H=3, d=32, wid=89, n_max=32, norm=synth.NORM_LN, n_pos=64,
+                     rab_std=0.3)
+    out.append(synth.with_layer(p, d_model=72, wid=99, x_std=1.0, w_std=0.1, bias_std=0.2))
+    return out
+
+
+@pytest.mark.parametrize("lp", _fused_cases(), ids=lambda v: v.name)
+def test_layer_fused_projection_matches_split_form(lp):
+    """f1 as the library's own GEMM with the SiLU split epilogue against the
+    library GEMM + separate SiLU pass: Z agrees to bf16 rounding, each of
+    U, V, Q, K is SiLU of the stored Z (computed here in fp32, one bf16
+    rounding apart), and the layer's outputs match the oracle either way."""
+    _say("layer fused f1", lp.name, "d_model", lp.d_model, "D", lp.core.H * lp.core.d, "T", lp.T)
+    ns = device.upload_layer(lp)
+    prev = api.set_fused_projection(True)
+    try:
+        ff = device.run_layer_fwd(ns, save_act=True)
+        api.set_fused_projection(False)
+        fs = device.run_layer_fwd(ns, save_act=True)
+    finally:
+        api.set_fused_projection(prev)
+    torch.cuda.synchronize()
+    ref = oracle_layer_fwd(lp)
+    D = lp.core.H * lp.core.d
+    for name, f in (("fused", ff), ("split", fs)):
+        errs = _check_fwd(lp, f, ref)
+        z = f.Z.float()
+        silu = (z * torch.sigmoid(z)).to(torch.bfloat16).float()
+        act = f.UVQK.float().reshape(4, lp.T, D)
+        for blk in range(4):
+            got = act[blk]
+            want = silu[:, blk * D:(blk + 1) * D]
+            bad = (got - want).abs() > 2.0 ** -7 * want.abs() + 1e-6
+            assert int(bad.sum()) == 0, (name, blk, int(bad.sum()))
+        _say(f"  {name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        for k, v in errs.items():
+            assert v <= tol(lp.core), (name, k, v)
+    dz = (ff.Z.float() - fs.Z.float()).abs()
+    assert rel_l2(ff.Z.float().cpu().numpy(), fs.Z.float().cpu().numpy()) <= 2e-3
+    assert float(dz.max()) <= 2.0 ** -6 * float(fs.Z.float().abs().max())
+
+
 def test_layer_bias_gradients_without_bias_inputs_are_column_sums():
     """With b1 = b2 = None the layer still returns db1, db2 (the gradients a
     zero bias would get): they must equal the column sums of dZ and dOut."""
