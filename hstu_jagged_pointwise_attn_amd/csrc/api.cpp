@@ -15,6 +15,7 @@
 
 #include "../../include/hstu.h"
 #include "hstu_internal.h"
+#include "proj_gemm.h"
 
 using namespace hstu;
 

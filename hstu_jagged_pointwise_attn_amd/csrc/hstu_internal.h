@@ -236,13 +236,6 @@ int gemm_init();
 const char *gemm_status_text(int st);
 bool gemm_unsupported(int st);  // no algorithm for the problem
 
-// f1 with the SiLU split in its epilogue (proj_gemm.hip): W1 [dm, 4D] is
-// transposed into W1t (f1_silu_gemm_ws_bytes), then Z [T, 4D] and U, V, Q, K
-// [T, D] are written (bf16). b1 may be NULL.
-bool f1_silu_gemm_supported(long long T, int dm, int D);
-size_t f1_silu_gemm_ws_bytes(int dm, int D);
-hipError_t launch_f1_silu_gemm(const void *X, long long T, int dm, const void *W1, const float *b1, int D,
-                               void *W1t, void *Z, void *U, void *V, void *Q, void *K, hipStream_t s);
 hipError_t launch_silu_split(const void *Z, long long T, int D, bool bf16, void *U, void *V, void *Q, void *K,
                              hipStream_t s);
 // Column sums run in two passes through a scratch `partial` of

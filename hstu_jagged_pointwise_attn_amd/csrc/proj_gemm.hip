@@ -32,7 +32,7 @@
 // bits.
 // W1 is first transposed to W1^T [4D, dm] by a small LDS-tiled kernel, so that
 // both operands are read along K.
-#include "hstu_internal.h"
+#include "proj_gemm.h"
 #include "device_common.h"
 
 #include <type_traits>
