@@ -344,6 +344,24 @@ def cpu_baseline_layer(lp, budget_s):
                       f"{w1 / 1e12:.3f} useful TFLOP); {t1:.1f} s of fp64 oracle time with OpenMP on {cores} threads"}
 
 
+def copy_probe(args):
+    """--copy-probe-mb: three device copies of a buffer of known size after
+    the timed region, the calibration of the HBM byte counters."""
+    import torch
+
+    if args.copy_probe_mb <= 0:
+        return
+    n = args.copy_probe_mb << 20
+    src_buf = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst_buf = torch.empty_like(src_buf)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst_buf.copy_(src_buf)
+    torch.cuda.synchronize()
+    log(f"[bench] copy probe: 3 x {n} bytes")
+    del src_buf, dst_buf
+
+
 def bench_layer(args):
     """One step = hstu_layer_fwd + hstu_layer_bwd of one batch. Useful FLOPs:
     12*d per visible pair and head for the attention core, and 2*M*N*K for
@@ -415,6 +433,7 @@ def bench_layer(args):
                 "traffic": traffic_from_profiles(args.workload, dom) if dom in KERNEL_SOURCES else None,
                 "kernel": dom + (" (6 launches per step)" if dom == "gemm" else ""),
                 "kernel_ms": per_step[dom], "per_kernel_ms_per_step": per_step, "per_launch_ms": per_launch}
+    copy_probe(args)
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
@@ -754,16 +773,7 @@ def main():
                 "traffic": traffic_from_profiles(wl, dom_name), "kernel": dom_name,
                 "kernel_ms": dom_ms, "per_kernel_ms": per, "hbm_algorithmic": hbm}
 
-    if args.copy_probe_mb > 0:
-        n = args.copy_probe_mb << 20
-        src_buf = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst_buf = torch.empty_like(src_buf)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst_buf.copy_(src_buf)
-        torch.cuda.synchronize()
-        log(f"[bench] copy probe: 3 x {n} bytes")
-        del src_buf, dst_buf
+    copy_probe(args)
 
     cpu = None
     if not args.no_cpu_baseline:
