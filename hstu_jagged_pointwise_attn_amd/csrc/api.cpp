@@ -593,11 +593,22 @@ hstu_status_t hstu_mfalcon_score(const hstu_problem_t *cand, const int32_t *hist
                      cand->timestamps, hist_ts, Yc, Oc, mean, rstd);
 }
 
-hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *K, const void *V,
+}  // extern "C"
+
+namespace {
+// A layer's backward writes dU, dV, dQ, dK straight into the column blocks
+// of its dZ [T, 4D] (row stride 4D), each times SiLU' of the same block of the
+// pre-activation Z (bf16 only). dU..dK then point into dZ; z is Z itself.
+struct DsiluOut {
+  const void *z;
+  long long ld;
+};
+
+hstu_status_t attn_bwd_impl(const hstu_problem_t *p, const void *Q, const void *K, const void *V,
                             const void *U, const void *O, const float *mean, const float *rstd,
                             const void *dY, void *dQ, void *dK, void *dV, void *dU,
                             float *d_rab_p, float *d_rab_t, float *d_gamma, float *d_beta,
-                            void *ws, size_t ws_bytes, void *stream) {
+                            void *ws, size_t ws_bytes, void *stream, const DsiluOut *zo) {
   hstu_status_t s = check_problem(p, HSTU_OP_BWD);
   if (s) return s;
   const long long T = p->total_tokens;
@@ -670,6 +681,8 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
     // dgamma / dbeta partials leave with one global atomic per column and run.
     n.tokens_per_wave = aff_lds ? L.norm_tpw : (dg || db) ? 32 : 1;
     n.dU = dU; n.dX = dO;
+    n.ldu = zo ? zo->ld : D;
+    n.zu = zo ? zo->z : nullptr;
     n.dgamma = dg; n.dbeta = db;
     n.partial = aff_lds ? at<float>(ws, L.npart) : nullptr;
     Timed t_(HSTU_KERNEL_NORM_BWD, st);
@@ -699,6 +712,13 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
   b.status = qa.hdr + kHdrStatus;
   b.desc = qa.desc;
   b.tiles = qa.tiles;
+  b.ldo = zo ? zo->ld : D;
+  if (zo) {
+    const size_t blk = (size_t)D * 2;  // bytes between column blocks of a bf16 row
+    b.zv = static_cast<const char *>(zo->z) + blk;
+    b.zq = static_cast<const char *>(zo->z) + 2 * blk;
+    b.zk = static_cast<const char *>(zo->z) + 3 * blk;
+  }
   long long units = L.max_tiles * p->H;
   if (units >= (1ll << 31) || L.max_ktiles * p->H >= (1ll << 31))
     return fail(HSTU_ERR_UNSUPPORTED, "too many work units");
@@ -722,6 +742,18 @@ hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *
     HIP_TRY(bf16 ? launch_attn_bwd_dkdv_bf16(b, st) : launch_attn_bwd_dkdv_f32(b, st), "dkdv launch");
   }
   return HSTU_OK;
+}
+}  // namespace
+
+extern "C" {
+
+hstu_status_t hstu_attn_bwd(const hstu_problem_t *p, const void *Q, const void *K, const void *V,
+                            const void *U, const void *O, const float *mean, const float *rstd,
+                            const void *dY, void *dQ, void *dK, void *dV, void *dU,
+                            float *d_rab_p, float *d_rab_t, float *d_gamma, float *d_beta,
+                            void *ws, size_t ws_bytes, void *stream) {
+  return attn_bwd_impl(p, Q, K, V, U, O, mean, rstd, dY, dQ, dK, dV, dU, d_rab_p, d_rab_t, d_gamma, d_beta, ws,
+                       ws_bytes, stream, nullptr);
 }
 
 hstu_status_t hstu_schedule_export(const hstu_problem_t *p, int32_t op,
@@ -977,13 +1009,28 @@ hstu_status_t hstu_layer_bwd(const hstu_problem_t *p, const hstu_layer_weights_t
       HIP_TRY(launch_silu_split(Z, T, (int)D, bf16, act, act + td, act + 2 * td, act + 3 * td, st),
               "SiLU split launch");
   }
-  // the attention core
-  s = hstu_attn_bwd(p, Q, K, V, U, O, mean, rstd, dY, dQ, dK, dV, dU, d_rab_p, d_rab_t, d_gamma, d_beta, ws,
-                    y.core_bytes, stream);
-  if (s) return s;
-  // phi1 and f1: dZ = [dU|dV|dQ|dK] * SiLU'(Z) into the activation buffer
-  void *dZ = act;
-  {
+  void *dZ;
+  if (bf16 && g_fused_proj.load()) {
+    // the attention core and the norm backward write dZ = [dU|dV|dQ|dK] *
+    // SiLU'(Z) themselves, into the gradient buffer (U, V, Q, K may sit in
+    // the activation buffer)
+    dZ = gr;
+    char *dz = gr;
+    const size_t blk = (size_t)D * 2;
+    const DsiluOut zo{Z, 4 * D};
+    s = attn_bwd_impl(p, Q, K, V, U, O, mean, rstd, dY, dz + 2 * blk, dz + 3 * blk, dz + blk, dz, d_rab_p, d_rab_t,
+                      d_gamma, d_beta, ws, y.core_bytes, stream, &zo);
+    if (s) return s;
+    Timed t_(HSTU_KERNEL_LAYER_EW, st);
+    if (db1) HIP_TRY(launch_colsum(dZ, T, (int)(4 * D), bf16, partial, db1, st), "bias-gradient launch");
+    if (T == 0) HIP_TRY(launch_fill_f32(dW1, dm * 4 * D, 0.f, st), "fill");
+  } else {
+    // the attention core, then phi1 and f1: dZ = [dU|dV|dQ|dK] * SiLU'(Z)
+    // into the activation buffer
+    s = hstu_attn_bwd(p, Q, K, V, U, O, mean, rstd, dY, dQ, dK, dV, dU, d_rab_p, d_rab_t, d_gamma, d_beta, ws,
+                      y.core_bytes, stream);
+    if (s) return s;
+    dZ = act;
     Timed t_(HSTU_KERNEL_LAYER_EW, st);
     HIP_TRY(launch_dsilu(Z, dU, dV, dQ, dK, T, (int)D, bf16, dZ, partial, db1, st), "SiLU backward launch");
     if (T == 0) HIP_TRY(launch_fill_f32(dW1, dm * 4 * D, 0.f, st), "fill");

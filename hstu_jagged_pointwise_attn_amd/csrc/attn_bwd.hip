@@ -60,7 +60,7 @@ struct PairPrefetch {
 // The sums go into rings indexed by the signed diagonal; diagonals that no
 // later key tile can touch are flushed to global memory after every tile.
 // ---------------------------------------------------------------------------
-template <int D, bool USE_P, bool USE_T, bool TF, bool DIAG_DPP>
+template <int D, bool USE_P, bool USE_T, bool TF, bool DIAG_DPP, bool ZO>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   static_assert(!DIAG_DPP || USE_P, "register diagonal sums are for rab_p");
   static_assert(!TF || USE_T, "the timestamp filter needs the timestamps");
@@ -579,6 +579,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       const bool cand = ok_r[nq] && fi0 + lrow >= sd.E;
       float qk = 0.f, dov = 0.f;
       const long long srow = (long long)(sd.self_base + fi0 + lrow - sd.E) * ld + h * D + lg * 8;
+      // the same row of dK / dV (row stride ldo: a layer's dZ blocks)
+      const long long sout = ZO ? (long long)(sd.self_base + fi0 + lrow - sd.E) * a.ldo + h * D + lg * 8 : srow;
       if (cand) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -612,8 +614,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
             wv[e] = pack_bf16x2((float)dof[nq][ks][2 * e] * as * a.inv_nmax,
                                 (float)dof[nq][ks][2 * e + 1] * as * a.inv_nmax);
           }
-          *(u32x4 *)(dK + srow + ks * 32) = wk;
-          *(u32x4 *)(dV + srow + ks * 32) = wv;
+          if constexpr (ZO) {  // a layer's dZ blocks: times SiLU'(Z), as the dK/dV kernel's own rows
+            wk = dsilu_bf16x8(wk, *(const u32x4 *)((const u16 *)a.zk + sout + ks * 32));
+            wv = dsilu_bf16x8(wv, *(const u32x4 *)((const u16 *)a.zv + sout + ks * 32));
+          }
+          *(u32x4 *)(dK + sout + ks * 32) = wk;
+          *(u32x4 *)(dV + sout + ks * 32) = wv;
         }
         if (lg == 0) atomicAdd(&self_acc, dss);
       }
@@ -646,6 +652,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }
     if (tid < 32 && htb[tid] != 0.f) atomicAdd(a.drab_t + tid, htb[tid] * a.inv_nmax);
   }
+  // A layer's pre-activation rows for the fused SiLU', requested before the
+  // staging below so that their latency overlaps it.
+  constexpr int NCO = BM * CH / NT;  // 16-byte chunks of dQ per thread
+  static_assert(BM * CH % NT == 0, "whole chunks per thread");
+  const u16 *zq = (const u16 *)a.zq;
+  u32x4 zpre[NCO];
+  if constexpr (ZO) {
+#pragma unroll
+    for (int j = 0; j < NCO; ++j) {
+      const int c = tid + j * NT, row = c / CH, col = (c % CH) * 8;
+      if (row < nrows) zpre[j] = *(const u32x4 *)(zq + (long long)(sd.q_base + row0 + row) * a.ldo + h * D + col);
+    }
+  }
   // Stage dQ through LDS for 16-byte row stores.
   u16 *os = KV;
 #pragma unroll
@@ -661,11 +680,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   __syncthreads();
   u16 *dQ = (u16 *)a.dQ;
-  for (int c = tid; c < BM * CH; c += NT) {
-    const int row = c / CH, col = (c % CH) * 8;
-    if (row < nrows)
-      *(u32x4 *)(dQ + (long long)(sd.q_base + row0 + row) * ld + h * D + col) =
-          *(const u32x4 *)(os + row * ST + col);
+  if constexpr (ZO) {
+#pragma unroll
+    for (int j = 0; j < NCO; ++j) {
+      const int c = tid + j * NT, row = c / CH, col = (c % CH) * 8;
+      if (row < nrows) {
+        const long long g = (long long)(sd.q_base + row0 + row) * a.ldo + h * D + col;
+        *(u32x4 *)(dQ + g) = dsilu_bf16x8(*(const u32x4 *)(os + row * ST + col), zpre[j]);  // a layer's dZ block
+      }
+    }
+  } else {
+    for (int c = tid; c < BM * CH; c += NT) {
+      const int row = c / CH, col = (c % CH) * 8;
+      if (row < nrows)
+        *(u32x4 *)(dQ + (long long)(sd.q_base + row0 + row) * ld + h * D + col) =
+            *(const u32x4 *)(os + row * ST + col);
+    }
   }
   if (USE_T && tid == 0 && s_bad) atomicOr(a.status, HSTU_DEV_BAD_TIMESTAMPS);
 }
@@ -673,7 +703,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK/dV kernel (key-major): 4 waves x 16 keys, query steps of 64 rows.
 // ---------------------------------------------------------------------------
-template <int D, bool USE_P, bool USE_T, bool TF>
+template <int D, bool USE_P, bool USE_T, bool TF, bool ZO>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   static_assert(!TF || USE_T, "the timestamp filter needs the timestamps");
   constexpr int BN = kBwdKBN, BM = kBwdKBM;
@@ -973,6 +1003,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   if (USE_T && bad_t) atomicOr(&s_bad, 1);
+  // A layer's pre-activation rows for the fused SiLU', requested before the
+  // staging below so that their latency overlaps it.
+  constexpr int NCO = BN * CH / 256;  // 16-byte chunks of dK (and dV) per thread
+  static_assert(BN * CH % 256 == 0, "whole chunks per thread");
+  const u16 *zk = (const u16 *)a.zk, *zv = (const u16 *)a.zv;
+  u32x4 zkp[NCO], zvp[NCO];
+  if constexpr (ZO) {
+#pragma unroll
+    for (int j = 0; j < NCO; ++j) {
+      const int c = tid + j * 256, row = c / CH, col = (c % CH) * 8;
+      if (row < nkeys) {
+        const long long g = (long long)(sd.kv_base + k0 + row) * a.ldo + h * D + col;
+        zkp[j] = *(const u32x4 *)(zk + g);
+        zvp[j] = *(const u32x4 *)(zv + g);
+      }
+    }
+  }
   // Stage dK and dV (C layout: key 4 lg + i, column 16 nd + lr) through LDS;
   // dV summed -log2(e) SiLU(.) dO, which -ln(2) / N_max restores.
   const float vscale = a.inv_nmax * -kLn2;
@@ -988,12 +1035,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   }
   __syncthreads();
   u16 *dK = (u16 *)a.dK, *dV = (u16 *)a.dV;
-  for (int c = tid; c < BN * CH; c += 256) {
-    const int row = c / CH, col = (c % CH) * 8;
-    if (row < nkeys) {
-      const long long g = (long long)(sd.kv_base + k0 + row) * ld + h * D + col;
-      *(u32x4 *)(dK + g) = *(const u32x4 *)(sk + row * ST + col);
-      *(u32x4 *)(dV + g) = *(const u32x4 *)(sv + row * ST + col);
+  if constexpr (ZO) {  // a layer's dZ blocks
+#pragma unroll
+    for (int j = 0; j < NCO; ++j) {
+      const int c = tid + j * 256, row = c / CH, col = (c % CH) * 8;
+      if (row < nkeys) {
+        const long long g = (long long)(sd.kv_base + k0 + row) * a.ldo + h * D + col;
+        *(u32x4 *)(dK + g) = dsilu_bf16x8(*(const u32x4 *)(sk + row * ST + col), zkp[j]);
+        *(u32x4 *)(dV + g) = dsilu_bf16x8(*(const u32x4 *)(sv + row * ST + col), zvp[j]);
+      }
+    }
+  } else {
+    for (int c = tid; c < BN * CH; c += 256) {
+      const int row = c / CH, col = (c % CH) * 8;
+      if (row < nkeys) {
+        const long long g = (long long)(sd.kv_base + k0 + row) * ld + h * D + col;
+        *(u32x4 *)(dK + g) = *(const u32x4 *)(sk + row * ST + col);
+        *(u32x4 *)(dV + g) = *(const u32x4 *)(sv + row * ST + col);
+      }
     }
   }
   if (USE_T && tid == 0 && s_bad) atomicOr(a.status, HSTU_DEV_BAD_TIMESTAMPS);
@@ -1205,43 +1264,43 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a) {
 }  // namespace
 
 #define HSTU_BWD_BF16_LAUNCH(KERNEL, NTHR)                                                      \
-  template <int D>                                                                              \
+  template <int D, bool ZO>                                                                     \
   hipError_t launch_##KERNEL##_d(const BwdArgs &a, hipStream_t s) {                             \
     const bool p = a.rab_p != nullptr, t = a.ts != nullptr;                                     \
     const dim3 g(a.units), b(NTHR);                                                             \
     if (a.tfilt) {                                                                              \
-      if (p) hipLaunchKernelGGL((KERNEL<D, true, true, true>), g, b, 0, s, a);                  \
-      else hipLaunchKernelGGL((KERNEL<D, false, true, true>), g, b, 0, s, a);                   \
+      if (p) hipLaunchKernelGGL((KERNEL<D, true, true, true, ZO>), g, b, 0, s, a);                  \
+      else hipLaunchKernelGGL((KERNEL<D, false, true, true, ZO>), g, b, 0, s, a);                   \
     } else if (p && t) {                                                                        \
-      hipLaunchKernelGGL((KERNEL<D, true, true, false>), g, b, 0, s, a);                        \
+      hipLaunchKernelGGL((KERNEL<D, true, true, false, ZO>), g, b, 0, s, a);                        \
     } else if (p) {                                                                             \
-      hipLaunchKernelGGL((KERNEL<D, true, false, false>), g, b, 0, s, a);                       \
+      hipLaunchKernelGGL((KERNEL<D, true, false, false, ZO>), g, b, 0, s, a);                       \
     } else if (t) {                                                                             \
-      hipLaunchKernelGGL((KERNEL<D, false, true, false>), g, b, 0, s, a);                       \
+      hipLaunchKernelGGL((KERNEL<D, false, true, false, ZO>), g, b, 0, s, a);                       \
     } else {                                                                                    \
-      hipLaunchKernelGGL((KERNEL<D, false, false, false>), g, b, 0, s, a);                      \
+      hipLaunchKernelGGL((KERNEL<D, false, false, false, ZO>), g, b, 0, s, a);                      \
     }                                                                                           \
     return hipGetLastError();                                                                   \
   }
 
-template <int D>
+template <int D, bool ZO>
 hipError_t launch_bwd_dq_kernel_d(const BwdArgs &a, hipStream_t s) {
   const bool p = a.rab_p != nullptr, t = a.ts != nullptr;
   const dim3 g(a.units), b(256);
   if (a.tfilt) {
-    if (p) hipLaunchKernelGGL((bwd_dq_kernel<D, true, true, true, false>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<D, false, true, true, false>), g, b, 0, s, a);
+    if (p) hipLaunchKernelGGL((bwd_dq_kernel<D, true, true, true, false, ZO>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<D, false, true, true, false, ZO>), g, b, 0, s, a);
   } else if (p && a.no_cand) {
-    if (t) hipLaunchKernelGGL((bwd_dq_kernel<D, true, true, false, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<D, true, false, false, true>), g, b, 0, s, a);
+    if (t) hipLaunchKernelGGL((bwd_dq_kernel<D, true, true, false, true, ZO>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<D, true, false, false, true, ZO>), g, b, 0, s, a);
   } else if (p && t) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true, true, false, false>), g, b, 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true, true, false, false, ZO>), g, b, 0, s, a);
   } else if (p) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true, false, false, false>), g, b, 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true, false, false, false, ZO>), g, b, 0, s, a);
   } else if (t) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false, true, false, false>), g, b, 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false, true, false, false, ZO>), g, b, 0, s, a);
   } else {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false, false, false, false>), g, b, 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false, false, false, false, ZO>), g, b, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -1250,9 +1309,9 @@ HSTU_BWD_BF16_LAUNCH(bwd_dkdv_kernel, 256)
 hipError_t launch_attn_bwd_dq_bf16(const BwdArgs &a, hipStream_t s) {
   if (a.units <= 0) return hipSuccess;
   switch (a.d) {
-    case 32: return launch_bwd_dq_kernel_d<32>(a, s);
-    case 64: return launch_bwd_dq_kernel_d<64>(a, s);
-    case 128: return launch_bwd_dq_kernel_d<128>(a, s);
+    case 32: return a.zq ? launch_bwd_dq_kernel_d<32, true>(a, s) : launch_bwd_dq_kernel_d<32, false>(a, s);
+    case 64: return a.zq ? launch_bwd_dq_kernel_d<64, true>(a, s) : launch_bwd_dq_kernel_d<64, false>(a, s);
+    case 128: return a.zq ? launch_bwd_dq_kernel_d<128, true>(a, s) : launch_bwd_dq_kernel_d<128, false>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1260,9 +1319,9 @@ hipError_t launch_attn_bwd_dq_bf16(const BwdArgs &a, hipStream_t s) {
 hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs &a, hipStream_t s) {
   if (a.units <= 0) return hipSuccess;
   switch (a.d) {
-    case 32: return launch_bwd_dkdv_kernel_d<32>(a, s);
-    case 64: return launch_bwd_dkdv_kernel_d<64>(a, s);
-    case 128: return launch_bwd_dkdv_kernel_d<128>(a, s);
+    case 32: return a.zq ? launch_bwd_dkdv_kernel_d<32, true>(a, s) : launch_bwd_dkdv_kernel_d<32, false>(a, s);
+    case 64: return a.zq ? launch_bwd_dkdv_kernel_d<64, true>(a, s) : launch_bwd_dkdv_kernel_d<64, false>(a, s);
+    case 128: return a.zq ? launch_bwd_dkdv_kernel_d<128, true>(a, s) : launch_bwd_dkdv_kernel_d<128, false>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -28,6 +28,12 @@ __device__ __forceinline__ float silu_fast(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
 }
 
+// SiLU'(z) = s (1 + z (1 - s)) with s = 1 / (1 + e^-z) (the layer's phi1).
+__device__ __forceinline__ float silu_grad(float z) {
+  const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+  return sg * (1.0f + z * (1.0f - sg));
+}
+
 // floor(log2(max(1, |dt|))) clamped to n_tb - 1.
 __device__ __forceinline__ int time_bucket(long long dt, int n_tb) {
   unsigned long long m = dt < 0 ? 0ull - (unsigned long long)dt : (unsigned long long)dt;
@@ -107,6 +113,19 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(u32, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// Eight bf16 gradients g times SiLU'(z) of eight bf16 pre-activations, each
+// product rounded once to bf16.
+__device__ __forceinline__ u32x4 dsilu_bf16x8(u32x4 g, u32x4 z) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float g0 = __uint_as_float(g[i] << 16), g1 = __uint_as_float(g[i] & 0xffff0000u);
+    const float z0 = __uint_as_float(z[i] << 16), z1 = __uint_as_float(z[i] & 0xffff0000u);
+    r[i] = pack_bf16x2(g0 * silu_grad(z0), g1 * silu_grad(z1));
+  }
+  return r;
 }
 
 // A raw buffer resource over [p, p + bytes) (bytes clamped to [0, 2^32 - 1];

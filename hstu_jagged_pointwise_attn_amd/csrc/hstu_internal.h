@@ -147,7 +147,9 @@ struct NormBwdArgs {
   long long T;
   int D;
   int tokens_per_wave;            // contiguous tokens handled by one wave
-  void *dU;                       // [T, D]
+  void *dU;                       // [T, D], row stride ldu
+  long long ldu;                  // D, or 4 D when dU is a column block of a layer's dZ
+  const void *zu;                 // with it (bf16 only), dU is multiplied by SiLU'(zu) (row stride ldu)
   void *dX;                       // [T, D] gradient w.r.t. the pre-norm output
   float *dgamma, *dbeta;          // [G, D] accumulated with atomics (zeroed by the caller), or NULL
   // When set, dgamma / dbeta are instead summed per workgroup in LDS into
@@ -183,6 +185,12 @@ struct BwdArgs {
   const SeqDesc *desc;
   const QTile *tiles;
   int units;                       // grid bound: records * H
+  // Row stride (elements) of dQ, dK, dV: H * d, or 4 H d when they are
+  // column blocks of a layer's dZ. With zq / zk / zv set (bf16 only), each
+  // is multiplied by SiLU' of the matching column block of the layer's
+  // pre-activation Z (same row stride) before it is stored.
+  long long ldo;
+  const void *zq, *zk, *zv;
 };
 // bf16: the query-major dQ kernel runs the forward's query tiles (kFwdBM x
 // kFwdBN); the key-major dK/dV kernel runs 64-key tiles x 64-row query steps.

@@ -6,6 +6,7 @@
 // One wave per token; the row sits in registers, the mean and the variance are
 // two wave reductions (the variance from the centred values).
 #include "hstu_internal.h"
+#include "device_common.h"
 #include "../../include/hstu.h"
 
 namespace hstu {
@@ -245,7 +246,8 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr bool PREFETCH = MAXCH <= 2;
   constexpr int RC = PREFETCH ? MAXCH : 1;
-  uint4 rx[RC], rdy[RC], ru[RC];
+  uint4 rx[RC], rdy[RC], ru[RC], rz[RC];
+  const bool fz = BF16 && a.zu != nullptr;  // a layer's fused SiLU' on dU
   float nmean = 0.f, nrstd = 1.f;
   int ngrp = 0;
   auto fetch = [&](long long t) __attribute__((always_inline)) {
@@ -258,6 +260,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
         rx[k] = *(const uint4 *)((const char *)a.X + off);
         rdy[k] = *(const uint4 *)((const char *)a.dY + off);
         ru[k] = *(const uint4 *)((const char *)a.U + off);
+        if (fz) rz[k] = *(const uint4 *)((const char *)a.zu + (t * a.ldu + ch * N) * ESZ);
       }
     }
     if (a.mode != HSTU_NORM_NONE) {
@@ -303,6 +306,26 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
         if (a.mode == HSTU_NORM_GLN) grp_t = a.group[t];
       }
     }
+    // A layer's fused SiLU': this token's pre-activation of the U block
+    // (requested with the token's rows when they are prefetched).
+    float zz[MAXCH][N];
+    if (fz) {
+#pragma unroll
+      for (int k = 0; k < MAXCH; ++k) {
+        const int ch = lane + 64 * k;
+        if (ch < nch) {
+          if constexpr (PREFETCH) V::unpack(rz[k], zz[k]);
+          else V::load(a.zu, t * a.ldu + ch * N, zz[k]);
+        }
+      }
+    }
+    auto store_du = [&](int k, int ch, float *du) __attribute__((always_inline)) {
+      if (fz) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) du[e] *= dev::silu_grad(zz[k][e]);
+      }
+      V::store(a.dU, t * a.ldu + ch * N, du);
+    };
     if constexpr (PREFETCH) {
       if (t + 1 < t1) fetch(t + 1);
     }
@@ -317,7 +340,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
             du[e] = x[k][e] * dy[k][e];
             dx[e] = dy[k][e] * u[k][e];
           }
-          V::store(a.dU, row + ch * N, du);
+          store_du(k, ch, du);
           V::store(a.dX, row + ch * N, dx);
         }
       }
@@ -359,7 +382,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
           s1 += gh[k][e];
           s2 += gh[k][e] * xh[k][e];
         }
-        V::store(a.dU, row + ch * N, du);
+        store_du(k, ch, du);
       }
     }
     const float m1 = wave_sum(s1) / (float)D, m2 = wave_sum(s2) / (float)D;

@@ -340,7 +340,13 @@ int32_t hstu_set_tile_order(int32_t order);
  * fp32, take the second form). enable = 0 selects the second form: a library
  * GEMM writing Z, then a separate SiLU split pass. Both forms round Z to bf16
  * and take the SiLU of the rounded value; they differ only in the GEMM's
- * summation order. Process-wide, host only; returns the previous setting.
+ * summation order. The same setting selects the bf16 backward's form: by
+ * default the norm backward and the two attention backward kernels write
+ * dZ = [dU | dV | dQ | dK] * SiLU'(Z) straight into dZ's column blocks (dU
+ * rounded once, dV, dQ, dK after their own bf16 rounding, as the separate
+ * pass sees them) and the bias gradient is a column sum of dZ; with 0 they
+ * write dU, dV, dQ, dK and a separate pass forms dZ and the column sums.
+ * Process-wide, host only; returns the previous setting.
  */
 int32_t hstu_set_fused_projection(int32_t enable);
 

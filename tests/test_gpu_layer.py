@@ -130,18 +130,36 @@ def test_layer_fused_projection_matches_split_form(lp):
     """f1 as the library's own GEMM with the SiLU split epilogue against the
     library GEMM + separate SiLU pass: Z agrees to bf16 rounding, each of
     U, V, Q, K is SiLU of the stored Z (computed here in fp32, one bf16
-    rounding apart), and the layer's outputs match the oracle either way."""
+    rounding apart), and the layer's outputs match the oracle either way;
+    likewise the backward with SiLU' applied by the kernels that produce
+    dU, dV, dQ, dK against the separate SiLU' pass."""
     _say("layer fused f1", lp.name, "d_model", lp.d_model, "D", lp.core.H * lp.core.d, "T", lp.T)
     ns = device.upload_layer(lp)
     prev = api.set_fused_projection(True)
     try:
         ff = device.run_layer_fwd(ns, save_act=True)
+        gf = device.run_layer_bwd(ns, ff)
         api.set_fused_projection(False)
         fs = device.run_layer_fwd(ns, save_act=True)
+        gs = device.run_layer_bwd(ns, fs)
     finally:
         api.set_fused_projection(prev)
     torch.cuda.synchronize()
+    assert api.device_status(gf.ws) == 0 and api.device_status(gs.ws) == 0
     ref = oracle_layer_fwd(lp)
+    rb = oracle_layer_bwd(lp)
+    # backward: fused (the attention and norm kernels write dZ with SiLU')
+    # and split (a separate SiLU' pass), both against the oracle
+    for name, g in (("fused", gf), ("split", gs)):
+        errs = {}
+        for k in ("dX", "dW1", "db1", "dW2", "db2"):
+            got = getattr(g, k)
+            if got is None or rb[k] is None or (lp.b1 is None and k == "db1") or (lp.b2 is None and k == "db2"):
+                continue
+            errs[k] = rel_l2(got.float().cpu().numpy(), rb[k])
+        _say(f"  {name} backward: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        for k, v in errs.items():
+            assert v <= tol(lp.core), (name, k, v)
     D = lp.core.H * lp.core.d
     for name, f in (("fused", ff), ("split", fs)):
         errs = _check_fwd(lp, f, ref)
