@@ -194,7 +194,7 @@ hipError_t norm_fwd_dispatch(const NormArgs &a, hipStream_t s) {
 // changes and at the end of its run: with `partial` into the workgroup's
 // [2][G][D] rows in LDS (written out per workgroup and reduced by a second
 // kernel), else with global atomics.
-template <bool BF16, int MAXCH>
+template <bool BF16, int MAXCH, bool ZU>
 __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
   using V = Vec<BF16>;
   constexpr int N = V::N;
@@ -246,8 +246,8 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr bool PREFETCH = MAXCH <= 2;
   constexpr int RC = PREFETCH ? MAXCH : 1;
-  uint4 rx[RC], rdy[RC], ru[RC], rz[RC];
-  const bool fz = BF16 && a.zu != nullptr;  // a layer's fused SiLU' on dU
+  constexpr bool fz = BF16 && ZU;  // a layer's fused SiLU' on dU
+  uint4 rx[RC], rdy[RC], ru[RC], rz[fz ? RC : 1];
   float nmean = 0.f, nrstd = 1.f;
   int ngrp = 0;
   auto fetch = [&](long long t) __attribute__((always_inline)) {
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
         rx[k] = *(const uint4 *)((const char *)a.X + off);
         rdy[k] = *(const uint4 *)((const char *)a.dY + off);
         ru[k] = *(const uint4 *)((const char *)a.U + off);
-        if (fz) rz[k] = *(const uint4 *)((const char *)a.zu + (t * a.ldu + ch * N) * ESZ);
+        if constexpr (fz) rz[k] = *(const uint4 *)((const char *)a.zu + (t * a.ldu + ch * N) * ESZ);
       }
     }
     if (a.mode != HSTU_NORM_NONE) {
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
     // A layer's fused SiLU': this token's pre-activation of the U block
     // (requested with the token's rows when they are prefetched).
     float zz[MAXCH][N];
-    if (fz) {
+    if constexpr (fz) {
 #pragma unroll
       for (int k = 0; k < MAXCH; ++k) {
         const int ch = lane + 64 * k;
@@ -320,11 +320,13 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
       }
     }
     auto store_du = [&](int k, int ch, float *du) __attribute__((always_inline)) {
-      if (fz) {
+      if constexpr (fz) {
 #pragma unroll
         for (int e = 0; e < N; ++e) du[e] *= dev::silu_grad(zz[k][e]);
+        V::store(a.dU, t * a.ldu + ch * N, du);
+      } else {
+        V::store(a.dU, t * D + ch * N, du);
       }
-      V::store(a.dU, t * a.ldu + ch * N, du);
     };
     if constexpr (PREFETCH) {
       if (t + 1 < t1) fetch(t + 1);
@@ -405,15 +407,15 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(NormBwdArgs a) {
   }
 }
 
-template <bool BF16>
+template <bool BF16, bool ZU>
 hipError_t norm_bwd_dispatch(const NormBwdArgs &a, hipStream_t s) {
   const int nch = a.D / Vec<BF16>::N;
   const dim3 grid((unsigned)norm_bwd_blocks(a.T, a.tokens_per_wave));
   const size_t lds = a.partial ? 2 * sizeof(float) * a.n_groups * a.D : 0;
-  if (nch <= 64) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 1>), grid, dim3(256), lds, s, a);
-  else if (nch <= 128) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 2>), grid, dim3(256), lds, s, a);
-  else if (nch <= 256) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 4>), grid, dim3(256), lds, s, a);
-  else if (nch <= 512) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 8>), grid, dim3(256), lds, s, a);
+  if (nch <= 64) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 1, ZU>), grid, dim3(256), lds, s, a);
+  else if (nch <= 128) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 2, ZU>), grid, dim3(256), lds, s, a);
+  else if (nch <= 256) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 4, ZU>), grid, dim3(256), lds, s, a);
+  else if (nch <= 512) hipLaunchKernelGGL((norm_bwd_kernel<BF16, 8, ZU>), grid, dim3(256), lds, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -469,7 +471,8 @@ long long norm_bwd_blocks(long long T, int tokens_per_wave) {
 
 hipError_t launch_norm_bwd(const NormBwdArgs &a, bool bf16, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  return bf16 ? norm_bwd_dispatch<true>(a, s) : norm_bwd_dispatch<false>(a, s);
+  if (bf16) return a.zu ? norm_bwd_dispatch<true, true>(a, s) : norm_bwd_dispatch<true, false>(a, s);
+  return norm_bwd_dispatch<false, false>(a, s);
 }
 
 hipError_t launch_norm_affine_reduce(const float *partial, long long blocks, int GD, float *dgamma, float *dbeta,
